@@ -1,0 +1,238 @@
+"""Seeded synthetic inputs for the gated delta-rule recurrence.
+
+This module is shared by the oracle-side tests and the GPU path (tests, smoke,
+bench).  It draws random numbers, applies the input recipe of each workload
+(L2-normalised q and k, sigmoid gates, bf16 storage) and nothing else: none of
+the recurrence's arithmetic lives here.
+
+Every tensor is returned as a NumPy array in its *stored* form:
+
+* bf16 tensors as ``uint16`` bit patterns (round-to-nearest-even from fp32),
+* fp32 tensors as ``float32``.
+
+``as_f64`` turns a stored array into the exact fp64 values it represents, which
+is what the oracle consumes; ``to_torch`` uploads a stored array with its
+dtype.
+
+Layouts (row-major):
+  prefill  q, k, k_w: [B, T, H, dk]   v: [B, T, H, dv]
+           alpha: [B, T, H] (scalar gate) or [B, T, H, dk] (channel gate)
+           beta_k: [B, T, H] (scalar) or [B, T, H, dk] (vector)
+           beta_v: [B, T, H, dv] (vector, separate write strength) or None
+           S0: [B, H, dk, dv] fp32 or None
+  decode   per-step tensors gain a leading step axis: q [steps, B, H, dk], ...
+           S: [B, H, dk, dv] fp32
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+BF16 = "bf16"
+F32 = "f32"
+
+GATE_SCALAR = 0
+GATE_CHANNEL = 1
+BETA_SCALAR = 0
+BETA_SHARED = 1
+BETA_KV = 2
+
+
+# ----------------------------------------------------------------------------
+# storage conversions (no method arithmetic)
+# ----------------------------------------------------------------------------
+
+def f32_to_bf16_bits(x) -> np.ndarray:
+    """Round fp32 values to bf16, nearest-even, returned as uint16 bit patterns."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = a.view(np.uint32).astype(np.uint64)
+    lsb = (u >> 16) & 1
+    r = ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+    nan = np.isnan(a)
+    if nan.any():
+        r[nan] = 0x7FC0
+    return r
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def as_f64(x: Optional[np.ndarray], dtype: str) -> Optional[np.ndarray]:
+    """Exact fp64 value of a stored array (bf16 bits or fp32)."""
+    if x is None:
+        return None
+    if dtype == BF16:
+        return bf16_bits_to_f32(x).astype(np.float64)
+    return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def store(x64: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 draw -> stored form (fp32 first, then bf16 RNE when asked)."""
+    x32 = np.asarray(x64, dtype=np.float32)
+    return f32_to_bf16_bits(x32) if dtype == BF16 else x32
+
+
+def to_torch(x: Optional[np.ndarray], dtype: str, device="cuda"):
+    """Upload a stored array to a torch tensor of the matching dtype."""
+    import torch
+
+    if x is None:
+        return None
+    if dtype == BF16:
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32))
+    return t.to(device)
+
+
+def _l2_normalise(x: np.ndarray) -> np.ndarray:
+    """Per-token L2 normalisation over the last axis, fp64, no epsilon."""
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True))
+
+
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+# ----------------------------------------------------------------------------
+# workload descriptions
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass(frozen=True)
+class Prefill:
+    """A prefill (chunk forward) workload and its input recipe."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    chunk: int
+    io: str = BF16              # q, k, k_w, v, o
+    gate: str = F32             # alpha, beta_k, beta_v
+    alpha_mode: int = GATE_SCALAR
+    beta_mode: int = BETA_SCALAR
+    alpha_mu: float = -4.0      # alpha = sigmoid(-N(mu, sd)) == exp(-softplus(N(mu, sd)))
+    alpha_sd: float = 1.0
+    alpha_flip: bool = False    # alpha = sigmoid(+N(mu, sd)) instead
+    write_key: bool = False     # k_w = bf16(d * k), d = 1 + 0.1 N(0, 1)
+    s0_std: float = 0.0         # 0 -> S0 is None
+    seed: int = 0
+
+    def scaled(self, **kw) -> "Prefill":
+        return dataclasses.replace(self, **kw)
+
+
+@dataclasses.dataclass(frozen=True)
+class Decode:
+    """A batched one-token decode workload: `steps` consecutive steps."""
+
+    name: str
+    B: int
+    H: int
+    dk: int
+    dv: int
+    steps: int
+    io: str = BF16
+    gate: str = BF16
+    alpha_mode: int = GATE_SCALAR
+    beta_mode: int = BETA_SCALAR
+    alpha_mu: float = -4.0
+    alpha_sd: float = 1.0
+    s_std: float = 0.02
+    seed: int = 0
+
+    def scaled(self, **kw) -> "Decode":
+        return dataclasses.replace(self, **kw)
+
+
+# The five workloads the library is specified against (named by content).
+TINY_GDN_F32 = Prefill("tiny_gdn_f32_B1H1T64d16C16", B=1, T=64, H=1, dk=16, dv=16, chunk=16,
+                       io=F32, gate=F32, alpha_mu=3.0, alpha_sd=0.5, alpha_flip=True, seed=8401)
+GDN_PREFILL = Prefill("gdn_bf16_B4H16T4096d128C64", B=4, T=4096, H=16, dk=128, dv=128, chunk=64,
+                      seed=8402)
+KDA_FG2PLUS_PREFILL = Prefill("kda_fg2plus_bf16_B4H16T4096d128C64", B=4, T=4096, H=16, dk=128,
+                              dv=128, chunk=64, alpha_mode=GATE_CHANNEL, beta_mode=BETA_KV,
+                              seed=8403)
+OSDN_LONG_PREFILL = Prefill("osdn_bf16_B1H32T65536d128C64", B=1, T=65536, H=32, dk=128, dv=128,
+                            chunk=64, write_key=True, s0_std=0.02, seed=8404)
+DECODE_B512 = Decode("decode_bf16_B512H16d128", B=512, H=16, dk=128, dv=128, steps=256, seed=8405)
+DECODE_DMEM_R8 = Decode("decode_deltamem_bf16_B8192H1r8", B=8192, H=1, dk=8, dv=8, steps=256,
+                        seed=8406)
+
+PREFILL_WORKLOADS = [TINY_GDN_F32, GDN_PREFILL, KDA_FG2PLUS_PREFILL, OSDN_LONG_PREFILL]
+DECODE_WORKLOADS = [DECODE_B512, DECODE_DMEM_R8]
+
+
+# ----------------------------------------------------------------------------
+# generators
+# ----------------------------------------------------------------------------
+
+def make_prefill(w: Prefill) -> dict:
+    """Draw one prefill batch.  Draw order: q, k, v, alpha, beta_k, beta_v, d, S0."""
+    rng = np.random.default_rng(w.seed)
+    B, T, H, dk, dv = w.B, w.T, w.H, w.dk, w.dv
+    q = store(_l2_normalise(rng.standard_normal((B, T, H, dk))), w.io)
+    k64 = _l2_normalise(rng.standard_normal((B, T, H, dk)))
+    k = store(k64, w.io)
+    v = store(rng.standard_normal((B, T, H, dv)), w.io)
+    ash = (B, T, H) if w.alpha_mode == GATE_SCALAR else (B, T, H, dk)
+    x = rng.normal(w.alpha_mu, w.alpha_sd, ash)
+    alpha = store(_sigmoid(x if w.alpha_flip else -x), w.gate)
+    bsh = (B, T, H) if w.beta_mode == BETA_SCALAR else (B, T, H, dk)
+    beta_k = store(_sigmoid(rng.standard_normal(bsh)), w.gate)
+    beta_v = None
+    if w.beta_mode == BETA_KV:
+        beta_v = store(_sigmoid(rng.standard_normal((B, T, H, dv))), w.gate)
+    k_w = None
+    if w.write_key:
+        d = 1.0 + 0.1 * rng.standard_normal((B, T, H, dk))
+        # the write key is formed from the *stored* key, in fp32, then rounded
+        k_w = store(d.astype(np.float32) * as_f64(k, w.io).astype(np.float32), w.io)
+    S0 = None
+    if w.s0_std > 0.0:
+        S0 = rng.normal(0.0, w.s0_std, (B, H, dk, dv)).astype(np.float32)
+    return dict(q=q, k=k, k_w=k_w, v=v, alpha=alpha, beta_k=beta_k, beta_v=beta_v, S0=S0)
+
+
+def make_decode(w: Decode) -> dict:
+    """Draw a decode run: per-step tensors [steps, B, H, .] and the initial state."""
+    rng = np.random.default_rng(w.seed)
+    n, B, H, dk, dv = w.steps, w.B, w.H, w.dk, w.dv
+    q = store(_l2_normalise(rng.standard_normal((n, B, H, dk))), w.io)
+    k = store(_l2_normalise(rng.standard_normal((n, B, H, dk))), w.io)
+    v = store(rng.standard_normal((n, B, H, dv)), w.io)
+    ash = (n, B, H) if w.alpha_mode == GATE_SCALAR else (n, B, H, dk)
+    alpha = store(_sigmoid(-rng.normal(w.alpha_mu, w.alpha_sd, ash)), w.gate)
+    bsh = (n, B, H) if w.beta_mode == BETA_SCALAR else (n, B, H, dk)
+    beta_k = store(_sigmoid(rng.standard_normal(bsh)), w.gate)
+    beta_v = None
+    if w.beta_mode == BETA_KV:
+        beta_v = store(_sigmoid(rng.standard_normal((n, B, H, dv))), w.gate)
+    S = rng.normal(0.0, w.s_std, (B, H, dk, dv)).astype(np.float32)
+    return dict(q=q, k=k, k_w=None, v=v, alpha=alpha, beta_k=beta_k, beta_v=beta_v, S=S)
+
+
+def prefill_f64(w: Prefill, x: dict) -> dict:
+    """The exact fp64 values of a prefill batch (what the oracle reads)."""
+    out = {}
+    for key in ("q", "k", "k_w", "v"):
+        out[key] = as_f64(x[key], w.io)
+    for key in ("alpha", "beta_k", "beta_v"):
+        out[key] = as_f64(x[key], w.gate)
+    out["S0"] = as_f64(x["S0"], F32)
+    return out
+
+
+def decode_f64(w: Decode, x: dict) -> dict:
+    out = {}
+    for key in ("q", "k", "k_w", "v"):
+        out[key] = as_f64(x[key], w.io)
+    for key in ("alpha", "beta_k", "beta_v"):
+        out[key] = as_f64(x[key], w.gate)
+    out["S"] = as_f64(x["S"], F32)
+    return out

@@ -1,0 +1,220 @@
+/*
+ * gdr_ref.c -- fp64 CPU oracle for the gated delta-rule recurrence.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only tests, the smoke check and the bench's CPU
+ * baseline may load this library.  It shares no code, header, table or helper
+ * with the GPU library; the two never include or link each other.
+ *
+ * What it computes: the plain sequential recurrence, one token at a time, in
+ * double precision, with no chunking and no reordering.  The state S of one
+ * (batch, head) is a dk x dv matrix (row i = key channel, column j = value
+ * channel), stored row-major, and the read-out is o_t = S_t^T q_t.  The pages
+ * write the transposed state (dv x dk) with prediction S k; every formula
+ * below is that formula transposed.
+ *
+ * Variants, each written in the form its page gives:
+ *
+ *  beta_mode 0 (scalar beta): gated delta rule.
+ *     X = Diag(alpha_t) S_{t-1}              forget gate, scalar alpha (Gated
+ *                                            DeltaNet) or one alpha per key
+ *                                            channel (Kimi Delta Attention);
+ *                                            [FG2-GDN page, section 1];
+ *                                            [SDM page, Mecanismo Central, item 3]
+ *     S_t = X + beta_t kw_t (v_t - X^T k_t)^T
+ *        kw = k: the DeltaNet online-gradient step on 1/2 |S k - v|^2
+ *                [OSDN page, section 1, update rule], gated.
+ *        kw = d (.) k: the diagonally right-preconditioned step; the page shows
+ *                that preconditioning the gradient equals scaling the write key
+ *                [OSDN page, section 2.1, both update equations].  The gate is
+ *                applied first, as for the other backbones the page uses.
+ *
+ *  beta_mode 1 (one beta vector in R^dk, needs dk == dv) and
+ *  beta_mode 2 (separate beta^k in R^dk and beta^v in R^dv):
+ *     kt = sqrt(beta^k) (.) k,  vt = sqrt(beta^v) (.) v   (beta^v = beta^k in mode 1)
+ *     S_t = (I - kt kt^T) Diag(alpha_t) S_{t-1} + kt vt^T
+ *        [FG2-GDN page, section 2.A, absorption and state update;
+ *         section 2.B, separate erase and write strengths].
+ *     When a separate write key kw is given, the left factor kt becomes
+ *     wt = sqrt(beta^k) (.) kw in both places (same rank-1 structure).
+ *
+ * Inputs are fp64 arrays holding the exact values the GPU path receives
+ * (bf16 or fp32 upcast), in the layouts
+ *     q, k, kw: [B, T, H, dk]   v: [B, T, H, dv]
+ *     alpha: [B, T, H] (mode 0) or [B, T, H, dk] (mode 1)
+ *     beta_k: [B, T, H] (beta mode 0) or [B, T, H, dk] (modes 1, 2)
+ *     beta_v: [B, T, H, dv] (beta mode 2 only)
+ *     S0, ST: [B, H, dk, dv];   o: [B, T, H, dv]
+ */
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define REF_OK 0
+#define REF_EINVAL (-1)
+
+/* One recurrence step on the state of one (batch, head).
+ * a: alpha (1 or dk values), bk: beta^k (1 or dk values), bv: beta^v (dv values or NULL). */
+static void ref_step(int dk, int dv, double *S, const double *a, int channel_alpha,
+                     int beta_mode, const double *bk, const double *bv,
+                     const double *k, const double *kw, const double *v,
+                     double *scratch /* >= 2*dk + 2*dv */)
+{
+    int i, j;
+    /* forget gate */
+    for (i = 0; i < dk; ++i) {
+        const double ai = channel_alpha ? a[i] : a[0];
+        for (j = 0; j < dv; ++j)
+            S[(size_t)i * dv + j] *= ai;
+    }
+    if (beta_mode == 0) {
+        /* prediction of v from the decayed state, then the rank-1 correction */
+        double *pred = scratch;
+        const double b = bk[0];
+        for (j = 0; j < dv; ++j) {
+            double s = 0.0;
+            for (i = 0; i < dk; ++i)
+                s += S[(size_t)i * dv + j] * k[i];
+            pred[j] = s;
+        }
+        for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] += b * kw[i] * (v[j] - pred[j]);
+    } else {
+        /* (I - wt kt^T) X + wt vt^T with kt = sqrt(beta^k) k, wt = sqrt(beta^k) kw,
+         * vt = sqrt(beta^v) v */
+        double *kt = scratch, *wt = scratch + dk, *vt = scratch + 2 * dk, *r = vt + dv;
+        const double *bvv = (beta_mode == 1) ? bk : bv;
+        for (i = 0; i < dk; ++i) {
+            kt[i] = sqrt(bk[i]) * k[i];
+            wt[i] = sqrt(bk[i]) * kw[i];
+        }
+        for (j = 0; j < dv; ++j)
+            vt[j] = sqrt(bvv[j]) * v[j];
+        for (j = 0; j < dv; ++j) { /* r = kt^T X */
+            double s = 0.0;
+            for (i = 0; i < dk; ++i)
+                s += kt[i] * S[(size_t)i * dv + j];
+            r[j] = s;
+        }
+        for (i = 0; i < dk; ++i)
+            for (j = 0; j < dv; ++j)
+                S[(size_t)i * dv + j] += wt[i] * (vt[j] - r[j]);
+    }
+}
+
+/* o = S^T q */
+static void ref_readout(int dk, int dv, const double *S, const double *q, double *o)
+{
+    int i, j;
+    for (j = 0; j < dv; ++j) {
+        double s = 0.0;
+        for (i = 0; i < dk; ++i)
+            s += S[(size_t)i * dv + j] * q[i];
+        o[j] = s;
+    }
+}
+
+static int ref_check(int B, int T, int H, int dk, int dv, int alpha_mode, int beta_mode)
+{
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dv < 1) return REF_EINVAL;
+    if (alpha_mode != 0 && alpha_mode != 1) return REF_EINVAL;
+    if (beta_mode < 0 || beta_mode > 2) return REF_EINVAL;
+    if (beta_mode == 1 && dk != dv) return REF_EINVAL;
+    return REF_OK;
+}
+
+/*
+ * Sequential forward over T tokens for the (batch, head) pairs listed in
+ * `heads` (indices b*H + h), or all of them when heads == NULL.  o rows and
+ * ST blocks of unlisted pairs are left untouched.  S0 == NULL starts from the
+ * zero state; ST == NULL skips the final-state store.  nthreads <= 0 uses the
+ * OpenMP default.
+ */
+int gdr_ref_forward(int B, int T, int H, int dk, int dv, int alpha_mode, int beta_mode,
+                    const double *q, const double *k, const double *kw, const double *v,
+                    const double *alpha, const double *beta_k, const double *beta_v,
+                    const double *S0, double *o, double *ST,
+                    const int *heads, int n_heads, int nthreads)
+{
+    int rc = ref_check(B, T, H, dk, dv, alpha_mode, beta_mode);
+    if (rc) return rc;
+    if (beta_mode == 2 && !beta_v) return REF_EINVAL;
+    if (!q || !k || !v || !alpha || !beta_k || !o) return REF_EINVAL;
+    const int total = heads ? n_heads : B * H;
+    const size_t sdim = (size_t)dk * dv;
+    const int a_n = alpha_mode ? dk : 1;
+    const int b_n = beta_mode ? dk : 1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(dynamic, 1)
+#endif
+    for (int idx = 0; idx < total; ++idx) {
+        const int bh = heads ? heads[idx] : idx;
+        if (bh < 0 || bh >= B * H) { failed = 1; continue; }
+        const int b = bh / H, h = bh % H;
+        double *S = (double *)malloc(sizeof(double) * (sdim + 2 * (size_t)dk + 2 * (size_t)dv));
+        if (!S) { failed = 1; continue; }
+        double *scratch = S + sdim;
+        if (S0) memcpy(S, S0 + (size_t)bh * sdim, sizeof(double) * sdim);
+        else memset(S, 0, sizeof(double) * sdim);
+        for (int t = 0; t < T; ++t) {
+            const size_t tok = ((size_t)b * T + t) * H + h;
+            const double *kt = k + tok * dk;
+            ref_step(dk, dv, S, alpha + tok * a_n, alpha_mode, beta_mode, beta_k + tok * b_n,
+                     beta_mode == 2 ? beta_v + tok * dv : NULL, kt, kw ? kw + tok * dk : kt,
+                     v + tok * dv, scratch);
+            ref_readout(dk, dv, S, q + tok * dk, o + tok * dv);
+        }
+        if (ST) memcpy(ST + (size_t)bh * sdim, S, sizeof(double) * sdim);
+        free(S);
+    }
+    return failed ? REF_EINVAL : REF_OK;
+}
+
+/*
+ * One decode step for every (batch, head): the same recurrence step applied
+ * to a caller-held state S [B, H, dk, dv] (updated in place), followed by the
+ * read-out o [B, H, dv].  Per-token inputs have the prefill layouts with T
+ * removed: q, k, kw [B, H, dk], v [B, H, dv], alpha [B, H] or [B, H, dk], ...
+ */
+int gdr_ref_decode_step(int B, int H, int dk, int dv, int alpha_mode, int beta_mode,
+                        const double *q, const double *k, const double *kw, const double *v,
+                        const double *alpha, const double *beta_k, const double *beta_v,
+                        double *S, double *o, int nthreads)
+{
+    int rc = ref_check(B, 1, H, dk, dv, alpha_mode, beta_mode);
+    if (rc) return rc;
+    if (beta_mode == 2 && !beta_v) return REF_EINVAL;
+    if (!q || !k || !v || !alpha || !beta_k || !S || !o) return REF_EINVAL;
+    const size_t sdim = (size_t)dk * dv;
+    const int a_n = alpha_mode ? dk : 1;
+    const int b_n = beta_mode ? dk : 1;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        double scratch[4 * 1024];
+        if (2 * dk + 2 * dv > 4 * 1024) { failed = 1; continue; }
+        const double *kt = k + (size_t)bh * dk;
+        ref_step(dk, dv, S + (size_t)bh * sdim, alpha + (size_t)bh * a_n, alpha_mode, beta_mode,
+                 beta_k + (size_t)bh * b_n, beta_mode == 2 ? beta_v + (size_t)bh * dv : NULL, kt,
+                 kw ? kw + (size_t)bh * dk : kt, v + (size_t)bh * dv, scratch);
+        ref_readout(dk, dv, S + (size_t)bh * sdim, q + (size_t)bh * dk, o + (size_t)bh * dv);
+    }
+    return failed ? REF_EINVAL : REF_OK;
+}
+
+int gdr_ref_max_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
