@@ -1,0 +1,169 @@
+"""Python binding of the gated delta-rule HIP library (libgdr.so, include/gdr.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C-ABI.  PyTorch supplies device memory and the current
+stream.  The functions with the C names (``gdr_chunk_fwd``, ``gdr_decode_step``,
+``gdr_chunk_fwd_workspace_size``, ``gdr_chunk_fwd_path``, ``gdr_status_string``)
+take a ``Desc`` and tensors (or None) and return the C status code;
+``chunk_fwd`` and ``decode_step`` allocate outputs and raise on a non-OK
+status.
+
+The library must have been built (``python -m gated_delta_rule_84_amd.build``);
+importing this package without it raises ImportError.  There is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch  # loads the HIP runtime the library binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EWORKSPACE, GDR_EHIP = 0, -1, -2, -3, -4
+GDR_BF16, GDR_F32 = 0, 1
+GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1
+GDR_BETA_SCALAR, GDR_BETA_SHARED, GDR_BETA_KV = 0, 1, 2
+GDR_FLAG_GENERIC_PATH = 0x1
+PATH_MFMA, PATH_VALU = 1, 2
+
+
+class Desc(ctypes.Structure):
+    """Mirror of ``gdr_desc``."""
+
+    _fields_ = [(n, ctypes.c_int32) for n in
+                ("B", "T", "H", "dk", "dv", "chunk", "io_dtype", "gate_dtype", "alpha_mode",
+                 "beta_mode", "flags")]
+
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_84_amd.build`")
+_lib = ctypes.CDLL(LIB_PATH)
+_vp = ctypes.c_void_p
+_dp = ctypes.POINTER(Desc)
+_lib.gdr_chunk_fwd_workspace_size.argtypes = [_dp]
+_lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_size_t
+_lib.gdr_chunk_fwd.argtypes = [_dp] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
+_lib.gdr_chunk_fwd.restype = ctypes.c_int
+_lib.gdr_decode_step.argtypes = [_dp] + [_vp] * 9 + [_vp]
+_lib.gdr_decode_step.restype = ctypes.c_int
+_lib.gdr_chunk_fwd_path.argtypes = [_dp]
+_lib.gdr_chunk_fwd_path.restype = ctypes.c_int
+_lib.gdr_status_string.argtypes = [ctypes.c_int]
+_lib.gdr_status_string.restype = ctypes.c_char_p
+_lib.gdr_version.argtypes = []
+_lib.gdr_version.restype = ctypes.c_int
+
+EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
+            "gdr_status_string", "gdr_version")
+
+
+class GdrError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {gdr_status_string(status)} ({status})")
+        self.status = status
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+# ---------------------------------------------------------------------------
+# the C entry points, one to one
+# ---------------------------------------------------------------------------
+
+def gdr_version() -> int:
+    return int(_lib.gdr_version())
+
+
+def gdr_status_string(status: int) -> str:
+    return _lib.gdr_status_string(int(status)).decode()
+
+
+def gdr_chunk_fwd_workspace_size(desc: Desc) -> int:
+    return int(_lib.gdr_chunk_fwd_workspace_size(ctypes.byref(desc)))
+
+
+def gdr_chunk_fwd_path(desc: Desc) -> int:
+    return int(_lib.gdr_chunk_fwd_path(ctypes.byref(desc)))
+
+
+def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace,
+                  workspace_bytes: int, stream=None) -> int:
+    return int(_lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
+                                  _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST),
+                                  _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
+    return int(_lib.gdr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
+                                    _ptr(beta_k), _ptr(beta_v), _ptr(S), _ptr(o), _stream(stream)))
+
+
+# ---------------------------------------------------------------------------
+# convenience wrappers (allocate outputs, raise on error)
+# ---------------------------------------------------------------------------
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GDR_BF16
+    if t.dtype == torch.float32:
+        return GDR_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, generic=False) -> Desc:
+    """Descriptor from tensor shapes: prefill q [B, T, H, dk], decode q [B, H, dk]."""
+    if decode:
+        B, H, dk = q.shape
+        T = 1
+        alpha_ch = alpha.dim() == 3
+        beta_vec = beta_k.dim() == 3
+    else:
+        B, T, H, dk = q.shape
+        alpha_ch = alpha.dim() == 4
+        beta_vec = beta_k.dim() == 4
+    beta_mode = GDR_BETA_KV if beta_v is not None else (GDR_BETA_SHARED if beta_vec else GDR_BETA_SCALAR)
+    return Desc(B=B, T=T, H=H, dk=dk, dv=v.shape[-1], chunk=chunk, io_dtype=_dtype_code(q),
+                gate_dtype=_dtype_code(alpha), alpha_mode=GDR_ALPHA_CHANNEL if alpha_ch else GDR_ALPHA_SCALAR,
+                beta_mode=beta_mode, flags=GDR_FLAG_GENERIC_PATH if generic else 0)
+
+
+def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=64, want_state=True,
+              out=None, final_state=None, workspace=None, generic=False, stream=None):
+    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None)."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic)
+    o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    ST = final_state
+    if ST is None and want_state:
+        ST = torch.empty((desc.B, desc.H, desc.dk, desc.dv), dtype=torch.float32, device=q.device)
+    need = gdr_chunk_fwd_workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = gdr_chunk_fwd(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace, wbytes, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd")
+    return o, ST
+
+
+def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, stream=None):
+    """One token for every (b, h); S [B, H, dk, dv] fp32 is updated in place.  Returns o [B, H, dv]."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, decode=True)
+    o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    rc = gdr_decode_step(desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_decode_step")
+    return o
+
+
+def loaded_library_path() -> str:
+    return LIB_PATH

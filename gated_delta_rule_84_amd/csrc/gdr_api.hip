@@ -1,0 +1,201 @@
+// gdr_api.hip -- the C-ABI entry points declared in include/gdr.h: host-side
+// validation, path selection and launches on the caller's stream.
+#include <stdint.h>
+#include <string.h>
+
+#include "gdr.h"
+#include "gdr_internal.hpp"
+
+namespace gdr {
+size_t chunk_valu_lds_bytes(int dk, int C);
+
+namespace {
+
+__global__ void state_copy_kernel(const float *__restrict__ src, float *__restrict__ dst, long n) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n) dst[i] = src ? src[i] : 0.f;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Byte ranges [a, a + na) and [b, b + nb) intersect (both non-empty).
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+    if (!a || !b || na == 0 || nb == 0) return false;
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+int check_desc(const gdr_desc *d, bool prefill) {
+    if (!d) return GDR_EINVAL;
+    if (d->B < 0 || d->H < 0 || (prefill && d->T < 0)) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->alpha_mode != GDR_ALPHA_SCALAR && d->alpha_mode != GDR_ALPHA_CHANNEL) return GDR_EINVAL;
+    if (d->beta_mode < GDR_BETA_SCALAR || d->beta_mode > GDR_BETA_KV) return GDR_EINVAL;
+    if (d->flags & ~GDR_FLAG_GENERIC_PATH) return GDR_EINVAL;
+    if (d->beta_mode == GDR_BETA_SHARED && d->dk != d->dv) return GDR_EINVAL;
+    if (d->dk < 8 || d->dk > 128 || (d->dk & 7) || d->dv < 8 || d->dv > 128 || (d->dv & 7))
+        return GDR_EUNSUPPORTED;
+    if (prefill && d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDR_EUNSUPPORTED;
+    const long long bh = (long long)d->B * d->H;
+    if (bh > 0x7fffffffLL) return GDR_EUNSUPPORTED;
+    return GDR_OK;
+}
+
+ChunkParams chunk_params(const gdr_desc *d) {
+    ChunkParams p;
+    memset(&p, 0, sizeof(p));
+    p.B = d->B; p.T = d->T; p.H = d->H; p.dk = d->dk; p.dv = d->dv; p.C = d->chunk;
+    p.io_bf16 = d->io_dtype == GDR_BF16;
+    p.gate_bf16 = d->gate_dtype == GDR_BF16;
+    p.alpha_ch = d->alpha_mode == GDR_ALPHA_CHANNEL;
+    p.beta_mode = d->beta_mode;
+    return p;
+}
+
+int select_path(const gdr_desc *d, const ChunkParams &p) {
+    if (!(d->flags & GDR_FLAG_GENERIC_PATH) && chunk_mfma_supported(p)) return 1;
+    return 2;
+}
+
+int device_lds_limit() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return -1;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) return -1;
+    return v;
+}
+
+}  // namespace
+}  // namespace gdr
+
+using namespace gdr;
+
+extern "C" {
+
+int gdr_version(void) { return (1 << 16) | 0; }
+
+const char *gdr_status_string(int s) {
+    switch (s) {
+    case GDR_OK: return "GDR_OK: success";
+    case GDR_EINVAL: return "GDR_EINVAL: invalid argument (NULL pointer, bad enum, negative size, "
+                            "misaligned or overlapping buffer, beta layout not matching beta_mode)";
+    case GDR_EUNSUPPORTED: return "GDR_EUNSUPPORTED: shape not implemented (dk, dv must be multiples "
+                                  "of 8 in [8, 128]; chunk must be 16, 32 or 64)";
+    case GDR_EWORKSPACE: return "GDR_EWORKSPACE: workspace missing or smaller than "
+                                "gdr_chunk_fwd_workspace_size()";
+    case GDR_EHIP: return "GDR_EHIP: the HIP runtime reported an error";
+    default: return "unknown gdr status";
+    }
+}
+
+int gdr_chunk_fwd_path(const gdr_desc *d) {
+    const int rc = check_desc(d, true);
+    if (rc) return rc;
+    return select_path(d, chunk_params(d));
+}
+
+size_t gdr_chunk_fwd_workspace_size(const gdr_desc *d) {
+    if (check_desc(d, true)) return 0;
+    const ChunkParams p = chunk_params(d);
+    return select_path(d, p) == 1 ? chunk_mfma_workspace(p) : 0;
+}
+
+int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                  const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                  void *o, float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+    int rc = check_desc(d, true);
+    if (rc) return rc;
+    ChunkParams p = chunk_params(d);
+    const long long ntok = (long long)d->B * d->T * d->H;
+    const size_t es = p.io_bf16 ? 2 : 4, gs = p.gate_bf16 ? 2 : 4;
+    const size_t nq = ntok * d->dk * es, nv = ntok * d->dv * es;
+    const size_t na = ntok * (p.alpha_ch ? d->dk : 1) * gs;
+    const size_t nbk = ntok * (d->beta_mode ? d->dk : 1) * gs, nbv = ntok * d->dv * gs;
+    const size_t ns = (size_t)d->B * d->H * d->dk * d->dv * sizeof(float);
+    if ((d->beta_mode == GDR_BETA_KV) != (beta_v != nullptr)) return GDR_EINVAL;
+    if (ntok > 0) {
+        if (!q || !k || !v || !alpha || !beta_k || !o) return GDR_EINVAL;
+        const void *ptrs[] = {q, k, k_w, v, alpha, beta_k, beta_v, o};
+        for (const void *x : ptrs)
+            if (x && !aligned16(x)) return GDR_EINVAL;
+        const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v, S0};
+        const size_t lens[] = {nq, nq, nq, nv, na, nbk, nbv, ns};
+        for (int i = 0; i < 8; ++i)
+            if (overlaps(o, nv, ins[i], lens[i])) return GDR_EINVAL;
+        if (ST && overlaps(o, nv, ST, ns)) return GDR_EINVAL;
+    }
+    if ((S0 && !aligned16(S0)) || (ST && !aligned16(ST))) return GDR_EINVAL;
+    if (ST && S0 && ST != S0 && overlaps(ST, ns, S0, ns)) return GDR_EINVAL;
+    if (ST && ntok > 0) {
+        const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v};
+        const size_t lens[] = {nq, nq, nq, nv, na, nbk, nbv};
+        for (int i = 0; i < 7; ++i)
+            if (overlaps(ST, ns, ins[i], lens[i])) return GDR_EINVAL;
+    }
+    const int path = select_path(d, p);
+    const size_t ws_need = path == 1 ? chunk_mfma_workspace(p) : 0;
+    if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned16(workspace)))
+        return GDR_EWORKSPACE;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    const long long nbh = (long long)d->B * d->H;
+    if (nbh == 0) return GDR_OK;
+    if (path == 2 && d->T > 0) {
+        const int lim = device_lds_limit();
+        if (lim < 0) return GDR_EHIP;
+        if (chunk_valu_lds_bytes(d->dk, d->chunk) > (size_t)lim) return GDR_EUNSUPPORTED;
+    }
+    if (d->T == 0) {
+        if (!ST || ST == S0) return GDR_OK;
+        const long n = (long)(ns / sizeof(float));
+        const float *src = S0;
+        float *dst = ST;
+        long nn = n;
+        void *args[] = {&src, &dst, &nn};
+        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&state_copy_kernel),
+                                             dim3((unsigned)((n + 255) / 256)), dim3(256), args, 0, st);
+        return e == hipSuccess ? GDR_OK : GDR_EHIP;
+    }
+    p.q = q; p.k = k; p.kw = k_w ? k_w : k; p.v = v;
+    p.alpha = alpha; p.beta_k = beta_k; p.beta_v = beta_v;
+    p.S0 = S0; p.o = o; p.ST = ST; p.ws = workspace;
+    const hipError_t e = path == 1 ? launch_chunk_mfma(p, st) : launch_chunk_valu(p, st);
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                    const void *alpha, const void *beta_k, const void *beta_v, float *S, void *o,
+                    void *stream) {
+    int rc = check_desc(d, false);
+    if (rc) return rc;
+    if ((d->beta_mode == GDR_BETA_KV) != (beta_v != nullptr)) return GDR_EINVAL;
+    const long long nbh = (long long)d->B * d->H;
+    if (nbh == 0) return GDR_OK;
+    if (!q || !k || !v || !alpha || !beta_k || !S || !o) return GDR_EINVAL;
+    const void *ptrs[] = {q, k, k_w, v, alpha, beta_k, beta_v, S, o};
+    for (const void *x : ptrs)
+        if (x && !aligned16(x)) return GDR_EINVAL;
+    const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;
+    const size_t no = nbh * d->dv * es, ns = nbh * d->dk * d->dv * sizeof(float);
+    const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v};
+    const size_t lens[] = {nbh * d->dk * es, nbh * d->dk * es, nbh * d->dk * es, no,
+                           nbh * (d->alpha_mode ? d->dk : 1) * gs, nbh * (d->beta_mode ? d->dk : 1) * gs,
+                           nbh * d->dv * gs};
+    for (int i = 0; i < 7; ++i)
+        if (overlaps(o, no, ins[i], lens[i]) || overlaps(S, ns, ins[i], lens[i])) return GDR_EINVAL;
+    if (overlaps(o, no, S, ns)) return GDR_EINVAL;
+
+    DecodeParams p;
+    memset(&p, 0, sizeof(p));
+    p.B = d->B; p.H = d->H; p.dk = d->dk; p.dv = d->dv;
+    p.io_bf16 = d->io_dtype == GDR_BF16;
+    p.gate_bf16 = d->gate_dtype == GDR_BF16;
+    p.alpha_ch = d->alpha_mode == GDR_ALPHA_CHANNEL;
+    p.beta_mode = d->beta_mode;
+    p.q = q; p.k = k; p.kw = k_w ? k_w : k; p.v = v;
+    p.alpha = alpha; p.beta_k = beta_k; p.beta_v = beta_v;
+    p.S = S; p.o = o;
+    const hipError_t e = launch_decode(p, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+}  // extern "C"

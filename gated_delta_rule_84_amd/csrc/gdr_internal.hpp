@@ -1,0 +1,41 @@
+// gdr_internal.hpp -- parameter blocks and launcher declarations shared by the
+// host API (gdr_api.cpp) and the kernel translation units.  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+// Parameters of one prefill call, already validated by the host API.
+struct ChunkParams {
+    int B, T, H, dk, dv, C;
+    int io_bf16;    // q, k, k_w, v, o are bf16 (else fp32)
+    int gate_bf16;  // alpha, beta_k, beta_v are bf16 (else fp32)
+    int alpha_ch;   // alpha is per key channel
+    int beta_mode;  // 0 scalar, 1 shared vector, 2 separate k / v vectors
+    const void *q, *k, *kw, *v, *alpha, *beta_k, *beta_v;  // kw never NULL here (defaults to k)
+    const float *S0;  // may be NULL (zero state)
+    void *o;
+    float *ST;        // may be NULL
+    void *ws;         // workspace (path dependent)
+};
+
+// Parameters of one decode step.
+struct DecodeParams {
+    int B, H, dk, dv;
+    int io_bf16, gate_bf16, alpha_ch, beta_mode;
+    const void *q, *k, *kw, *v, *alpha, *beta_k, *beta_v;
+    float *S;
+    void *o;
+};
+
+// Launchers (defined next to their kernels).  They only enqueue work.
+hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
+hipError_t launch_chunk_valu(const ChunkParams &p, hipStream_t s);
+size_t chunk_mfma_workspace(const ChunkParams &p);
+bool chunk_mfma_supported(const ChunkParams &p);
+hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t s);
+hipError_t launch_state_copy(const float *S0, float *ST, long n, hipStream_t s);
+
+}  // namespace gdr

@@ -1,0 +1,160 @@
+/*
+ * gdr.h -- C-ABI of the gated delta-rule library for AMD Instinct MI355X (gfx950).
+ *
+ * The library evaluates the gated delta-rule state recurrence.  For one
+ * (batch b, head h) the state S is a dk x dv fp32 matrix (row i = key
+ * channel, column j = value channel).  Each token t applies
+ *
+ *     X_t = Diag(alpha_t) S_{t-1}                                   (forget gate)
+ *     S_t = X_t + w_t (vh_t - X_t^T u_t)^T                          (rank-1 delta write)
+ *     o_t = S_t^T q_t                                               (read-out after the write)
+ *
+ * with erase key u = sqrt(beta^k) (.) k, write key w = sqrt(beta^k) (.) k_w and
+ * written value vh = sqrt(beta^v) (.) v; a scalar beta broadcasts.  This one
+ * step covers the variants on the source pages:
+ *   - Gated DeltaNet: scalar alpha and beta, k_w = k
+ *       [FG2-GDN page, section 1; SDM page, Mecanismo Central item 3];
+ *   - Kimi Delta Attention: one alpha per key channel
+ *       [FG2-GDN page, section 1];
+ *   - FG2-GDN: one beta vector absorbed as sqrt(beta) into k and v (dk == dv)
+ *       [FG2-GDN page, section 2.A, state-update equation];
+ *   - FG2-GDN+: separate erase and write strengths beta^k, beta^v
+ *       [FG2-GDN page, section 2.B];
+ *   - OSDN: write key k_w = d (.) k, the diagonally right-preconditioned
+ *       online-gradient step [OSDN page, section 2.1, both update equations].
+ * Prefill runs the chunkwise-parallel WY / UT-transform form of the same
+ * recurrence (the block Gram matrix of the write and erase keys, its
+ * unit-lower-triangular inverse, and the intra-chunk scores: FG2-GDN page,
+ * section 3; OSDN page, section 2.1); decode applies one step to a resident state
+ * [OSDN page, section 1; delta-mem page, section 2.A].
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, keeps no pointer after a call returns and has no
+ *     global mutable state (calls from several host threads are safe).
+ *   - Every tensor is dense, row-major, 16-byte aligned.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
+ *     default stream).  Nothing synchronises inside the library.
+ *   - Arguments are validated on the host before anything is enqueued; on a
+ *     non-OK status nothing has been launched and no output was touched.
+ *   - NaN / Inf inputs propagate; they are not detected.
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Return codes. */
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_EINVAL = -1,       /* NULL required pointer, bad enum, negative size, misalignment,
+                              aliasing output, beta layout inconsistent with beta_mode */
+    GDR_EUNSUPPORTED = -2, /* shape outside what the kernels implement (see below) */
+    GDR_EWORKSPACE = -3,   /* workspace missing or smaller than gdr_chunk_fwd_workspace_size */
+    GDR_EHIP = -4          /* the HIP runtime reported an error at launch */
+} gdr_status;
+
+/* Element types. */
+typedef enum gdr_dtype {
+    GDR_BF16 = 0,          /* bfloat16; the library rounds to nearest-even when it stores one */
+    GDR_F32 = 1
+} gdr_dtype;
+
+/* Forget-gate layout.  SCALAR: alpha [.., H]   CHANNEL: alpha [.., H, dk]. */
+typedef enum gdr_alpha_mode { GDR_ALPHA_SCALAR = 0, GDR_ALPHA_CHANNEL = 1 } gdr_alpha_mode;
+
+/* Write-strength layout.
+ *   SCALAR: beta_k [.., H], beta_v must be NULL           (GDN / KDA / OSDN)
+ *   SHARED: beta_k [.., H, dk] used for k and v, dk == dv,
+ *           beta_v must be NULL                           (FG2-GDN)
+ *   KV:     beta_k [.., H, dk] and beta_v [.., H, dv]     (FG2-GDN+) */
+typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_KV = 2 } gdr_beta_mode;
+
+/* Flags (gdr_desc.flags). */
+#define GDR_FLAG_GENERIC_PATH 0x1  /* prefill: use the fp32 vector-ALU chunk kernel even where
+                                      the bf16 matrix-core kernel applies (testing aid) */
+
+/* Problem descriptor.
+ *   B, H  >= 0; T >= 0 (prefill only; ignored by decode).
+ *   dk, dv: multiples of 8 in [8, 128]                      (else GDR_EUNSUPPORTED)
+ *   chunk:  prefill chunk length, 16, 32 or 64              (else GDR_EUNSUPPORTED)
+ *   io_dtype:   element type of q, k, k_w, v and o
+ *   gate_dtype: element type of alpha, beta_k, beta_v
+ * The scalar-gate bf16 kernel on matrix cores serves io_dtype == GDR_BF16,
+ * dk == dv == 128, chunk == 64; every other accepted shape runs the fp32
+ * vector-ALU kernel.  With alpha_mode == CHANNEL the per-channel cumulative
+ * log-decay inside one chunk must stay above about -80 (fp32 exponent range
+ * of the factored decay); use a shorter chunk for faster-decaying inputs. */
+typedef struct gdr_desc {
+    int32_t B, T, H, dk, dv;
+    int32_t chunk;
+    int32_t io_dtype;
+    int32_t gate_dtype;
+    int32_t alpha_mode;
+    int32_t beta_mode;
+    int32_t flags;
+} gdr_desc;
+
+/* Bytes of device workspace gdr_chunk_fwd needs for `desc` (0 if none).
+ * Returns 0 for a descriptor gdr_chunk_fwd would reject. */
+size_t gdr_chunk_fwd_workspace_size(const gdr_desc *desc);
+
+/*
+ * Prefill: run T tokens for every (b, h) and write every read-out.
+ *
+ *   q, k      [B, T, H, dk]  io_dtype   (required)
+ *   k_w       [B, T, H, dk]  io_dtype   write key; NULL means k_w = k
+ *   v         [B, T, H, dv]  io_dtype   (required)
+ *   alpha     [B, T, H] or [B, T, H, dk]            gate_dtype (required)
+ *   beta_k    [B, T, H] or [B, T, H, dk]            gate_dtype (required)
+ *   beta_v    [B, T, H, dv]  gate_dtype, GDR_BETA_KV only, else NULL
+ *   S0        [B, H, dk, dv] fp32 initial state; NULL means zero
+ *   o         [B, T, H, dv]  io_dtype   output (required; must not overlap any input)
+ *   ST        [B, H, dk, dv] fp32 final state; NULL means not written.
+ *             ST == S0 is allowed (in-place resume); partial overlap is not.
+ *   workspace device scratch of at least gdr_chunk_fwd_workspace_size(desc) bytes
+ *             (may be NULL when that size is 0); its contents on entry do not matter.
+ *
+ * A T that is not a multiple of chunk is handled inside the kernels (the last
+ * chunk is shorter).  T == 0 writes ST = S0 (or zeros) and no o.  Results are
+ * deterministic: the same inputs give bit-identical outputs.
+ */
+int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
+                  const void *v, const void *alpha, const void *beta_k, const void *beta_v,
+                  const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
+                  void *stream);
+
+/*
+ * Decode: one token for every (b, h), applied in place to a resident state.
+ *
+ *   q, k, k_w [B, H, dk], v [B, H, dv]          io_dtype (k_w NULL means k)
+ *   alpha     [B, H] or [B, H, dk]              gate_dtype
+ *   beta_k    [B, H] or [B, H, dk]; beta_v [B, H, dv] (GDR_BETA_KV only)
+ *   S         [B, H, dk, dv] fp32, read and overwritten with the new state
+ *   o         [B, H, dv] io_dtype, o = S_new^T q (must not overlap any input)
+ * desc->T and desc->chunk are ignored.
+ */
+int gdr_decode_step(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
+                    const void *v, const void *alpha, const void *beta_k, const void *beta_v,
+                    float *S, void *o, void *stream);
+
+/* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
+ * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */
+int gdr_chunk_fwd_path(const gdr_desc *desc);
+
+/* Static, NUL-terminated description of a status code. */
+const char *gdr_status_string(int status);
+
+/* ABI version: (major << 16) | minor. */
+int gdr_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

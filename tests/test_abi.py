@@ -1,0 +1,154 @@
+"""The C-ABI library loads, exports every symbol include/gdr.h declares, and
+rejects bad arguments on the host with the documented status before anything
+is launched (these calls never reach the GPU, so they run anywhere)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdr.h")
+
+
+@pytest.fixture(scope="module")
+def g():
+    import gated_delta_rule_84_amd as g
+
+    return g
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(g):
+    declared = _declared_functions()
+    assert {"gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_workspace_size"} <= set(declared)
+    out = subprocess.run(["nm", "-D", "--defined-only", g.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT (gdr_[a-z0-9_]+)", out))
+    missing = [f for f in declared if f not in exported]
+    assert not missing, f"declared but not exported: {missing}"
+    assert set(g.EXPORTED) == set(declared)
+
+
+def test_header_compiles_as_c():
+    src = '#include "gdr.h"\nint main(void){gdr_desc d={0};(void)d;return (int)sizeof(gdr_desc);}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.dirname(HEADER), "-x", "c", "-",
+                        "-fsyntax-only"], input=src, text=True, capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_version_and_status_strings(g):
+    assert g.gdr_version() >> 16 == 1
+    for s in (g.GDR_OK, g.GDR_EINVAL, g.GDR_EUNSUPPORTED, g.GDR_EWORKSPACE, g.GDR_EHIP):
+        assert g.gdr_status_string(s).startswith("GDR_")
+    assert "unknown" in g.gdr_status_string(12345)
+
+
+def _desc(g, **kw):
+    base = dict(B=2, T=100, H=3, dk=128, dv=128, chunk=64, io_dtype=g.GDR_BF16, gate_dtype=g.GDR_F32,
+                alpha_mode=g.GDR_ALPHA_SCALAR, beta_mode=g.GDR_BETA_SCALAR, flags=0)
+    base.update(kw)
+    return g.Desc(**base)
+
+
+class FakePtr:
+    """A stand-in tensor: only data_ptr() is used by the binding and the
+    library never dereferences it on a rejected call."""
+
+    def __init__(self, addr):
+        self.addr = addr
+
+    def data_ptr(self):
+        return self.addr
+
+
+def _ptrs(start=0x10000000, n=10, step=0x1000000):
+    return [FakePtr(start + i * step) for i in range(n)]
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("B", -1, -1), ("T", -1, -1), ("H", -1, -1),
+    ("dk", 0, -2), ("dk", 12, -2), ("dk", 136, -2), ("dv", 4, -2), ("dv", 256, -2),
+    ("chunk", 8, -2), ("chunk", 128, -2), ("chunk", 48, -2),
+    ("io_dtype", 7, -1), ("gate_dtype", -3, -1), ("alpha_mode", 2, -1), ("beta_mode", 3, -1),
+    ("flags", 0x10, -1),
+])
+def test_descriptor_validation(g, field, value, status):
+    d = _desc(g, **{field: value})
+    q, k, v, a, b, o, st = _ptrs(n=7)
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, o, st, None, 0, 0) == status
+    assert g.gdr_chunk_fwd_path(d) == status
+    assert g.gdr_chunk_fwd_workspace_size(d) == 0
+
+
+def test_shared_beta_needs_square(g):
+    d = _desc(g, dk=64, dv=128, beta_mode=g.GDR_BETA_SHARED)
+    q, k, v, a, b, o, st = _ptrs(n=7)
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, o, st, None, 0, 0) == g.GDR_EINVAL
+
+
+def test_null_and_misaligned_pointers(g):
+    d = _desc(g)
+    q, k, v, a, b, o, st = _ptrs(n=7)
+    assert g.gdr_chunk_fwd(d, None, k, None, v, a, b, None, None, o, st, None, 0, 0) == g.GDR_EINVAL
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, None, st, None, 0, 0) == g.GDR_EINVAL
+    assert g.gdr_chunk_fwd(d, FakePtr(q.addr + 8), k, None, v, a, b, None, None, o, st, None, 0, 0) \
+        == g.GDR_EINVAL
+    # beta_v given without the KV layout, and missing with it
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, FakePtr(0x20000000), None, o, st, None, 0, 0) \
+        == g.GDR_EINVAL
+    dkv = _desc(g, beta_mode=g.GDR_BETA_KV)
+    assert g.gdr_chunk_fwd(dkv, q, k, None, v, a, b, None, None, o, st, None, 0, 0) == g.GDR_EINVAL
+
+
+def test_output_may_not_alias_inputs(g):
+    d = _desc(g)
+    q, k, v, a, b, o, st = _ptrs(n=7)
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, q, st, None, 0, 0) == g.GDR_EINVAL
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, FakePtr(v.addr + 64), st, None, 0, 0) \
+        == g.GDR_EINVAL
+    # partial overlap of S0 and ST is rejected
+    s0 = FakePtr(0x50000000)
+    assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, s0, o, FakePtr(s0.addr + 256), None, 0, 0) \
+        == g.GDR_EINVAL
+
+
+def test_decode_validation(g):
+    d = _desc(g, T=1)
+    q, k, v, a, b, S, o = _ptrs(n=7)
+    assert g.gdr_decode_step(_desc(g, dk=20), q, k, None, v, a, b, None, S, o, 0) == g.GDR_EUNSUPPORTED
+    assert g.gdr_decode_step(d, q, k, None, v, a, None, None, S, o, 0) == g.GDR_EINVAL
+    assert g.gdr_decode_step(d, q, k, None, v, a, b, None, S, S, 0) == g.GDR_EINVAL
+    assert g.gdr_decode_step(d, q, k, None, v, a, b, None, FakePtr(S.addr + 4), o, 0) == g.GDR_EINVAL
+    # empty batch is a no-op even with NULL pointers
+    assert g.gdr_decode_step(_desc(g, B=0), None, None, None, None, None, None, None, None, None, 0) == g.GDR_OK
+
+
+def test_empty_batch_is_noop(g):
+    d = _desc(g, B=0)
+    assert g.gdr_chunk_fwd(d, None, None, None, None, None, None, None, None, None, None, None, 0, 0) == g.GDR_OK
+
+
+def test_path_selection(g):
+    assert g.gdr_chunk_fwd_path(_desc(g, io_dtype=g.GDR_F32)) == g.PATH_VALU
+    assert g.gdr_chunk_fwd_path(_desc(g, dk=64, dv=64)) == g.PATH_VALU
+    assert g.gdr_chunk_fwd_path(_desc(g, flags=g.GDR_FLAG_GENERIC_PATH)) == g.PATH_VALU
+
+
+def test_binding_fails_loudly_without_library(tmp_path):
+    """Importing the binding with no built library raises; nothing falls back."""
+    import shutil
+    import sys
+
+    pkg = tmp_path / "gated_delta_rule_84_amd"
+    pkg.mkdir()
+    shutil.copy(os.path.join(ROOT, "gated_delta_rule_84_amd", "__init__.py"), pkg / "__init__.py")
+    code = "import gated_delta_rule_84_amd"
+    r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
+    assert r.returncode != 0 and "ImportError" in r.stderr
