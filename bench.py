@@ -1,0 +1,250 @@
+#!/usr/bin/env python3
+"""Throughput of the gated delta-rule hot path on one MI355X.
+
+One step = one gdr_chunk_fwd over the batch B=4, H=16, T=4096, dk=dv=128,
+chunk 64 (bf16 q/k/v, fp32 scalar gates, zero initial state, o and the final
+state written), inputs resident in HBM.  The decode step (B=512, H=16,
+d=128, 256 steps replayed as one HIP graph, and the r=8 small-state case) is
+timed in the same run and reported under "decode".
+
+Prints ONE JSON line.  `value` is prefill tokens/s (B*T per step).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "gdr_device.hpp",
+                  "gdr_internal.hpp"]
+
+
+def prefill_flops_per_token_head(C, dk, dv):
+    """Algorithmic flops of the chunked WY / UT form per token per head:
+    Gram C*dk, UT inverse C^2/3, W' C*dk, U' C*dv, intra scores C*dk, P.Delta C*dv
+    (triangular products at their nonzero half, 2 flops per MAC) plus the three
+    dk x dv state products (W'S, QS, W^T Delta) at 2*dk*dv each."""
+    return 3 * C * dk + 2 * C * dv + C * C / 3.0 + 6 * dk * dv
+
+
+def prefill_bytes(w):
+    """Every input read once, every output written once."""
+    io = 2 if w.io == "bf16" else 4
+    g = 2 if w.gate == "bf16" else 4
+    ntok = w.B * w.T * w.H
+    n = ntok * (2 * w.dk + w.dv) * io                    # q, k, v
+    n += ntok * (w.dk if w.write_key else 0) * io        # k_w
+    n += ntok * (w.dk if w.alpha_mode else 1) * g        # alpha
+    n += ntok * (w.dk if w.beta_mode else 1) * g         # beta_k
+    n += ntok * (w.dv if w.beta_mode == 2 else 0) * g    # beta_v
+    n += ntok * w.dv * io                                # o
+    st = w.B * w.H * w.dk * w.dv * 4
+    n += st * (2 if w.s0_std > 0 else 1)                 # S0 (if any), ST
+    return n
+
+
+def decode_bytes_per_step(w):
+    io = 2 if w.io == "bf16" else 4
+    g = 2 if w.gate == "bf16" else 4
+    nbh = w.B * w.H
+    return nbh * (2 * w.dk * w.dv * 4 + (2 * w.dk + 2 * w.dv) * io + 2 * g)
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "gated_delta_rule_84_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(name, digest):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{name}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_digest") != digest:
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, x, budget_heads):
+    """The fp64 oracle as it stands, on a bounded sample of the same batch:
+    `budget_heads` (b, h) pairs over the full T."""
+    import numpy as np
+
+    import gdr_inputs as gi
+    import oracle
+
+    oracle.build(force=False)
+    f = gi.prefill_f64(w, x)
+    heads = list(range(min(budget_heads, w.B * w.H)))
+    threads = min(len(heads), os.cpu_count() or 1, 16)
+    t0 = time.perf_counter()
+    oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta_k"], heads=heads, nthreads=threads)
+    dt = time.perf_counter() - t0
+    tokens = w.T * len(heads) / w.H  # tokens carry all H heads in the GPU metric
+    return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(heads)} of {w.B * w.H} (batch, head) pairs x {w.T} tokens, fp64 sequential "
+                      f"recurrence, OpenMP over pairs, {dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--decode-reps", type=int, default=5)
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-heads", type=int, default=64)
+    ap.add_argument("--generic", action="store_true", help="force the fp32 vector-ALU prefill kernel")
+    ap.add_argument("--only-prefill", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(sequences shard over (batch, head) with no communication).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import gated_delta_rule_84_amd as g
+    import gdr_inputs as gi
+    from gated_delta_rule_84_amd.graph import DecodeGraph
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        n = 1 << 28  # 2^28 fp32 = 1 GiB read + 1 GiB written per copy
+        a = torch.ones(n, dtype=torch.float32, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
+        return
+    w = gi.GDN_PREFILL
+    x = gi.make_prefill(w)
+    d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
+         for k in x}
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk,
+                       generic=args.generic)
+    path = g.gdr_chunk_fwd_path(desc)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    wsz = g.gdr_chunk_fwd_workspace_size(desc)
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        rc = g.gdr_chunk_fwd(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"], d["beta_v"],
+                             d["S0"], o, ST, ws, wsz, stream)
+        if rc != g.GDR_OK:
+            raise g.GdrError(rc, "gdr_chunk_fwd")
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(stream)
+        step()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_event = sum(launch_ms) / len(launch_ms)
+    ms_step = wall * 1e3 / args.steps
+
+    # cold-cache time: flush L2 and the Infinity Cache between launches
+    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+    cold = []
+    for _ in range(5):
+        flush.fill_(1.0)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        torch.cuda.synchronize()
+        cold.append(a.elapsed_time(b))
+    del flush
+    ms_cold = sorted(cold)[len(cold) // 2]
+
+    tokens = w.B * w.T
+    flops = prefill_flops_per_token_head(w.chunk, w.dk, w.dv) * tokens * w.H
+    nbytes = prefill_bytes(w)
+    digest = kernel_source_digest()
+    traffic = load_traffic(w.name, digest)
+    roof = {"bound": "hbm", "achieved": nbytes / (ms_event * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "traffic": traffic}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    out = {
+        "metric": "tokens/s gated-delta chunk fwd (H=16,d=128,T=4096); % MFMA peak; decode GB/s",
+        "value": tokens / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "gates": "fp32 scalar alpha, beta", "S0": "zero", "global_batch": w.B, "seq_len": w.T,
+                   "parallelism": "single GPU", "kernel_path": {1: "bf16-mfma", 2: "fp32-valu"}[path]},
+        "roofline": roof,
+        "mfma_frac": flops / (ms_event * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+        "prefill_detail": {"ms_event_mean": ms_event, "ms_event_min": min(launch_ms), "ms_cold_median": ms_cold,
+                           "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+                           "gbs_cold": nbytes / (ms_cold * 1e-3) / 1e9, "kernel_source_digest": digest},
+    }
+
+    if not args.only_prefill:
+        dec = {}
+        for wd in (gi.DECODE_B512.scaled(steps=args.decode_steps), gi.DECODE_DMEM_R8.scaled(steps=args.decode_steps)):
+            xd = gi.make_decode(wd)
+            dd = {k: gi.to_torch(xd[k], wd.io if k in ("q", "k", "k_w", "v") else (wd.gate if k != "S" else gi.F32))
+                  for k in xd}
+            S = dd["S"].clone()
+            graph = DecodeGraph(S, dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta_k"], k_w=dd["k_w"],
+                                beta_v=dd["beta_v"])
+            graph.replay()
+            torch.cuda.synchronize()
+            times = []
+            for _ in range(args.decode_reps):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                graph.replay()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            ms = sorted(times)[len(times) // 2]
+            us_step = ms * 1e3 / wd.steps
+            bps = decode_bytes_per_step(wd)
+            gbs = bps / (us_step * 1e-6) / 1e9
+            dec[wd.name] = {"us_per_step": us_step, "tokens_per_s": wd.B / (us_step * 1e-6),
+                            "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "steps_per_graph": wd.steps,
+                            "bytes_per_step": bps}
+            del graph, dd, S
+        out["decode"] = dec
+
+    if not args.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,6 +17,7 @@ __global__ void state_copy_kernel(const float *__restrict__ src, float *__restri
 }
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 
 // Byte ranges [a, a + na) and [b, b + nb) intersect (both non-empty).
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
@@ -115,9 +116,12 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k
     if ((d->beta_mode == GDR_BETA_KV) != (beta_v != nullptr)) return GDR_EINVAL;
     if (ntok > 0) {
         if (!q || !k || !v || !alpha || !beta_k || !o) return GDR_EINVAL;
-        const void *ptrs[] = {q, k, k_w, v, alpha, beta_k, beta_v, o};
-        for (const void *x : ptrs)
+        const void *vec[] = {q, k, k_w, v, o};
+        for (const void *x : vec)
             if (x && !aligned16(x)) return GDR_EINVAL;
+        const void *gates[] = {alpha, beta_k, beta_v};
+        for (const void *x : gates)
+            if (x && !aligned_to(x, gs)) return GDR_EINVAL;
         const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v, S0};
         const size_t lens[] = {nq, nq, nq, nv, na, nbk, nbv, ns};
         for (int i = 0; i < 8; ++i)
@@ -171,10 +175,13 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     const long long nbh = (long long)d->B * d->H;
     if (nbh == 0) return GDR_OK;
     if (!q || !k || !v || !alpha || !beta_k || !S || !o) return GDR_EINVAL;
-    const void *ptrs[] = {q, k, k_w, v, alpha, beta_k, beta_v, S, o};
-    for (const void *x : ptrs)
-        if (x && !aligned16(x)) return GDR_EINVAL;
     const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;
+    const void *vec[] = {q, k, k_w, v, S, o};
+    for (const void *x : vec)
+        if (x && !aligned16(x)) return GDR_EINVAL;
+    const void *gates[] = {alpha, beta_k, beta_v};
+    for (const void *x : gates)
+        if (x && !aligned_to(x, gs)) return GDR_EINVAL;
     const size_t no = nbh * d->dv * es, ns = nbh * d->dk * d->dv * sizeof(float);
     const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v};
     const size_t lens[] = {nbh * d->dk * es, nbh * d->dk * es, nbh * d->dk * es, no,

@@ -32,7 +32,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates nothing, keeps no pointer after a call returns and has no
  *     global mutable state (calls from several host threads are safe).
- *   - Every tensor is dense, row-major, 16-byte aligned.
+ *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
+ *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
+ *     alignment (so per-step slices of a gate array are accepted).
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL is the
  *     default stream).  Nothing synchronises inside the library.
  *   - Arguments are validated on the host before anything is enqueued; on a

@@ -1,0 +1,95 @@
+"""The bf16 matrix-core prefill path: its per-chunk workspace record (UT transform,
+intra-chunk scores, decay factors) against NumPy fp64 built from the same stored
+inputs, and the path selection.  The end-to-end parity of this path against the
+oracle is in test_gpu_prefill.py (every bf16 d=128 chunk-64 scalar-gate case
+selects it)."""
+import numpy as np
+import pytest
+
+import gdr_inputs as gi
+from tests.gpu_util import gpu, log, upload
+
+pytestmark = pytest.mark.gpu
+
+REC_BYTES = 25216  # per-chunk record: T bf16[64][64] | P hi bf16[64][64] | P lo | gam f32[64] | fac f32[64] | gC
+
+
+def _bf16(u16):
+    return gi.bf16_bits_to_f32(u16).astype(np.float64)
+
+
+@pytest.mark.parametrize("T,write_key", [(200, False), (128, True)])
+def test_prep_record_matches_numpy(T, write_key):
+    torch, g = gpu()
+    w = gi.GDN_PREFILL.scaled(B=1, T=T, H=2, write_key=write_key, seed=51)
+    x = gi.make_prefill(w)
+    d = upload(x, w)
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None, chunk=64)
+    assert g.gdr_chunk_fwd_path(desc) == g.PATH_MFMA
+    nbytes = g.gdr_chunk_fwd_workspace_size(desc)
+    NT = (T + 63) // 64
+    assert nbytes == w.B * w.H * NT * REC_BYTES
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], k_w=d["k_w"], workspace=ws)
+    torch.cuda.synchronize()
+    raw = ws.cpu().numpy()
+    f = gi.prefill_f64(w, x)
+    kw = f["k"] if f["k_w"] is None else f["k_w"]
+    worst = {"T": 0.0, "P": 0.0, "gam": 0.0, "fac": 0.0}
+    for bh in range(w.B * w.H):
+        b, h = divmod(bh, w.H)
+        for c in range(NT):
+            rec = raw[(bh * NT + c) * REC_BYTES:(bh * NT + c + 1) * REC_BYTES]
+            Tg = _bf16(rec[0:8192].view(np.uint16).reshape(64, 64))
+            Pg = _bf16(rec[8192:16384].view(np.uint16).reshape(64, 64)) + \
+                _bf16(rec[16384:24576].view(np.uint16).reshape(64, 64))
+            gam = rec[24576:24832].view(np.float32).astype(np.float64)
+            fac = rec[24832:25088].view(np.float32).astype(np.float64)
+            gC = float(rec[25088:25092].view(np.float32)[0])
+            t0, n = 64 * c, min(64, T - 64 * c)
+            K = np.zeros((64, 128)); KW = np.zeros((64, 128)); Q = np.zeros((64, 128))
+            K[:n] = f["k"][b, t0:t0 + n, h]
+            KW[:n] = kw[b, t0:t0 + n, h]
+            Q[:n] = f["q"][b, t0:t0 + n, h]
+            be = np.zeros(64); be[:n] = f["beta_k"][b, t0:t0 + n, h]
+            la = np.zeros(64); la[:n] = np.log(f["alpha"][b, t0:t0 + n, h])
+            gcum = np.cumsum(la)
+            W = be[None, :] * np.exp(gcum[:, None] - gcum[None, :])
+            A = np.tril((K @ KW.T) * W, -1)
+            Tr = np.linalg.inv(np.eye(64) + A)
+            Pr = np.tril((Q @ KW.T) * W, 0)
+            worst["T"] = max(worst["T"], np.abs(Tg - Tr).max() / np.abs(Tr).max())
+            worst["P"] = max(worst["P"], np.abs(Pg - Pr).max() / max(np.abs(Pr).max(), 1e-30))
+            worst["gam"] = max(worst["gam"], np.abs(gam - np.exp(gcum)).max())
+            fr = be * np.exp(gcum[n - 1] - gcum)
+            fr[n:] = 0
+            worst["fac"] = max(worst["fac"], np.abs(fac - fr).max())
+            assert abs(gC - np.exp(gcum[n - 1])) < 1e-5
+    log(f"[prep record] worst {worst}")
+    assert worst["T"] < 8e-3      # stored in bf16
+    assert worst["P"] < 1e-5      # two bf16 terms
+    assert worst["gam"] < 1e-5 and worst["fac"] < 1e-5
+
+
+def test_mfma_and_generic_paths_agree():
+    torch, g = gpu()
+    w = gi.OSDN_LONG_PREFILL.scaled(B=2, T=333, H=3, seed=52)
+    d = upload(gi.make_prefill(w), w)
+    a = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], k_w=d["k_w"], S0=d["S0"])
+    b = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], k_w=d["k_w"], S0=d["S0"], generic=True)
+    torch.cuda.synchronize()
+    from oracle import rel_l2
+    eo = rel_l2(a[0].float().cpu().numpy(), b[0].float().cpu().numpy())
+    es = rel_l2(a[1].cpu().numpy(), b[1].cpu().numpy())
+    log(f"[mfma vs generic] o {eo:.3e} S {es:.3e}")
+    assert eo < 2e-3 and es < 2e-3
+
+
+def test_path_selection_on_device():
+    torch, g = gpu()
+    w = gi.GDN_PREFILL.scaled(B=1, T=64, H=1)
+    d = upload(gi.make_prefill(w), w)
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None, chunk=64)
+    assert g.gdr_chunk_fwd_path(desc) == g.PATH_MFMA
+    desc32 = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None, chunk=32)
+    assert g.gdr_chunk_fwd_path(desc32) == g.PATH_VALU
