@@ -171,11 +171,11 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
             const int s = 16 * J + r;
             if (J <= IG) {
                 const int t = 16 * IG + 4 * q + i;
-                As[t][s] = (s < t && t < n) ? accG[J][i] * bS[J] * expf(gG[i] - gS[J]) : 0.f;
+                As[t][s] = (s < t && t < n) ? accG[J][i] * bS[J] * __expf(gG[i] - gS[J]) : 0.f;
             }
             const int tp = 16 * IP + 4 * q + i;
             float pv = 0.f;
-            if (J <= IP && s <= tp && tp < n) pv = accP[J][i] * bS[J] * expf(gP[i] - gS[J]);
+            if (J <= IP && s <= tp && tp < n) pv = accP[J][i] * bS[J] * __expf(gP[i] - gS[J]);
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
             Ph[tp][s] = __builtin_bit_cast(uint16_t, hi);
@@ -227,7 +227,11 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
             float x = 0.f;
             for (int Kb = J; Kb < I; ++Kb) {
 #pragma unroll
-                for (int m = 0; m < 16; ++m) x += As[16 * I + rr][16 * Kb + m] * Ts[16 * Kb + m][16 * J + cc];
+                for (int m4 = 0; m4 < 4; ++m4) {
+                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&As[16 * I + rr][16 * Kb + 4 * m4]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) x += a[u] * Ts[16 * Kb + 4 * m4 + u][16 * J + cc];
+                }
             }
             Xs[J][rr][cc] = x;
         }
@@ -236,7 +240,11 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
             const int J = e >> 8, I = J + d, rr = (e >> 4) & 15, cc = e & 15;
             float x = 0.f;
 #pragma unroll
-            for (int m = 0; m < 16; ++m) x -= Ts[16 * I + rr][16 * I + m] * Xs[J][m][cc];
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const f32x4 tr = *reinterpret_cast<const f32x4 *>(&Ts[16 * I + rr][16 * I + 4 * m4]);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) x -= tr[u] * Xs[J][4 * m4 + u][cc];
+            }
             Ts[16 * I + rr][16 * J + cc] = x;
         }
         __syncthreads();
@@ -260,9 +268,9 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
     if (tid < kC) {
         float *gam = reinterpret_cast<float *>(rec + kRecGam);
         float *fac = reinterpret_cast<float *>(rec + kRecFac);
-        gam[tid] = expf(gl[tid]);
-        fac[tid] = tid < n ? bl[tid] * expf(gl[n - 1] - gl[tid]) : 0.f;
-        if (tid == 0) *reinterpret_cast<float *>(rec + kRecGC) = expf(gl[n - 1]);
+        gam[tid] = __expf(gl[tid]);
+        fac[tid] = tid < n ? bl[tid] * __expf(gl[n - 1] - gl[tid]) : 0.f;
+        if (tid == 0) *reinterpret_cast<float *>(rec + kRecGC) = __expf(gl[n - 1]);
     }
 }
 
@@ -381,7 +389,7 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
                 sacc[ct][nt][i] = p.S0 ? p.S0[((long)bh * kD + ch) * kD + j0 + 16 * nt + r] : 0.f;
             }
 
-    auto put_z = [&]() {
+    auto put_z = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
@@ -393,7 +401,7 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
             }
     };
     // the transposed write key comes from the key rows the wave already holds
-    auto put_inputs = [&](const ChunkFrags<BV> &f, int buf) {
+    auto put_inputs = [&](const ChunkFrags<BV> &f, int buf) __attribute__((always_inline)) {
         const int s = 16 * w + r;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
@@ -413,7 +421,7 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
     uint16_t *O = static_cast<uint16_t *>(p.o);
     // one chunk: consumes `cur` (loaded one chunk earlier) and fills `nxt`; the loop
     // below alternates the two buffers so no fragment is ever copied
-    auto chunk_step = [&](const int c, ChunkFrags<BV> &cur, ChunkFrags<BV> &nxt) {
+    auto chunk_step = [&](const int c, ChunkFrags<BV> &cur, ChunkFrags<BV> &nxt) __attribute__((always_inline)) {
         const int t0 = c * kC, n = min(kC, p.T - t0);
         const int buf = c & 1;
         load_chunk<BV>(p, NT, bh, b, h, j0, min(c + 1, NT - 1), tid, sep_kw, nxt);
