@@ -237,7 +237,9 @@ def main():
             gbs = bps / (us_step * 1e-6) / 1e9
             dec[wd.name] = {"us_per_step": us_step, "tokens_per_s": wd.B / (us_step * 1e-6),
                             "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "steps_per_graph": wd.steps,
-                            "bytes_per_step": bps}
+                            "bytes_per_step": bps,
+                            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                         "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(wd.name, digest)}}
             del graph, dd, S
         out["decode"] = dec
 
