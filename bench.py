@@ -112,6 +112,8 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--generic", action="store_true", help="force the fp32 vector-ALU prefill kernel")
     ap.add_argument("--only-prefill", action="store_true")
+    ap.add_argument("--state-kernel", choices=["cols16", "cols32", "wavecols"], default=None,
+                    help="matrix-core state kernel (default: the library's choice)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -142,7 +144,9 @@ def main():
     d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
          for k in x}
     desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk,
-                       generic=args.generic)
+                       generic=args.generic, flags={None: 0, "cols16": g.GDR_FLAG_STATE_COLS16,
+                                                    "cols32": g.GDR_FLAG_STATE_COLS32,
+                                                    "wavecols": g.GDR_FLAG_STATE_WAVECOLS}[args.state_kernel])
     path = g.gdr_chunk_fwd_path(desc)
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
     ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)

@@ -27,6 +27,9 @@ GDR_BF16, GDR_F32 = 0, 1
 GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1
 GDR_BETA_SCALAR, GDR_BETA_SHARED, GDR_BETA_KV = 0, 1, 2
 GDR_FLAG_GENERIC_PATH = 0x1
+GDR_FLAG_STATE_COLS16 = 0x2
+GDR_FLAG_STATE_COLS32 = 0x4
+GDR_FLAG_STATE_WAVECOLS = 0x8
 PATH_MFMA, PATH_VALU = 1, 2
 
 
@@ -120,7 +123,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, generic=False) -> Desc:
+def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, generic=False, flags=0) -> Desc:
     """Descriptor from tensor shapes: prefill q [B, T, H, dk], decode q [B, H, dk]."""
     if decode:
         B, H, dk = q.shape
@@ -134,13 +137,14 @@ def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, gener
     beta_mode = GDR_BETA_KV if beta_v is not None else (GDR_BETA_SHARED if beta_vec else GDR_BETA_SCALAR)
     return Desc(B=B, T=T, H=H, dk=dk, dv=v.shape[-1], chunk=chunk, io_dtype=_dtype_code(q),
                 gate_dtype=_dtype_code(alpha), alpha_mode=GDR_ALPHA_CHANNEL if alpha_ch else GDR_ALPHA_SCALAR,
-                beta_mode=beta_mode, flags=GDR_FLAG_GENERIC_PATH if generic else 0)
+                beta_mode=beta_mode, flags=flags | (GDR_FLAG_GENERIC_PATH if generic else 0))
 
 
 def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=64, want_state=True,
-              out=None, final_state=None, workspace=None, generic=False, stream=None):
-    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None)."""
-    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic)
+              out=None, final_state=None, workspace=None, generic=False, flags=0, stream=None):
+    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None).
+    `flags` adds GDR_FLAG_* bits to the descriptor (kernel-selection testing aids)."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic, flags=flags)
     o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     ST = final_state
     if ST is None and want_state:

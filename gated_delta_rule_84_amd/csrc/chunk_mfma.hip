@@ -78,11 +78,15 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ float ld_gate(const void *p, long i, int bf16) { return ld_elem(p, i, bf16); }
 
-// Workgroup barrier that waits only for this wave's LDS traffic.  __syncthreads()
-// also drains outstanding global loads, which would stall on the next chunk's
-// prefetch at every barrier; the "memory" clobber keeps the compiler from moving
-// LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+// Workgroup barrier ordered for LDS only: the fences are restricted to the local
+// address space, so the barrier waits for this wave's LDS traffic but not for its
+// outstanding global loads (or copies into LDS), which stay in flight across it.
+// __syncthreads() would drain every outstanding global load at each barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 
 // ---------------------------------------------------------------------------
 // prep kernel
@@ -350,8 +354,10 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
                pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u))};
 }
 
-template <int BV>
-__global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int NT, int nbh) {
+// SEPKW: a separate write key is streamed (compile time, so that with k_w = k the
+// key fragments are used directly and no register copy of a load in flight exists)
+template <int BV, bool SEPKW>
+__global__ void __launch_bounds__(kThreads, BV == 16 ? 2 : 1) gdr_state_kernel(ChunkParams p, int NT, int nbh) {
     constexpr int NJ = BV / 16;    // value-column tiles
     constexpr int NVB = kD / BV;
     constexpr int LZ = kD + 8;     // bf16 row pitch of the state operand arrays
@@ -375,7 +381,7 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
     if (bh >= nbh) return;
     const int b = bh / p.H, h = bh % p.H, j0 = vb * BV;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
-    const bool sep_kw = p.kw != p.k;
+    constexpr bool sep_kw = SEPKW;
 
     // state, C layout: sacc[ct][nt][i] = S[16 (2 w + ct) + 4 q + i][j0 + 16 nt + r]
     f32x4 sacc[2][NJ];
@@ -449,11 +455,15 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
         // R = V - e^{g_t} Y, zero past the end of the chunk
 #pragma unroll
         for (int nt = 0; nt < NJ; ++nt) {
+            // V is read unconditionally (a read inside the tail test becomes a branch
+            // with its own LDS round trip per element); rows past the end are zeroed after
             f32x4 rv;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float vv = bf16_to_f32(VO[w][4 * q + i][16 * nt + r]);
-                rv[i] = 16 * w + 4 * q + i < n ? vv - gam[i] * accY[nt][i] : 0.f;
+            for (int i = 0; i < 4; ++i) rv[i] = bf16_to_f32(VO[w][4 * q + i][16 * nt + r]) - gam[i] * accY[nt][i];
+            if (n < kC) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (16 * w + 4 * q + i >= n) rv[i] = 0.f;
             }
             u32x2 hi, lo;
             split4(rv, hi, lo);
@@ -577,14 +587,325 @@ __global__ void __launch_bounds__(kThreads) gdr_state_kernel(ChunkParams p, int 
     }
 }
 
-int value_block(long nbh) {
-    static const int forced = [] {
-        const char *e = getenv("GDR_STATE_BV");
-        return e ? atoi(e) : 0;
-    }();
-    if (forced == 16 || forced == 32) return forced;
-    return nbh * (kD / 32) >= 256 ? 32 : 16;
+// ---------------------------------------------------------------------------
+// state kernel, column-owner form
+// ---------------------------------------------------------------------------
+// Two waves per workgroup; wave w owns value columns j0 + 16 w .. j0 + 16 w + 15
+// of one (batch, head) for all 64 tokens and all 128 key channels, so the
+// state, the residuals R, D and the weighted residuals E never leave the wave:
+// every product in the chunk is a 16-column MFMA whose B operand is built in
+// registers from the C tiles of the product before it.  A C tile holds
+// rows 4q .. 4q+3 of its 16 rows in lane (r, q), so two vertically adjacent C
+// tiles give lane (r, q) the eight rows {4q .. 4q+3, 16+4q .. 16+4q+3} of a
+// 32-row block: the contraction index of every product runs in that order
+// within each 32-block, and the A operands are read from LDS in the same order
+// (two 8-byte reads per fragment).  The transposed write key comes from the
+// row-major key tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16:
+// lane j of each 16-lane group receives element j of the 4 rows addressed by
+// its group).
+//
+// Operands of a chunk (keys, queries, write keys, Tm, the P terms, the V tile
+// and the decay factors) are copied global -> LDS by the waves' own
+// global_load_lds copies one chunk ahead into a double buffer; one barrier per
+// chunk hands a buffer over.  LDS rows are kept whole; 16-byte pieces are
+// XOR-swizzled by row so each read spreads over the LDS banks.
+constexpr int kCW = 32;  // value columns per workgroup
+
+struct ColBuf {
+    uint16_t K[kC][kD];    // key rows; piece p of row t stored at piece p ^ (t & 15)
+    uint16_t Q[kC][kD];    // query rows, same layout
+    uint16_t KW[kC][kD];   // separate write-key rows, same layout
+    uint16_t T[kC][kC];    // Tm rows; piece p of row t stored at p ^ ((t >> 1) & 7)
+    uint16_t Ph[kC][kC];   // P leading term, same layout
+    uint16_t Pl[kC][kC];   // P remainder, same layout
+    uint16_t V[kC][kCW];   // V tile, plain
+    float G[256];          // record tail: e^{g_t} [64] | fac_t [64] | e^{g_C}
+};
+
+typedef __attribute__((address_space(3))) void *lds_void_t;
+typedef __attribute__((address_space(1))) void *gbl_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_t;
+
+// 16 bytes per lane, global -> LDS; lane l writes dst + 16 l (dst wave-uniform)
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)dst, 16, 0, 0);
 }
+
+__device__ __forceinline__ u32x2 ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
+
+__device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
+    return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(p)));
+}
+
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
+
+// two C tiles (rows 4q..4q+3 of each) -> one B fragment as two bf16 terms
+__device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
+    u32x2 ha, la, hb, lb;
+    split4(a, ha, la);
+    split4(b, hb, lb);
+    hi = cat(ha, hb);
+    lo = cat(la, lb);
+}
+
+template <bool SEPKW>
+__global__ void __launch_bounds__(128) gdr_state_cols_kernel(ChunkParams p, int NT, int nbh) {
+    __shared__ ColBuf buf[2];
+    const int x = blockIdx.x;
+    const int xcd = x & 7, rr = x >> 3;
+    const int vb = rr % (kD / kCW), bh = rr / (kD / kCW) * 8 + xcd;  // the 4 blocks of a head share an XCD
+    if (bh >= nbh) return;
+    const int b = bh / p.H, h = bh % p.H, j0 = vb * kCW;
+    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+    const int cw = j0 + 16 * w;  // first value column of this wave
+    const uint16_t *K = static_cast<const uint16_t *>(p.k);
+    const uint16_t *KWg = static_cast<const uint16_t *>(p.kw);
+    const uint16_t *Qg = static_cast<const uint16_t *>(p.q);
+    const uint16_t *V = static_cast<const uint16_t *>(p.v);
+    uint16_t *O = static_cast<uint16_t *>(p.o);
+
+    // copies of chunk c into buffer bb, split between the two waves
+    auto issue = [&](int c, int bb) __attribute__((always_inline)) {
+        ColBuf &B = buf[bb];
+        const int t0 = c * kC, n = min(kC, p.T - t0);
+        auto rowoff = [&](int t) -> long { return (((long)b * p.T + t0 + min(t, n - 1)) * p.H + h) * kD; };
+        const char *rec = static_cast<const char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
+        // key-width tiles: 1 KB = 4 rows per copy; lane l -> row 4u + l / 16, stored piece l % 16
+        auto wide = [&](const uint16_t *src, uint16_t(*dst)[kD]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int t = 4 * u + (l >> 4), pc = (l & 15) ^ (t & 15);
+                dma16(src + rowoff(t) + 8 * pc, &dst[4 * u][0]);
+            }
+        };
+        // chunk-width tiles from the record: 8 rows per copy
+        auto narrow = [&](int off, uint16_t(*dst)[kC]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int t = 8 * u + (l >> 3), pc = (l & 7) ^ ((t >> 1) & 7);
+                dma16(rec + off + (t * kC + 8 * pc) * 2, &dst[8 * u][0]);
+            }
+        };
+        // V tile: 16 rows of 32 columns per copy, two copies per wave
+        auto vtile = [&](int u) __attribute__((always_inline)) {
+            const int t = 16 * u + (l >> 2);
+            dma16(V + rowoff(t) + j0 + 8 * (l & 3), &B.V[16 * u][0]);
+        };
+        if (w == 0) {
+            wide(K, B.K);
+            narrow(kRecT, B.T);
+            narrow(kRecPhi, B.Ph);
+            vtile(0);
+            vtile(1);
+        } else {
+            wide(Qg, B.Q);
+            if (SEPKW) wide(KWg, B.KW);
+            narrow(kRecPlo, B.Pl);
+            vtile(2);
+            vtile(3);
+            if (l < (kRecBytes - kRecGam) / 16) dma16(rec + kRecGam + 16 * l, &B.G[0]);
+        }
+    };
+
+    // state, C layout: S[kt][i] = S[16 kt + 4 q + i][cw + r]
+    f32x4 S[8];
+    if (p.S0) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+    } else {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    issue(0, 0);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
+    __syncthreads();
+
+    for (int c = 0; c < NT; ++c) {
+        const int bb = c & 1;
+        const ColBuf &B = buf[bb];
+        const int t0 = c * kC, n = min(kC, p.T - t0);
+        if (c + 1 < NT) issue(c + 1, bb ^ 1);
+
+        // Each phase reads all of its LDS fragments before its first product so the
+        // reads are in flight together (one wave per SIMD: nothing else hides them).
+
+        // Y = K S and O0 = Q S, all 64 tokens (S as two bf16 terms)
+        f32x4 Y[4], O0[4];
+        {
+            u32x4 ka[4][4], qa[4][4], sh[4], sl[4];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    const int t = 16 * tt + r;
+                    ka[kk][tt] = cat(ld8(&B.K[t][8 * (p1 ^ r) + hf]), ld8(&B.K[t][8 * (p2 ^ r) + hf]));
+                    qa[kk][tt] = cat(ld8(&B.Q[t][8 * (p1 ^ r) + hf]), ld8(&B.Q[t][8 * (p2 ^ r) + hf]));
+                }
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) split_frag(S[2 * kk], S[2 * kk + 1], sh[kk], sl[kk]);
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                O0[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sh[kk]), Y[tt]);
+                    O0[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sh[kk]), O0[tt]);
+                }
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sl[kk]), Y[tt]);
+                    O0[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sl[kk]), O0[tt]);
+                }
+        }
+
+        // R = V - e^{g_t} Y (rows past the chunk end zeroed)
+        f32x4 R[4], gam[4], fac[4];
+        {
+            f32x4 vf[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) {
+                gam[tt] = *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
+                fac[tt] = *reinterpret_cast<const f32x4 *>(&B.G[kC + 16 * tt + 4 * q]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vf[tt][i] = bf16_to_f32(B.V[16 * tt + 4 * q + i][16 * w + r]);
+            }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) R[tt] = vf[tt] - gam[tt] * Y[tt];
+            if (n < kC) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * tt + 4 * q + i >= n) R[tt][i] = 0.f;
+            }
+        }
+        u32x4 rh[2], rl[2];
+        split_frag(R[0], R[1], rh[0], rl[0]);
+        split_frag(R[2], R[3], rh[1], rl[1]);
+
+        // A fragments of Tm and of the P terms, flat over the (token tile, k step) pairs
+        // that are not all zero (Tm, P lower triangular: tiles 0, 1 need k step 0 only)
+        u32x4 ta[6], pha[6], pla[6];
+#pragma unroll
+        for (int tt = 0, f = 0; tt < 4; ++tt) {
+            const int t = 16 * tt + r, sw = (t >> 1) & 7;
+#pragma unroll
+            for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                ta[f] = cat(ld8(&B.T[t][8 * (p1 ^ sw) + hf]), ld8(&B.T[t][8 * (p2 ^ sw) + hf]));
+                pha[f] = cat(ld8(&B.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&B.Ph[t][8 * (p2 ^ sw) + hf]));
+                pla[f] = cat(ld8(&B.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&B.Pl[t][8 * (p2 ^ sw) + hf]));
+            }
+        }
+
+        // D = Tm R
+        f32x4 D[4];
+#pragma unroll
+        for (int tt = 0, f = 0; tt < 4; ++tt) {
+            D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rh[kk]), D[tt]);
+                D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rl[kk]), D[tt]);
+            }
+        }
+        u32x4 dh[2], dl[2], eh[2], el[2];
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+            split_frag(D[2 * kk], D[2 * kk + 1], dh[kk], dl[kk]);
+            split_frag(D[2 * kk] * fac[2 * kk], D[2 * kk + 1] * fac[2 * kk + 1], eh[kk], el[kk]);
+        }
+
+        // S <- e^{g_C} S + K_w^T E; A fragments of K_w^T by the transposing read.  This
+        // comes before the output stores: the compiler makes the first transposing
+        // read wait for every outstanding vector-memory operation (it cannot tell the
+        // read from the copies into the other buffer), which then are copies only.
+        {
+            const float gC = B.G[2 * kC];
+            const uint16_t(*KWs)[kD] = SEPKW ? B.KW : B.K;
+            const int a = r & 3, m = r >> 2;
+            u32x4 kw[8][2];
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
+                    const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
+                    kw[kt][kk] = cat(ld_tr(&KWs[t1][8 * (pc ^ (t1 & 15)) + hf]),
+                                     ld_tr(&KWs[t2][8 * (pc ^ (t2 & 15)) + hf]));
+                }
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) S[kt] *= gC;
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) {
+                    S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(eh[kk]), S[kt]);
+                    S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(el[kk]), S[kt]);
+                }
+        }
+
+        // O = e^{g_t} O0 + P D, then stored per lane (4 tokens of one value column per tile)
+        {
+            f32x4 o[4];
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) o[tt] = O0[tt] * gam[tt];
+#pragma unroll
+            for (int tt = 0, f = 0; tt < 4; ++tt)
+#pragma unroll
+                for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                    o[tt] = mfma(as_bf16x8(pha[f]), as_bf16x8(dh[kk]), o[tt]);
+                    o[tt] = mfma(as_bf16x8(pha[f]), as_bf16x8(dl[kk]), o[tt]);
+                    o[tt] = mfma(as_bf16x8(pla[f]), as_bf16x8(dh[kk]), o[tt]);
+                }
+            // token 4 q of the chunk, value column cw + r; tokens are H * 128 elements apart
+            const long tstr = (long)p.H * kD;
+            uint16_t *dst = O + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
+            if (n == kC) {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t o2 = pk_bf16(o[tt][i], o[tt][i + 1]);
+                        dst[(16 * tt + i) * tstr] = (uint16_t)(o2 & 0xffffu);
+                        dst[(16 * tt + i + 1) * tstr] = (uint16_t)(o2 >> 16);
+                    }
+            } else {
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * tt + 4 * q + i < n) dst[(16 * tt + i) * tstr] = f32_to_bf16(o[tt][i]);
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
+        __syncthreads();                     // ... for both waves; this buffer is free again
+    }
+
+    if (p.ST) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+    }
+}
+
+// State kernel: 16 / 32 = the four-wave kernel with that many value columns per
+// workgroup (32 by default), 1 = the column-owner kernel (selected by flags).
+int state_variant(const ChunkParams &p) { return p.state_cols == 16 || p.state_cols == 1 ? p.state_cols : 32; }
 
 }  // namespace
 
@@ -612,12 +933,18 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     }
     void *args[] = {&arg, &nt, &nb};
     const long groups = (nbh + 7) / 8;
-    if (value_block(nbh) == 32) {
-        return hipLaunchKernel(reinterpret_cast<const void *>(&gdr_state_kernel<32>),
-                               dim3((unsigned)(groups * 8 * (kD / 32))), dim3(kThreads), args, 0, st);
+    const bool sep = p.kw != p.k;
+    const int bv = state_variant(p);
+    if (bv == 1) {
+        const void *fn = sep ? reinterpret_cast<const void *>(&gdr_state_cols_kernel<true>)
+                             : reinterpret_cast<const void *>(&gdr_state_cols_kernel<false>);
+        return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(128), args, 0, st);
     }
-    return hipLaunchKernel(reinterpret_cast<const void *>(&gdr_state_kernel<16>),
-                           dim3((unsigned)(groups * 8 * (kD / 16))), dim3(kThreads), args, 0, st);
+    const void *fn = bv == 32 ? (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<32, true>)
+                                     : reinterpret_cast<const void *>(&gdr_state_kernel<32, false>))
+                              : (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<16, true>)
+                                     : reinterpret_cast<const void *>(&gdr_state_kernel<16, false>));
+    return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / bv))), dim3(kThreads), args, 0, st);
 }
 
 }  // namespace gdr

@@ -33,7 +33,12 @@ int check_desc(const gdr_desc *d, bool prefill) {
     if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
     if (d->alpha_mode != GDR_ALPHA_SCALAR && d->alpha_mode != GDR_ALPHA_CHANNEL) return GDR_EINVAL;
     if (d->beta_mode < GDR_BETA_SCALAR || d->beta_mode > GDR_BETA_KV) return GDR_EINVAL;
-    if (d->flags & ~GDR_FLAG_GENERIC_PATH) return GDR_EINVAL;
+    if (d->flags & ~(GDR_FLAG_GENERIC_PATH | GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS))
+        return GDR_EINVAL;
+    {
+        const int sel = d->flags & (GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS);
+        if (sel & (sel - 1)) return GDR_EINVAL;  // at most one state-kernel selector
+    }
     if (d->beta_mode == GDR_BETA_SHARED && d->dk != d->dv) return GDR_EINVAL;
     if (d->dk < 8 || d->dk > 128 || (d->dk & 7) || d->dv < 8 || d->dv > 128 || (d->dv & 7))
         return GDR_EUNSUPPORTED;
@@ -51,6 +56,10 @@ ChunkParams chunk_params(const gdr_desc *d) {
     p.gate_bf16 = d->gate_dtype == GDR_BF16;
     p.alpha_ch = d->alpha_mode == GDR_ALPHA_CHANNEL;
     p.beta_mode = d->beta_mode;
+    p.state_cols = (d->flags & GDR_FLAG_STATE_COLS16)     ? 16
+                   : (d->flags & GDR_FLAG_STATE_COLS32)   ? 32
+                   : (d->flags & GDR_FLAG_STATE_WAVECOLS) ? 1
+                                                          : 0;
     return p;
 }
 

@@ -45,16 +45,17 @@ def to_np(t):
         t.detach().cpu().numpy().astype(np.float64)
 
 
-def run_prefill(w, x, *, generic=False, heads=None, nthreads=0):
+def run_prefill(w, x, *, generic=False, flags=0, heads=None, nthreads=0):
     """GPU chunk forward vs the fp64 oracle on (optionally sampled) heads.
     Returns dict of rel-L2 errors and the path used."""
     torch, g = gpu()
     d = upload(x, w)
-    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk, generic=generic)
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk, generic=generic,
+                       flags=flags)
     path = g.gdr_chunk_fwd_path(desc)
     log(f"[prefill] {w.name} B={w.B} T={w.T} H={w.H} dk={w.dk} dv={w.dv} C={w.chunk} path={path}")
     o, ST = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], k_w=d["k_w"], beta_v=d["beta_v"],
-                        S0=d["S0"], chunk=w.chunk, generic=generic)
+                        S0=d["S0"], chunk=w.chunk, generic=generic, flags=flags)
     torch.cuda.synchronize()
     o_gpu, S_gpu = to_np(o), to_np(ST)
     f = gi.prefill_f64(w, x)

@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import gdr_inputs as gi
-from tests.gpu_util import gpu, log, upload
+from tests.gpu_util import TOL, gpu, log, run_prefill, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -93,3 +93,26 @@ def test_path_selection_on_device():
     assert g.gdr_chunk_fwd_path(desc) == g.PATH_MFMA
     desc32 = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None, chunk=32)
     assert g.gdr_chunk_fwd_path(desc32) == g.PATH_VALU
+
+
+STATE_CASES = [
+    # several chunks with a ragged tail; B * H not a multiple of 8 (idle workgroups)
+    ("gdn_ragged", gi.GDN_PREFILL.scaled(B=3, T=333, H=3, seed=61)),
+    ("osdn_kw_S0", gi.OSDN_LONG_PREFILL.scaled(B=1, T=300, H=5, seed=62)),
+    ("gdn_T_lt_C", gi.GDN_PREFILL.scaled(B=2, T=41, H=2, s0_std=0.02, seed=63)),
+    ("gdn_T_one_chunk", gi.GDN_PREFILL.scaled(B=1, T=64, H=9, seed=64)),
+]
+
+
+@pytest.mark.parametrize("name,w", STATE_CASES, ids=[c[0] for c in STATE_CASES])
+@pytest.mark.parametrize("variant", ["cols", "four_wave16", "four_wave32"])
+def test_state_kernel_variants(name, w, variant):
+    """Every state-kernel variant (the column-owner kernel; the four-wave kernel with
+    16 or 32 value columns per workgroup, 32 being the default) against the oracle."""
+    torch, g = gpu()
+    flag = {"cols": g.GDR_FLAG_STATE_WAVECOLS, "four_wave16": g.GDR_FLAG_STATE_COLS16,
+            "four_wave32": g.GDR_FLAG_STATE_COLS32}[variant]
+    r = run_prefill(w, gi.make_prefill(w), flags=flag)
+    assert r["path"] == g.PATH_MFMA
+    assert r["finite"]
+    assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
