@@ -56,7 +56,9 @@ constexpr int kRecPlo = 16384;  // bf16 [64][64]  P, remainder
 constexpr int kRecGam = 24576;  // f32 [64]  e^{g_t}
 constexpr int kRecFac = 24832;  // f32 [64]  beta_s e^{g_C - g_s}, 0 past the chunk end
 constexpr int kRecGC = 25088;   // f32       e^{g_C}
-constexpr int kRecBytes = 25216;
+constexpr int kRecGlog = 25216; // f32 [64]  g_t (cumulative log decay inside the chunk)
+constexpr int kRecBeta = 25472; // f32 [64]  beta_t, 0 past the chunk end
+constexpr int kRecBytes = 25728;
 
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -275,6 +277,8 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
         gam[tid] = __expf(gl[tid]);
         fac[tid] = tid < n ? bl[tid] * __expf(gl[n - 1] - gl[tid]) : 0.f;
         if (tid == 0) *reinterpret_cast<float *>(rec + kRecGC) = __expf(gl[n - 1]);
+        reinterpret_cast<float *>(rec + kRecGlog)[tid] = gl[tid];
+        reinterpret_cast<float *>(rec + kRecBeta)[tid] = bl[tid];
     }
 }
 
@@ -588,38 +592,53 @@ __global__ void __launch_bounds__(kThreads, BV == 16 ? 2 : 1) gdr_state_kernel(C
 }
 
 // ---------------------------------------------------------------------------
-// state kernel, column-owner form
+// state kernel, wave-specialised form
 // ---------------------------------------------------------------------------
-// Two waves per workgroup; wave w owns value columns j0 + 16 w .. j0 + 16 w + 15
-// of one (batch, head) for all 64 tokens and all 128 key channels, so the
-// state, the residuals R, D and the weighted residuals E never leave the wave:
-// every product in the chunk is a 16-column MFMA whose B operand is built in
-// registers from the C tiles of the product before it.  A C tile holds
-// rows 4q .. 4q+3 of its 16 rows in lane (r, q), so two vertically adjacent C
-// tiles give lane (r, q) the eight rows {4q .. 4q+3, 16+4q .. 16+4q+3} of a
-// 32-row block: the contraction index of every product runs in that order
-// within each 32-block, and the A operands are read from LDS in the same order
-// (two 8-byte reads per fragment).  The transposed write key comes from the
-// row-major key tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16:
-// lane j of each 16-lane group receives element j of the 4 rows addressed by
-// its group).
-//
-// Operands of a chunk (keys, queries, write keys, Tm, the P terms, the V tile
-// and the decay factors) are copied global -> LDS by the waves' own
-// global_load_lds copies one chunk ahead into a double buffer; one barrier per
-// chunk hands a buffer over.  LDS rows are kept whole; 16-byte pieces are
-// XOR-swizzled by row so each read spreads over the LDS banks.
+// Four waves per workgroup, one per SIMD, for value columns j0 .. j0 + 31 of one
+// (batch, head).  Waves 0 and 1 ("chain" waves) own value columns
+// j0 + 16 w .. j0 + 16 w + 15 for all 64 tokens and 128 key channels and carry
+// only the sequential part of a chunk:
+//     Y = K S,  R = V - Diag(e^g) Y,  D = Tm R,  S <- e^{g_C} S + K_w^T (fac D).
+// The state, R, D and the weighted residuals never leave the wave: each product
+// is a 16-column MFMA whose B operand is built in registers from the C tiles of
+// the product before it.  A C tile holds rows 4q .. 4q+3 of its 16 rows in lane
+// (r, q), so two vertically adjacent C tiles give lane (r, q) the eight rows
+// {4q .. 4q+3, 16+4q .. 16+4q+3} of a 32-row block: the contraction index of
+// every product runs in that order within each 32-block, and the A operands are
+// read from LDS in the same order (two 8-byte reads per fragment).  The
+// transposed write key comes from the row-major key tile with the gfx950
+// transposing LDS read (ds_read_b64_tr_b16: lane j of each 16-lane group receives
+// element j of the 4 rows addressed by its group).
+// Waves 2 and 3 ("side" waves) take the rest for the same columns: they copy the
+// next chunk's operands global -> LDS (global_load_lds; keys, queries, write keys,
+// Tm and the decay factors into the other half of a double buffer at the chunk
+// start, V and the two P terms into single buffers once the current ones have
+// been read), form O0 = Q S from the state fragments the chain wave leaves in
+// LDS, and after the chain wave has published D, form and store
+// O = Diag(e^g) O0 + P D.  Two barriers per chunk.
+// LDS rows are kept whole; 16-byte pieces are XOR-swizzled by row so that each
+// read spreads over the LDS banks.
 constexpr int kCW = 32;  // value columns per workgroup
 
-struct ColBuf {
-    uint16_t K[kC][kD];    // key rows; piece p of row t stored at piece p ^ (t & 15)
-    uint16_t Q[kC][kD];    // query rows, same layout
-    uint16_t KW[kC][kD];   // separate write-key rows, same layout
-    uint16_t T[kC][kC];    // Tm rows; piece p of row t stored at p ^ ((t >> 1) & 7)
-    uint16_t Ph[kC][kC];   // P leading term, same layout
-    uint16_t Pl[kC][kC];   // P remainder, same layout
-    uint16_t V[kC][kCW];   // V tile, plain
-    float G[256];          // record tail: e^{g_t} [64] | fac_t [64] | e^{g_C}
+struct WsBuf {
+    uint16_t K[kC][kD];   // key rows; piece p of row t stored at piece p ^ (t & 15)
+    uint16_t Q[kC][kD];   // query rows, same layout
+    uint16_t KW[kC][kD];  // separate write-key rows, same layout
+    uint16_t T[kC][kC];   // Tm rows; piece p of row t stored at p ^ ((t >> 1) & 7)
+    float G[288];         // record tail: e^{g_t} | fac_t | e^{g_C} (+pad) | g_t | beta_t
+};
+constexpr int kGFac = 64, kGGC = 128, kGLog = 160, kGBeta = 224;
+static_assert((kRecBytes - kRecGam) == 288 * 4, "gate block of the record");
+static_assert(kRecFac - kRecGam == 4 * kGFac && kRecGC - kRecGam == 4 * kGGC, "gate block layout");
+static_assert(kRecGlog - kRecGam == 4 * kGLog && kRecBeta - kRecGam == 4 * kGBeta, "gate block layout");
+
+struct WsLds {
+    WsBuf buf[2];          // double buffered: copied one chunk ahead at the chunk start
+    uint16_t V[kC][kCW];   // single buffered: the next chunk's copy is issued once the
+    uint16_t Ph[kC][kC];   //   chain waves have read V and the side waves have read
+    uint16_t Pl[kC][kC];   //   the P terms (first barrier of the chunk); layout as T
+    u32x4 Sx[2][8][64];    // per chain wave: state fragments (hi, lo for 4 k steps) of the chunk start
+    u32x4 Dx[2][4][64];    // per chain wave: D fragments (hi, lo for 2 k steps)
 };
 
 typedef __attribute__((address_space(3))) void *lds_void_t;
@@ -649,253 +668,328 @@ __device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &l
     lo = cat(la, lb);
 }
 
+// A fragment of rows t (lane row r) of a key-width tile, k step kk, in the
+// contraction order {4q .. 4q+3, 16+4q .. 16+4q+3} of the 32-block
+__device__ __forceinline__ u32x4 frag_wide(const uint16_t (*M)[kD], int t, int kk, int q) {
+    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1), sw = t & 15;
+    return cat(ld8(&M[t][8 * (p1 ^ sw) + hf]), ld8(&M[t][8 * (p2 ^ sw) + hf]));
+}
+
+// B fragment (natural order: 8 consecutive keys) of a key-width tile row t
+__device__ __forceinline__ u32x4 frag_row(const uint16_t (*M)[kD], int t, int kk, int q) {
+    return *reinterpret_cast<const u32x4 *>(&M[t][8 * ((4 * kk + q) ^ (t & 15))]);
+}
+
 template <bool SEPKW>
-__global__ void __launch_bounds__(128) gdr_state_cols_kernel(ChunkParams p, int NT, int nbh) {
-    __shared__ ColBuf buf[2];
+__global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT, int nbh) {
+    __shared__ WsLds sm;
     const int x = blockIdx.x;
     const int xcd = x & 7, rr = x >> 3;
     const int vb = rr % (kD / kCW), bh = rr / (kD / kCW) * 8 + xcd;  // the 4 blocks of a head share an XCD
     if (bh >= nbh) return;
     const int b = bh / p.H, h = bh % p.H, j0 = vb * kCW;
-    const int w = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int w = wv & 1;  // column tile of this wave
     const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
-    const int cw = j0 + 16 * w;  // first value column of this wave
-    const uint16_t *K = static_cast<const uint16_t *>(p.k);
-    const uint16_t *KWg = static_cast<const uint16_t *>(p.kw);
-    const uint16_t *Qg = static_cast<const uint16_t *>(p.q);
-    const uint16_t *V = static_cast<const uint16_t *>(p.v);
-    uint16_t *O = static_cast<uint16_t *>(p.o);
+    const int cw = j0 + 16 * w;
+    const bool chain = wv < 2;
 
-    // copies of chunk c into buffer bb, split between the two waves
+    // copies of chunk c into buffer bb, by the two side waves.  For a full chunk every
+    // copy is a uniform base plus one of a few per-lane offsets fixed for the whole
+    // kernel: row l / 16 of a 4-row unit of a key-width tile (its stored piece depends
+    // on the unit index mod 4), row l / 8 of an 8-row unit of Tm (unit index mod 2),
+    // row l / 4 of a 16-row unit of the V tile.  A short last chunk clamps its rows.
+    const unsigned rstr = (unsigned)p.H * kD;  // elements from one token to the next
+    unsigned offW[4], offT[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * j + (l >> 4);
+        offW[j] = (unsigned)(l >> 4) * rstr + 8u * (unsigned)((l & 15) ^ (t & 15));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = 8 * j + (l >> 3);
+        offT[j] = (unsigned)((l >> 3) * kC + 8 * ((l & 7) ^ ((t >> 1) & 7)));
+    }
+    const unsigned offV = (unsigned)(l >> 2) * rstr + (unsigned)(j0 + 8 * (l & 3));
     auto issue = [&](int c, int bb) __attribute__((always_inline)) {
-        ColBuf &B = buf[bb];
+        WsBuf &B = sm.buf[bb];
         const int t0 = c * kC, n = min(kC, p.T - t0);
-        auto rowoff = [&](int t) -> long { return (((long)b * p.T + t0 + min(t, n - 1)) * p.H + h) * kD; };
+        const long base = (((long)b * p.T + t0) * p.H + h) * kD;
         const char *rec = static_cast<const char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
-        // key-width tiles: 1 KB = 4 rows per copy; lane l -> row 4u + l / 16, stored piece l % 16
-        auto wide = [&](const uint16_t *src, uint16_t(*dst)[kD]) __attribute__((always_inline)) {
+        auto wide = [&](const void *src, uint16_t(*dst)[kD]) __attribute__((always_inline)) {
+            const uint16_t *s16 = static_cast<const uint16_t *>(src) + base;
+            if (n == kC) {
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int t = 4 * u + (l >> 4), pc = (l & 15) ^ (t & 15);
-                dma16(src + rowoff(t) + 8 * pc, &dst[4 * u][0]);
-            }
-        };
-        // chunk-width tiles from the record: 8 rows per copy
-        auto narrow = [&](int off, uint16_t(*dst)[kC]) __attribute__((always_inline)) {
+                for (int u = 0; u < 16; ++u) dma16(s16 + (long)(4 * u) * rstr + offW[u & 3], &dst[4 * u][0]);
+            } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int t = 8 * u + (l >> 3), pc = (l & 7) ^ ((t >> 1) & 7);
-                dma16(rec + off + (t * kC + 8 * pc) * 2, &dst[8 * u][0]);
+                for (int u = 0; u < 16; ++u) {
+                    const int t = 4 * u + (l >> 4), pc = (l & 15) ^ (t & 15);
+                    dma16(s16 + (long)min(t, n - 1) * rstr + 8 * pc, &dst[4 * u][0]);
+                }
             }
-        };
-        // V tile: 16 rows of 32 columns per copy, two copies per wave
-        auto vtile = [&](int u) __attribute__((always_inline)) {
-            const int t = 16 * u + (l >> 2);
-            dma16(V + rowoff(t) + j0 + 8 * (l & 3), &B.V[16 * u][0]);
         };
         if (w == 0) {
-            wide(K, B.K);
-            narrow(kRecT, B.T);
-            narrow(kRecPhi, B.Ph);
-            vtile(0);
-            vtile(1);
+            wide(p.k, B.K);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dma16(rec + kRecT + 2 * (512 * u + offT[u & 1]), &B.T[8 * u][0]);
         } else {
-            wide(Qg, B.Q);
-            if (SEPKW) wide(KWg, B.KW);
-            narrow(kRecPlo, B.Pl);
-            vtile(2);
-            vtile(3);
-            if (l < (kRecBytes - kRecGam) / 16) dma16(rec + kRecGam + 16 * l, &B.G[0]);
+            wide(p.q, B.Q);
+            if (SEPKW) wide(p.kw, B.KW);
+            dma16(rec + kRecGam + 16 * l, &B.G[0]);
+            if (l < 8) dma16(rec + kRecGam + 1024 + 16 * l, &B.G[256]);
+        }
+    };
+    // the single-buffered tiles of chunk c: V (side wave 0) and the P terms
+    auto issue_late = [&](int c) __attribute__((always_inline)) {
+        const int t0 = c * kC, n = min(kC, p.T - t0);
+        const char *rec = static_cast<const char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
+        if (w == 0) {
+            const uint16_t *Vg = static_cast<const uint16_t *>(p.v) + (((long)b * p.T + t0) * p.H + h) * kD;
+            if (n == kC) {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) dma16(Vg + (long)(16 * u) * rstr + offV, &sm.V[16 * u][0]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    const int t = 16 * u + (l >> 2);
+                    dma16(Vg + (long)min(t, n - 1) * rstr + j0 + 8 * (l & 3), &sm.V[16 * u][0]);
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dma16(rec + kRecPhi + 2 * (512 * u + offT[u & 1]), &sm.Ph[8 * u][0]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) dma16(rec + kRecPlo + 2 * (512 * u + offT[u & 1]), &sm.Pl[8 * u][0]);
         }
     };
 
-    // state, C layout: S[kt][i] = S[16 kt + 4 q + i][cw + r]
-    f32x4 S[8];
-    if (p.S0) {
+    f32x4 S[8];  // chain waves: S[kt][i] = S[16 kt + 4 q + i][cw + r]
+    auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
-        for (int kt = 0; kt < 8; ++kt)
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 hi, lo;
+            split_frag(S[2 * kk], S[2 * kk + 1], hi, lo);
+            sm.Sx[w][2 * kk][l] = hi;
+            sm.Sx[w][2 * kk + 1][l] = lo;
+        }
+    };
+    if (chain) {
+        if (p.S0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        publish_state();
     } else {
-#pragma unroll
-        for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        issue(0, 0);
+        issue_late(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
-
-    issue(0, 0);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's copies have landed
     __syncthreads();
 
     for (int c = 0; c < NT; ++c) {
         const int bb = c & 1;
-        const ColBuf &B = buf[bb];
+        const WsBuf &B = sm.buf[bb];
         const int t0 = c * kC, n = min(kC, p.T - t0);
-        if (c + 1 < NT) issue(c + 1, bb ^ 1);
-
-        // Each phase reads all of its LDS fragments before its first product so the
-        // reads are in flight together (one wave per SIMD: nothing else hides them).
-
-        // Y = K S and O0 = Q S, all 64 tokens (S as two bf16 terms)
-        f32x4 Y[4], O0[4];
-        {
-            u32x4 ka[4][4], qa[4][4], sh[4], sl[4];
+        if (chain) {
+            // Y = K S (S as two bf16 terms)
+            f32x4 Y[4];
+            {
+                u32x4 ka[4][4], sh[4], sl[4];
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) ka[kk][tt] = frag_wide(B.K, 16 * tt + r, kk, q);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    sh[kk] = sm.Sx[w][2 * kk][l];
+                    sl[kk] = sm.Sx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sh[kk]), Y[tt]);
+                        Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sl[kk]), Y[tt]);
+                    }
+            }
+            // R = V - e^{g_t} Y (rows past the chunk end zeroed)
+            u32x4 rh[2], rl[2];
+            {
+                f32x4 R[4];
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
-                    const int t = 16 * tt + r;
-                    ka[kk][tt] = cat(ld8(&B.K[t][8 * (p1 ^ r) + hf]), ld8(&B.K[t][8 * (p2 ^ r) + hf]));
-                    qa[kk][tt] = cat(ld8(&B.Q[t][8 * (p1 ^ r) + hf]), ld8(&B.Q[t][8 * (p2 ^ r) + hf]));
+                    const f32x4 gam = *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
+                    f32x4 vf;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) vf[i] = bf16_to_f32(sm.V[16 * tt + 4 * q + i][16 * w + r]);
+                    R[tt] = vf - gam * Y[tt];
                 }
-            }
+                if (n < kC) {
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) split_frag(S[2 * kk], S[2 * kk + 1], sh[kk], sl[kk]);
+                    for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-                O0[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sh[kk]), Y[tt]);
-                    O0[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sh[kk]), O0[tt]);
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * tt + 4 * q + i >= n) R[tt][i] = 0.f;
                 }
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt) {
-                    Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sl[kk]), Y[tt]);
-                    O0[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sl[kk]), O0[tt]);
-                }
-        }
-
-        // R = V - e^{g_t} Y (rows past the chunk end zeroed)
-        f32x4 R[4], gam[4], fac[4];
-        {
-            f32x4 vf[4];
-#pragma unroll
-            for (int tt = 0; tt < 4; ++tt) {
-                gam[tt] = *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
-                fac[tt] = *reinterpret_cast<const f32x4 *>(&B.G[kC + 16 * tt + 4 * q]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vf[tt][i] = bf16_to_f32(B.V[16 * tt + 4 * q + i][16 * w + r]);
+                split_frag(R[0], R[1], rh[0], rl[0]);
+                split_frag(R[2], R[3], rh[1], rl[1]);
             }
+            // D = Tm R (Tm unit lower triangular: token tiles 0, 1 need k step 0 only)
+            f32x4 D[4];
+            {
+                u32x4 ta[6];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) R[tt] = vf[tt] - gam[tt] * Y[tt];
-            if (n < kC) {
+                for (int tt = 0, f = 0; tt < 4; ++tt) {
+                    const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * tt + 4 * q + i >= n) R[tt][i] = 0.f;
-            }
-        }
-        u32x4 rh[2], rl[2];
-        split_frag(R[0], R[1], rh[0], rl[0]);
-        split_frag(R[2], R[3], rh[1], rl[1]);
-
-        // A fragments of Tm and of the P terms, flat over the (token tile, k step) pairs
-        // that are not all zero (Tm, P lower triangular: tiles 0, 1 need k step 0 only)
-        u32x4 ta[6], pha[6], pla[6];
-#pragma unroll
-        for (int tt = 0, f = 0; tt < 4; ++tt) {
-            const int t = 16 * tt + r, sw = (t >> 1) & 7;
-#pragma unroll
-            for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
-                ta[f] = cat(ld8(&B.T[t][8 * (p1 ^ sw) + hf]), ld8(&B.T[t][8 * (p2 ^ sw) + hf]));
-                pha[f] = cat(ld8(&B.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&B.Ph[t][8 * (p2 ^ sw) + hf]));
-                pla[f] = cat(ld8(&B.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&B.Pl[t][8 * (p2 ^ sw) + hf]));
-            }
-        }
-
-        // D = Tm R
-        f32x4 D[4];
-#pragma unroll
-        for (int tt = 0, f = 0; tt < 4; ++tt) {
-            D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rh[kk]), D[tt]);
-                D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rl[kk]), D[tt]);
-            }
-        }
-        u32x4 dh[2], dl[2], eh[2], el[2];
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            split_frag(D[2 * kk], D[2 * kk + 1], dh[kk], dl[kk]);
-            split_frag(D[2 * kk] * fac[2 * kk], D[2 * kk + 1] * fac[2 * kk + 1], eh[kk], el[kk]);
-        }
-
-        // S <- e^{g_C} S + K_w^T E; A fragments of K_w^T by the transposing read.  This
-        // comes before the output stores: the compiler makes the first transposing
-        // read wait for every outstanding vector-memory operation (it cannot tell the
-        // read from the copies into the other buffer), which then are copies only.
-        {
-            const float gC = B.G[2 * kC];
-            const uint16_t(*KWs)[kD] = SEPKW ? B.KW : B.K;
-            const int a = r & 3, m = r >> 2;
-            u32x4 kw[8][2];
-#pragma unroll
-            for (int kt = 0; kt < 8; ++kt)
-#pragma unroll
-                for (int kk = 0; kk < 2; ++kk) {
-                    const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
-                    const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
-                    kw[kt][kk] = cat(ld_tr(&KWs[t1][8 * (pc ^ (t1 & 15)) + hf]),
-                                     ld_tr(&KWs[t2][8 * (pc ^ (t2 & 15)) + hf]));
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                        ta[f] = cat(ld8(&B.T[t][8 * (p1 ^ sw) + hf]), ld8(&B.T[t][8 * (p2 ^ sw) + hf]));
+                    }
                 }
 #pragma unroll
-            for (int kt = 0; kt < 8; ++kt) S[kt] *= gC;
+                for (int tt = 0, f = 0; tt < 4; ++tt) {
+                    D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-                for (int kt = 0; kt < 8; ++kt) {
-                    S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(eh[kk]), S[kt]);
-                    S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(el[kk]), S[kt]);
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rh[kk]), D[tt]);
+                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rl[kk]), D[tt]);
+                    }
                 }
-        }
+            }
+            // publish D for the side wave; E = fac D stays here
+            u32x4 eh[2], el[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                u32x4 dh, dl;
+                split_frag(D[2 * kk], D[2 * kk + 1], dh, dl);
+                sm.Dx[w][2 * kk][l] = dh;
+                sm.Dx[w][2 * kk + 1][l] = dl;
+                const f32x4 f0 = *reinterpret_cast<const f32x4 *>(&B.G[kGFac + 32 * kk + 4 * q]);
+                const f32x4 f1 = *reinterpret_cast<const f32x4 *>(&B.G[kGFac + 32 * kk + 16 + 4 * q]);
+                split_frag(D[2 * kk] * f0, D[2 * kk + 1] * f1, eh[kk], el[kk]);
+            }
+            lds_barrier();  // B1: D published; V and the P terms of this chunk consumed
 
-        // O = e^{g_t} O0 + P D, then stored per lane (4 tokens of one value column per tile)
-        {
-            f32x4 o[4];
+            // S <- e^{g_C} S + K_w^T E; A fragments of K_w^T by the transposing read
+            {
+                const float gC = B.G[kGGC];
+                const uint16_t(*KWs)[kD] = SEPKW ? B.KW : B.K;
+                const int a = r & 3, m = r >> 2;
+                u32x4 kw[8][2];
 #pragma unroll
-            for (int tt = 0; tt < 4; ++tt) o[tt] = O0[tt] * gam[tt];
+                for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-            for (int tt = 0, f = 0; tt < 4; ++tt)
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
+                        const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
+                        kw[kt][kk] = cat(ld_tr(&KWs[t1][8 * (pc ^ (t1 & 15)) + hf]),
+                                         ld_tr(&KWs[t2][8 * (pc ^ (t2 & 15)) + hf]));
+                    }
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) S[kt] *= gC;
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+                    for (int kt = 0; kt < 8; ++kt) {
+                        S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(eh[kk]), S[kt]);
+                        S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(el[kk]), S[kt]);
+                    }
+            }
+            publish_state();  // for the next chunk (the side wave read this chunk's before B1)
+        } else {
+            if (c + 1 < NT) issue(c + 1, bb ^ 1);
+            // O0 = Q S from the published state fragments
+            f32x4 O[4];
+            {
+                u32x4 qa[4][4], sh[4], sl[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) qa[kk][tt] = frag_wide(B.Q, 16 * tt + r, kk, q);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    sh[kk] = sm.Sx[w][2 * kk][l];
+                    sl[kk] = sm.Sx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sh[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sl[kk]), O[tt]);
+                    }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) O[tt] *= *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
+            }
+            // A fragments of the two P terms (record), read before the first barrier:
+            // the next chunk's copy into the same tiles is issued right after it
+            u32x4 ph[6], pl[6];
+#pragma unroll
+            for (int tt = 0, f = 0; tt < 4; ++tt) {
+                const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
                 for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                    o[tt] = mfma(as_bf16x8(pha[f]), as_bf16x8(dh[kk]), o[tt]);
-                    o[tt] = mfma(as_bf16x8(pha[f]), as_bf16x8(dl[kk]), o[tt]);
-                    o[tt] = mfma(as_bf16x8(pla[f]), as_bf16x8(dh[kk]), o[tt]);
+                    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                    ph[f] = cat(ld8(&sm.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Ph[t][8 * (p2 ^ sw) + hf]));
+                    pl[f] = cat(ld8(&sm.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Pl[t][8 * (p2 ^ sw) + hf]));
                 }
-            // token 4 q of the chunk, value column cw + r; tokens are H * 128 elements apart
-            const long tstr = (long)p.H * kD;
-            uint16_t *dst = O + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
-            if (n == kC) {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; i += 2) {
-                        const uint32_t o2 = pk_bf16(o[tt][i], o[tt][i + 1]);
-                        dst[(16 * tt + i) * tstr] = (uint16_t)(o2 & 0xffffu);
-                        dst[(16 * tt + i + 1) * tstr] = (uint16_t)(o2 >> 16);
-                    }
-            } else {
-#pragma unroll
-                for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * tt + 4 * q + i < n) dst[(16 * tt + i) * tstr] = f32_to_bf16(o[tt][i]);
             }
+            lds_barrier();  // B1: D published; V and the P terms of this chunk consumed
+            if (c + 1 < NT) issue_late(c + 1);
+
+            // O += P D, then stored per lane (4 tokens of one value column per tile)
+            {
+                u32x4 dh[2], dl[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    dh[kk] = sm.Dx[w][2 * kk][l];
+                    dl[kk] = sm.Dx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0, f = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dh[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dl[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(pl[f]), as_bf16x8(dh[kk]), O[tt]);
+                    }
+                const long tstr = (long)p.H * kD;  // tokens are H * 128 elements apart
+                uint16_t *dst = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
+                if (n == kC) {
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; i += 2) {
+                            const uint32_t o2 = pk_bf16(O[tt][i], O[tt][i + 1]);
+                            dst[(16 * tt + i) * tstr] = (uint16_t)(o2 & 0xffffu);
+                            dst[(16 * tt + i + 1) * tstr] = (uint16_t)(o2 >> 16);
+                        }
+                } else {
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * tt + 4 * q + i < n) dst[(16 * tt + i) * tstr] = f32_to_bf16(O[tt][i]);
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
         }
-        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
-        __syncthreads();                     // ... for both waves; this buffer is free again
+        __syncthreads();  // B2: next buffer complete, next state published, this buffer free
     }
 
-    if (p.ST) {
+    if (chain && p.ST) {
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
@@ -903,9 +997,9 @@ __global__ void __launch_bounds__(128) gdr_state_cols_kernel(ChunkParams p, int 
     }
 }
 
-// State kernel: 16 / 32 = the four-wave kernel with that many value columns per
-// workgroup (32 by default), 1 = the column-owner kernel (selected by flags).
-int state_variant(const ChunkParams &p) { return p.state_cols == 16 || p.state_cols == 1 ? p.state_cols : 32; }
+// State kernel: 1 = the wave-specialised kernel (default), 16 / 32 = the four-wave
+// kernel with that many value columns per workgroup (selected by flags, for testing).
+int state_variant(const ChunkParams &p) { return p.state_cols == 16 || p.state_cols == 32 ? p.state_cols : 1; }
 
 }  // namespace
 
@@ -936,9 +1030,9 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     const bool sep = p.kw != p.k;
     const int bv = state_variant(p);
     if (bv == 1) {
-        const void *fn = sep ? reinterpret_cast<const void *>(&gdr_state_cols_kernel<true>)
-                             : reinterpret_cast<const void *>(&gdr_state_cols_kernel<false>);
-        return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(128), args, 0, st);
+        const void *fn = sep ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
+                             : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
+        return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(256), args, 0, st);
     }
     const void *fn = bv == 32 ? (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<32, true>)
                                      : reinterpret_cast<const void *>(&gdr_state_kernel<32, false>))

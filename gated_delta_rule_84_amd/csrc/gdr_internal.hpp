@@ -14,7 +14,7 @@ struct ChunkParams {
     int gate_bf16;  // alpha, beta_k, beta_v are bf16 (else fp32)
     int alpha_ch;   // alpha is per key channel
     int beta_mode;  // 0 scalar, 1 shared vector, 2 separate k / v vectors
-    int state_cols; // matrix-core state kernel: 16 / 32 four-wave width, 1 column-owner, 0 default
+    int state_cols; // matrix-core state kernel: 16 / 32 four-wave width, 1 wave-specialised, 0 default
     const void *q, *k, *kw, *v, *alpha, *beta_k, *beta_v;  // kw never NULL here (defaults to k)
     const float *S0;  // may be NULL (zero state)
     void *o;

@@ -80,12 +80,11 @@ typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_
 /* Flags (gdr_desc.flags). */
 #define GDR_FLAG_GENERIC_PATH 0x1  /* prefill: use the fp32 vector-ALU chunk kernel even where
                                       the bf16 matrix-core kernel applies (testing aid) */
-#define GDR_FLAG_STATE_COLS16 0x2  /* prefill, matrix-core kernel: run the state recurrence with
-                                      16 value columns per workgroup (testing aid) */
-#define GDR_FLAG_STATE_COLS32 0x4  /* the same with 32 value columns (the default) */
-#define GDR_FLAG_STATE_WAVECOLS 0x8 /* prefill, matrix-core kernel: the state kernel whose waves
-                                      each own 16 value columns (testing aid); at most one of
-                                      the three STATE flags */
+#define GDR_FLAG_STATE_COLS16 0x2  /* prefill, matrix-core path: run the state recurrence with the
+                                      four-wave kernel, 16 value columns per workgroup (testing aid) */
+#define GDR_FLAG_STATE_COLS32 0x4  /* the same with 32 value columns per workgroup (testing aid) */
+#define GDR_FLAG_STATE_WAVECOLS 0x8 /* the wave-specialised state kernel (the default); at most one
+                                      of the three STATE flags */
 
 /* Problem descriptor.
  *   B, H  >= 0; T >= 0 (prefill only; ignored by decode).

@@ -11,7 +11,8 @@ from tests.gpu_util import TOL, gpu, log, run_prefill, upload
 
 pytestmark = pytest.mark.gpu
 
-REC_BYTES = 25216  # per-chunk record: T bf16[64][64] | P hi bf16[64][64] | P lo | gam f32[64] | fac f32[64] | gC
+REC_BYTES = 25728  # per-chunk record: T bf16[64][64] | P hi bf16[64][64] | P lo | gam f32[64] | fac f32[64]
+#                    | gC (128-byte slot) | g f32[64] | beta f32[64]
 
 
 def _bf16(u16):
@@ -46,6 +47,8 @@ def test_prep_record_matches_numpy(T, write_key):
             gam = rec[24576:24832].view(np.float32).astype(np.float64)
             fac = rec[24832:25088].view(np.float32).astype(np.float64)
             gC = float(rec[25088:25092].view(np.float32)[0])
+            glog = rec[25216:25472].view(np.float32).astype(np.float64)
+            beta = rec[25472:25728].view(np.float32).astype(np.float64)
             t0, n = 64 * c, min(64, T - 64 * c)
             K = np.zeros((64, 128)); KW = np.zeros((64, 128)); Q = np.zeros((64, 128))
             K[:n] = f["k"][b, t0:t0 + n, h]
@@ -61,6 +64,8 @@ def test_prep_record_matches_numpy(T, write_key):
             worst["T"] = max(worst["T"], np.abs(Tg - Tr).max() / np.abs(Tr).max())
             worst["P"] = max(worst["P"], np.abs(Pg - Pr).max() / max(np.abs(Pr).max(), 1e-30))
             worst["gam"] = max(worst["gam"], np.abs(gam - np.exp(gcum)).max())
+            worst["g"] = max(worst.get("g", 0.0), np.abs(glog - gcum).max())
+            worst["beta"] = max(worst.get("beta", 0.0), np.abs(beta - be).max())
             fr = be * np.exp(gcum[n - 1] - gcum)
             fr[n:] = 0
             worst["fac"] = max(worst["fac"], np.abs(fac - fr).max())
@@ -69,6 +74,7 @@ def test_prep_record_matches_numpy(T, write_key):
     assert worst["T"] < 8e-3      # stored in bf16
     assert worst["P"] < 1e-5      # two bf16 terms
     assert worst["gam"] < 1e-5 and worst["fac"] < 1e-5
+    assert worst["g"] < 1e-4 and worst["beta"] < 1e-6
 
 
 def test_mfma_and_generic_paths_agree():
@@ -105,12 +111,12 @@ STATE_CASES = [
 
 
 @pytest.mark.parametrize("name,w", STATE_CASES, ids=[c[0] for c in STATE_CASES])
-@pytest.mark.parametrize("variant", ["cols", "four_wave16", "four_wave32"])
+@pytest.mark.parametrize("variant", ["wave_specialised", "four_wave16", "four_wave32"])
 def test_state_kernel_variants(name, w, variant):
-    """Every state-kernel variant (the column-owner kernel; the four-wave kernel with
-    16 or 32 value columns per workgroup, 32 being the default) against the oracle."""
+    """Every state-kernel variant (the wave-specialised kernel, the default; the
+    four-wave kernel with 16 or 32 value columns per workgroup) against the oracle."""
     torch, g = gpu()
-    flag = {"cols": g.GDR_FLAG_STATE_WAVECOLS, "four_wave16": g.GDR_FLAG_STATE_COLS16,
+    flag = {"wave_specialised": g.GDR_FLAG_STATE_WAVECOLS, "four_wave16": g.GDR_FLAG_STATE_COLS16,
             "four_wave32": g.GDR_FLAG_STATE_COLS32}[variant]
     r = run_prefill(w, gi.make_prefill(w), flags=flag)
     assert r["path"] == g.PATH_MFMA
