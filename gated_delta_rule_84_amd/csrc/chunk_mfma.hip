@@ -93,11 +93,13 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // prep kernel
 // ---------------------------------------------------------------------------
+// GBF16: the gates are bf16 (compile time, so the gate loads carry no branch)
+template <bool GBF16>
 __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int NT) {
     __shared__ float gl[kC], bl[kC];
     __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part
     __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform; first holds the two P terms
-    __shared__ float Xs[3][16][17];
+    __shared__ __align__(16) float Xs[4][16][20];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
     uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
     uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
 
@@ -105,28 +107,17 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
     const int c = blk % NT, bh = blk / NT;
     const int b = bh / p.H, h = bh % p.H;
     const int t0 = c * kC, n = min(kC, p.T - t0);
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
+    const int tid = threadIdx.x, l = tid & 63, r = l & 15, q = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
     auto tok = [&](int t) -> long { return ((long)b * p.T + t0 + t) * p.H + h; };
     const uint16_t *K = static_cast<const uint16_t *>(p.k);
     const uint16_t *KW = static_cast<const uint16_t *>(p.kw);
     const uint16_t *Q = static_cast<const uint16_t *>(p.q);
 
-    // cumulative log decay and beta (wave 0)
-    if (w == 0) {
-        float la = 0.f, be = 0.f;
-        if (l < n) {
-            la = logf(ld_gate(p.alpha, tok(l), p.gate_bf16));
-            be = ld_gate(p.beta_k, tok(l), p.gate_bf16);
-        }
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(la, off);
-            if (l >= off) la += y;
-        }
-        gl[l] = la;
-        bl[l] = be;
-    }
-
+    // gates first (rows past the chunk end read the last row, replaced below), so
+    // that the gate math waits for them alone, not for the tiles issued after them
+    const float a_raw = ld_gate(p.alpha, tok(min(l, n - 1)), GBF16);
+    const float b_raw = ld_gate(p.beta_k, tok(min(l, n - 1)), GBF16);
     // Gram row-block I = w (tiles J <= w) and score row-block IP = 3 - w (tiles J <= IP)
     const int IG = w, IP = 3 - w;
     // rows past the end of a short chunk read the last valid row; their Gram and
@@ -158,6 +149,19 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
             if (J <= IP) accP[J] = mfma(as_bf16x8(qa[kk]), as_bf16x8(kb[J][kk]), accP[J]);
         }
     }
+    // cumulative log decay and beta (wave 0)
+    if (w == 0) {
+        float la = l < n ? logf(a_raw) : 0.f;
+        const float be = l < n ? b_raw : 0.f;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(la, off);
+            if (l >= off) la += y;
+        }
+        gl[l] = la;
+        bl[l] = be;
+    }
+
     __syncthreads();
 
     // decay / beta weights; Gram to LDS (fp32), scores to LDS as two bf16 terms.
@@ -175,13 +179,19 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 16 * J + r;
+            // computed for every lane and selected (no divergent branch); the exponent is
+            // clamped at 0, which changes only entries the mask discards (g decreases in t)
             if (J <= IG) {
                 const int t = 16 * IG + 4 * q + i;
-                As[t][s] = (s < t && t < n) ? accG[J][i] * bS[J] * __expf(gG[i] - gS[J]) : 0.f;
+                const float v = accG[J][i] * bS[J] * __expf(fminf(gG[i] - gS[J], 0.f));
+                As[t][s] = (s < t && t < n) ? v : 0.f;
             }
             const int tp = 16 * IP + 4 * q + i;
             float pv = 0.f;
-            if (J <= IP && s <= tp && tp < n) pv = accP[J][i] * bS[J] * __expf(gP[i] - gS[J]);
+            if (J <= IP) {
+                const float v = accP[J][i] * bS[J] * __expf(fminf(gP[i] - gS[J], 0.f));
+                pv = (s <= tp && tp < n) ? v : 0.f;
+            }
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
             Ph[tp][s] = __builtin_bit_cast(uint16_t, hi);
@@ -225,33 +235,60 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
         for (int rr = 0; rr < 16; ++rr) Ts[base + rr][base + cc] = col[rr];
     }
     __syncthreads();
-    // off-diagonal blocks by distance d: T_IJ = -T_II * sum_{K=J}^{I-1} A_IK T_KJ
-    for (int d = 1; d < 4; ++d) {
-        const int nb = 4 - d;
-        for (int e = tid; e < nb * 256; e += kThreads) {
-            const int J = e >> 8, I = J + d, rr = (e >> 4) & 15, cc = e & 15;
-            float x = 0.f;
-            for (int Kb = J; Kb < I; ++Kb) {
+    // Off-diagonal 16 x 16 blocks on fp32 matrix cores (v_mfma_f32_16x16x4_f32; lane
+    // (r, q) supplies A[r][k] and B[k][r] of k step s, C tiles as for bf16), by the
+    // 2 x 2 block inverse [[T_a, 0], [L, T_b]]^-1 lower-left = -T_b L T_a, first on the
+    // two 32 x 32 diagonal halves, then on the 64 x 64 matrix.
+    {
+        // C = M1 M2 for 16 x 16 blocks of LDS matrices (row pitch ld1, ld2)
+        auto mm = [&](const float *M1, int ld1, const float *M2, int ld2, f32x4 acc) __attribute__((always_inline)) {
 #pragma unroll
-                for (int m4 = 0; m4 < 4; ++m4) {
-                    const f32x4 a = *reinterpret_cast<const f32x4 *>(&As[16 * I + rr][16 * Kb + 4 * m4]);
+            for (int s4 = 0; s4 < 4; ++s4)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * s4 + q], M2[(4 * s4 + q) * ld2 + r], acc, 0, 0, 0);
+            return acc;
+        };
+        // C = M1 X with X a C tile held in registers: k step s4 takes row 4 q + s4 of X
+        auto mmr = [&](const float *M1, int ld1, f32x4 X, f32x4 acc) __attribute__((always_inline)) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) x += a[u] * Ts[16 * Kb + 4 * m4 + u][16 * J + cc];
-                }
-            }
-            Xs[J][rr][cc] = x;
+            for (int s4 = 0; s4 < 4; ++s4)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * q + s4], X[s4], acc, 0, 0, 0);
+            return acc;
+        };
+        auto Ab = [&](int I, int J) { return &As[16 * I][16 * J]; };
+        auto Tb = [&](int I, int J) { return &Ts[16 * I][16 * J]; };
+        constexpr int LA = kC + 4, LT = kC + 8;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        auto storeT = [&](int I, int J, f32x4 v) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ts[16 * I + 4 * q + i][16 * J + r] = -v[i];
+        };
+        // level 1: T_10 (wave 0), T_32 (wave 1); waves 2, 3 start the 64 x 64 level
+        f32x4 xa = z, xb = z;
+        if (w < 2) {
+            const int o = 2 * w;  // block offset of this 32 x 32 half
+            const f32x4 x = mm(Ab(o + 1, o), LA, Tb(o, o), LT, z);
+            storeT(o + 1, o, mmr(Tb(o + 1, o + 1), LT, x, z));
+        } else {
+            const int I = w;      // X_I0 (partial) and X_I1 = A_I1 T_11 for block row I = 2, 3
+            xa = mm(Ab(I, 0), LA, Tb(0, 0), LT, z);
+            xb = mm(Ab(I, 1), LA, Tb(1, 1), LT, z);
         }
         __syncthreads();
-        for (int e = tid; e < nb * 256; e += kThreads) {
-            const int J = e >> 8, I = J + d, rr = (e >> 4) & 15, cc = e & 15;
-            float x = 0.f;
+        if (w >= 2) {  // X_I0 += A_I1 T_10; publish X_I0, X_I1
+            const int I = w;
+            xa = mm(Ab(I, 1), LA, Tb(1, 0), LT, xa);
 #pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 tr = *reinterpret_cast<const f32x4 *>(&Ts[16 * I + rr][16 * I + 4 * m4]);
-#pragma unroll
-                for (int u = 0; u < 4; ++u) x -= tr[u] * Xs[J][4 * m4 + u][cc];
+            for (int i = 0; i < 4; ++i) {
+                Xs[2 * (I - 2)][4 * q + i][r] = xa[i];
+                Xs[2 * (I - 2) + 1][4 * q + i][r] = xb[i];
             }
-            Ts[16 * I + rr][16 * J + cc] = x;
+        }
+        __syncthreads();
+        {   // T_IJ = -sum_{M=2}^{I} T_IM X_MJ for I = 2 + (w >> 1), J = w & 1
+            const int I = 2 + (w >> 1), J = w & 1;
+            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 20, z);
+            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 20, t);
+            storeT(I, J, t);
         }
         __syncthreads();
     }
@@ -1021,7 +1058,9 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     int nb = (int)nbh;
     {
         void *args[] = {&arg, &nt};
-        const hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(&gdr_prep_kernel),
+        const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
+                                       : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
+        const hipError_t e = hipLaunchKernel(prep,
                                              dim3((unsigned)(nbh * NT)), dim3(kThreads), args, 0, st);
         if (e != hipSuccess) return e;
     }
