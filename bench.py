@@ -93,7 +93,8 @@ def cpu_baseline(w, x, budget_heads):
     heads = list(range(min(budget_heads, w.B * w.H)))
     threads = min(len(heads), os.cpu_count() or 1, 16)
     t0 = time.perf_counter()
-    oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta_k"], heads=heads, nthreads=threads)
+    oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta_k"], k_w=f["k_w"], beta_v=f["beta_v"], S0=f["S0"],
+                   heads=heads, nthreads=threads)
     dt = time.perf_counter() - t0
     tokens = w.T * len(heads) / w.H  # tokens carry all H heads in the GPU metric
     return {"value": tokens / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
@@ -114,6 +115,8 @@ def main():
     ap.add_argument("--only-prefill", action="store_true")
     ap.add_argument("--state-kernel", choices=["cols16", "cols32", "wavecols"], default=None,
                     help="matrix-core state kernel (default: the library's choice)")
+    ap.add_argument("--workload", choices=["gdn", "kda_fg2plus", "osdn_long"], default="gdn",
+                    help="prefill workload (default: the B4 H16 T4096 GDN batch the metric is quoted on)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy 3 times (HBM counter calibration)")
     args = ap.parse_args()
@@ -139,7 +142,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
         return
-    w = gi.GDN_PREFILL
+    w = {"gdn": gi.GDN_PREFILL, "kda_fg2plus": gi.KDA_FG2PLUS_PREFILL, "osdn_long": gi.OSDN_LONG_PREFILL}[args.workload]
     x = gi.make_prefill(w)
     d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
          for k in x}
@@ -148,7 +151,7 @@ def main():
                                                     "cols32": g.GDR_FLAG_STATE_COLS32,
                                                     "wavecols": g.GDR_FLAG_STATE_WAVECOLS}[args.state_kernel])
     path = g.gdr_chunk_fwd_path(desc)
-    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.bfloat16, device=dev)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device=dev)
     ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     wsz = g.gdr_chunk_fwd_workspace_size(desc)
     ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
@@ -207,7 +210,10 @@ def main():
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
-                   "gates": "fp32 scalar alpha, beta", "S0": "zero", "global_batch": w.B, "seq_len": w.T,
+                   "gates": ("fp32 " + ("channel" if w.alpha_mode else "scalar") + " alpha, "
+                             + ["scalar", "shared-vector", "key/value-vector"][w.beta_mode] + " beta"
+                             + (", write key" if w.write_key else "")),
+                   "S0": "nonzero" if w.s0_std > 0 else "zero", "global_batch": w.B, "seq_len": w.T,
                    "parallelism": "single GPU", "kernel_path": {1: "bf16-mfma", 2: "fp32-valu"}[path]},
         "roofline": roof,
         "mfma_frac": flops / (ms_event * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),

@@ -107,6 +107,9 @@ STATE_CASES = [
     ("osdn_kw_S0", gi.OSDN_LONG_PREFILL.scaled(B=1, T=300, H=5, seed=62)),
     ("gdn_T_lt_C", gi.GDN_PREFILL.scaled(B=2, T=41, H=2, s0_std=0.02, seed=63)),
     ("gdn_T_one_chunk", gi.GDN_PREFILL.scaled(B=1, T=64, H=9, seed=64)),
+    # 64 (batch, head) pairs: the wave-specialised kernel takes two column tiles per workgroup
+    ("gdn_64heads_ragged", gi.GDN_PREFILL.scaled(B=4, T=130, H=16, seed=65)),
+    ("osdn_64heads_S0", gi.OSDN_LONG_PREFILL.scaled(B=2, T=100, H=32, seed=66)),
 ]
 
 
