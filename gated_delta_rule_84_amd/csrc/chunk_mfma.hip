@@ -1010,8 +1010,9 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                         for (int i = 0; i < 4; i += 2) {
                             const uint32_t o2 = pk_bf16(O[tt][i], O[tt][i + 1]);
-                            dst[(16 * tt + i) * tstr] = (uint16_t)(o2 & 0xffffu);
-                            dst[(16 * tt + i + 1) * tstr] = (uint16_t)(o2 >> 16);
+                            // the output is never read back here: non-temporal stores
+                            __builtin_nontemporal_store((uint16_t)(o2 & 0xffffu), dst + (16 * tt + i) * tstr);
+                            __builtin_nontemporal_store((uint16_t)(o2 >> 16), dst + (16 * tt + i + 1) * tstr);
                         }
                 } else {
 #pragma unroll
