@@ -60,6 +60,21 @@ constexpr int kRecGlog = 25216; // f32 [64]  g_t (cumulative log decay inside th
 constexpr int kRecBeta = 25472; // f32 [64]  beta_t, 0 past the chunk end
 constexpr int kRecBytes = 25728;
 
+// per-chunk workspace record of the general-gate path (channel decay and/or beta
+// vectors): every key-side operand already carries its decay and beta, as two bf16
+// terms (hi + lo) each
+constexpr int kRcT = 0;          // bf16 [64][64]   Tm
+constexpr int kRcPh = 8192;      // bf16 [64][64]   P, leading term
+constexpr int kRcPl = 16384;     // bf16 [64][64]   P, remainder
+constexpr int kRcUh = 24576;     // bf16 [64][128]  U_t = u_t (.) e^{g_t}              (erase key)
+constexpr int kRcUl = 40960;
+constexpr int kRcQh = 57344;     // bf16 [64][128]  Q_t = q_t (.) e^{g_t}
+constexpr int kRcQl = 73728;
+constexpr int kRcWh = 90112;     // bf16 [64][128]  W_t = w_t (.) e^{g_C - g_t}        (write key)
+constexpr int kRcWl = 106496;
+constexpr int kRcGC = 122880;    // f32 [128]       e^{g_C} per key channel
+constexpr int kRcBytes = 123392;
+
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -88,6 +103,130 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// ---------------------------------------------------------------------------
+// pieces shared by the two prep kernels (256 threads, four waves)
+// ---------------------------------------------------------------------------
+// Tm = (I + A)^{-1} for the strictly lower 64 x 64 A in As, into the lower part of
+// Ts (fp32; the unit diagonal and the upper part are not written).  Ends with a
+// barrier; starts reading As, so the caller has published it with a barrier.
+__device__ __forceinline__ void ut_transform(float (*As)[kC + 4], float (*Ts)[kC + 8], float (*Xs)[16][20],
+                                             const int w, const int l) {
+    const int r = l & 15, q = l >> 4;
+    // diagonal 16 x 16 blocks of (I + A)^{-1}: wave w, lane c < 16 owns column c;
+    // row rr of the block is read as four 16-byte loads
+    if (l < 16) {
+        const int base = 16 * w, cc = l;
+        float col[16];
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) {
+            float a[16];
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4) {
+                const f32x4 x = *reinterpret_cast<const f32x4 *>(&As[base + rr][base + 4 * m4]);
+                a[4 * m4] = x[0];
+                a[4 * m4 + 1] = x[1];
+                a[4 * m4 + 2] = x[2];
+                a[4 * m4 + 3] = x[3];
+            }
+            float v = rr == cc ? 1.f : 0.f;
+#pragma unroll
+            for (int m = 0; m < rr; ++m) v -= a[m] * col[m];
+            col[rr] = v;
+        }
+#pragma unroll
+        for (int rr = 0; rr < 16; ++rr) Ts[base + rr][base + cc] = col[rr];
+    }
+    __syncthreads();
+    // Off-diagonal 16 x 16 blocks on fp32 matrix cores (v_mfma_f32_16x16x4_f32; lane
+    // (r, q) supplies A[r][k] and B[k][r] of k step s, C tiles as for bf16), by the
+    // 2 x 2 block inverse [[T_a, 0], [L, T_b]]^-1 lower-left = -T_b L T_a, first on the
+    // two 32 x 32 diagonal halves, then on the 64 x 64 matrix.
+    {
+        // C = M1 M2 for 16 x 16 blocks of LDS matrices (row pitch ld1, ld2)
+        auto mm = [&](const float *M1, int ld1, const float *M2, int ld2, f32x4 acc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * s4 + q], M2[(4 * s4 + q) * ld2 + r], acc, 0, 0, 0);
+            return acc;
+        };
+        // C = M1 X with X a C tile held in registers: k step s4 takes row 4 q + s4 of X
+        auto mmr = [&](const float *M1, int ld1, f32x4 X, f32x4 acc) __attribute__((always_inline)) {
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * q + s4], X[s4], acc, 0, 0, 0);
+            return acc;
+        };
+        auto Ab = [&](int I, int J) { return &As[16 * I][16 * J]; };
+        auto Tb = [&](int I, int J) { return &Ts[16 * I][16 * J]; };
+        constexpr int LA = kC + 4, LT = kC + 8;
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        auto storeT = [&](int I, int J, f32x4 v) __attribute__((always_inline)) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) Ts[16 * I + 4 * q + i][16 * J + r] = -v[i];
+        };
+        // level 1: T_10 (wave 0), T_32 (wave 1); waves 2, 3 start the 64 x 64 level
+        f32x4 xa = z, xb = z;
+        if (w < 2) {
+            const int o = 2 * w;  // block offset of this 32 x 32 half
+            const f32x4 x = mm(Ab(o + 1, o), LA, Tb(o, o), LT, z);
+            storeT(o + 1, o, mmr(Tb(o + 1, o + 1), LT, x, z));
+        } else {
+            const int I = w;      // X_I0 (partial) and X_I1 = A_I1 T_11 for block row I = 2, 3
+            xa = mm(Ab(I, 0), LA, Tb(0, 0), LT, z);
+            xb = mm(Ab(I, 1), LA, Tb(1, 1), LT, z);
+        }
+        __syncthreads();
+        if (w >= 2) {  // X_I0 += A_I1 T_10; publish X_I0, X_I1
+            const int I = w;
+            xa = mm(Ab(I, 1), LA, Tb(1, 0), LT, xa);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                Xs[2 * (I - 2)][4 * q + i][r] = xa[i];
+                Xs[2 * (I - 2) + 1][4 * q + i][r] = xb[i];
+            }
+        }
+        __syncthreads();
+        {   // T_IJ = -sum_{M=2}^{I} T_IM X_MJ for I = 2 + (w >> 1), J = w & 1
+            const int I = 2 + (w >> 1), J = w & 1;
+            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 20, z);
+            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 20, t);
+            storeT(I, J, t);
+        }
+        __syncthreads();
+    }
+
+}
+
+// The lower-triangular Tm (fp32 rows in Ts, unit diagonal implied) to the record as
+// bf16 rows of 64, 16 bytes per store.
+__device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[kC + 8], const int tid) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {  // 512 pieces of 8 bf16
+        const int pc = tid + 256 * m, row = pc >> 3, c0 = (pc & 7) * 8;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int ca = c0 + 2 * j, cb = ca + 1;
+            const float va = ca < row ? Ts[row][ca] : (ca == row ? 1.f : 0.f);
+            const float vb = cb < row ? Ts[row][cb] : (cb == row ? 1.f : 0.f);
+            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)va) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)vb) << 16);
+        }
+        *reinterpret_cast<u32x4 *>(dst + (row * kC + c0) * 2) = o;
+    }
+}
+
+// The two bf16 terms of P (rows of 64 in LDS, pitch kC + 8) to the record.
+__device__ __forceinline__ void store_p(char *dh, char *dl, const uint16_t (*Ph)[kC + 8],
+                                        const uint16_t (*Pl)[kC + 8], const int tid) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const int pc = tid + 256 * m, row = pc >> 3, c0 = (pc & 7) * 8;
+        *reinterpret_cast<u32x4 *>(dh + (row * kC + c0) * 2) = *reinterpret_cast<const u32x4 *>(&Ph[row][c0]);
+        *reinterpret_cast<u32x4 *>(dl + (row * kC + c0) * 2) = *reinterpret_cast<const u32x4 *>(&Pl[row][c0]);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -200,114 +339,13 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
     }
     __syncthreads();
     char *rec = static_cast<char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {  // P terms to the record, 16 bytes per store
-        const int pc = tid + 256 * m, row = pc >> 3, c0 = (pc & 7) * 8;
-        *reinterpret_cast<u32x4 *>(rec + kRecPhi + (row * kC + c0) * 2) =
-            *reinterpret_cast<const u32x4 *>(&Ph[row][c0]);
-        *reinterpret_cast<u32x4 *>(rec + kRecPlo + (row * kC + c0) * 2) =
-            *reinterpret_cast<const u32x4 *>(&Pl[row][c0]);
-    }
+    store_p(rec + kRecPhi, rec + kRecPlo, Ph, Pl, tid);
     __syncthreads();
 
-    // diagonal 16 x 16 blocks of (I + A)^{-1}: wave w, lane c < 16 owns column c;
-    // row rr of the block is read as four 16-byte loads
-    if (l < 16) {
-        const int base = 16 * w, cc = l;
-        float col[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float a[16];
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&As[base + rr][base + 4 * m4]);
-                a[4 * m4] = x[0];
-                a[4 * m4 + 1] = x[1];
-                a[4 * m4 + 2] = x[2];
-                a[4 * m4 + 3] = x[3];
-            }
-            float v = rr == cc ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < rr; ++m) v -= a[m] * col[m];
-            col[rr] = v;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) Ts[base + rr][base + cc] = col[rr];
-    }
-    __syncthreads();
-    // Off-diagonal 16 x 16 blocks on fp32 matrix cores (v_mfma_f32_16x16x4_f32; lane
-    // (r, q) supplies A[r][k] and B[k][r] of k step s, C tiles as for bf16), by the
-    // 2 x 2 block inverse [[T_a, 0], [L, T_b]]^-1 lower-left = -T_b L T_a, first on the
-    // two 32 x 32 diagonal halves, then on the 64 x 64 matrix.
-    {
-        // C = M1 M2 for 16 x 16 blocks of LDS matrices (row pitch ld1, ld2)
-        auto mm = [&](const float *M1, int ld1, const float *M2, int ld2, f32x4 acc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * s4 + q], M2[(4 * s4 + q) * ld2 + r], acc, 0, 0, 0);
-            return acc;
-        };
-        // C = M1 X with X a C tile held in registers: k step s4 takes row 4 q + s4 of X
-        auto mmr = [&](const float *M1, int ld1, f32x4 X, f32x4 acc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * q + s4], X[s4], acc, 0, 0, 0);
-            return acc;
-        };
-        auto Ab = [&](int I, int J) { return &As[16 * I][16 * J]; };
-        auto Tb = [&](int I, int J) { return &Ts[16 * I][16 * J]; };
-        constexpr int LA = kC + 4, LT = kC + 8;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        auto storeT = [&](int I, int J, f32x4 v) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[16 * I + 4 * q + i][16 * J + r] = -v[i];
-        };
-        // level 1: T_10 (wave 0), T_32 (wave 1); waves 2, 3 start the 64 x 64 level
-        f32x4 xa = z, xb = z;
-        if (w < 2) {
-            const int o = 2 * w;  // block offset of this 32 x 32 half
-            const f32x4 x = mm(Ab(o + 1, o), LA, Tb(o, o), LT, z);
-            storeT(o + 1, o, mmr(Tb(o + 1, o + 1), LT, x, z));
-        } else {
-            const int I = w;      // X_I0 (partial) and X_I1 = A_I1 T_11 for block row I = 2, 3
-            xa = mm(Ab(I, 0), LA, Tb(0, 0), LT, z);
-            xb = mm(Ab(I, 1), LA, Tb(1, 1), LT, z);
-        }
-        __syncthreads();
-        if (w >= 2) {  // X_I0 += A_I1 T_10; publish X_I0, X_I1
-            const int I = w;
-            xa = mm(Ab(I, 1), LA, Tb(1, 0), LT, xa);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Xs[2 * (I - 2)][4 * q + i][r] = xa[i];
-                Xs[2 * (I - 2) + 1][4 * q + i][r] = xb[i];
-            }
-        }
-        __syncthreads();
-        {   // T_IJ = -sum_{M=2}^{I} T_IM X_MJ for I = 2 + (w >> 1), J = w & 1
-            const int I = 2 + (w >> 1), J = w & 1;
-            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 20, z);
-            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 20, t);
-            storeT(I, J, t);
-        }
-        __syncthreads();
-    }
+    ut_transform(As, Ts, Xs, w, l);
 
     // write the rest of the record
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {  // Tm: 512 pieces of 8 bf16
-        const int pc = tid + 256 * m, row = pc >> 3, c0 = (pc & 7) * 8;
-        u32x4 o;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int ca = c0 + 2 * j, cb = ca + 1;
-            const float va = ca < row ? Ts[row][ca] : (ca == row ? 1.f : 0.f);
-            const float vb = cb < row ? Ts[row][cb] : (cb == row ? 1.f : 0.f);
-            o[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)va) |
-                   ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)vb) << 16);
-        }
-        *reinterpret_cast<u32x4 *>(rec + kRecT + (row * kC + c0) * 2) = o;
-    }
+    store_ut(rec + kRecT, Ts, tid);
     if (tid < kC) {
         float *gam = reinterpret_cast<float *>(rec + kRecGam);
         float *fac = reinterpret_cast<float *>(rec + kRecFac);
@@ -317,6 +355,178 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int N
         reinterpret_cast<float *>(rec + kRecGlog)[tid] = gl[tid];
         reinterpret_cast<float *>(rec + kRecBeta)[tid] = bl[tid];
     }
+}
+
+
+// ---------------------------------------------------------------------------
+// prep kernel, general gates
+// ---------------------------------------------------------------------------
+// One 256-thread block per chunk for a forget gate per key channel (ACH) and / or
+// beta vectors (BVEC; u = sqrt(beta^k) (.) k, w = sqrt(beta^k) (.) k_w; a scalar beta
+// gives u = k, w = beta k_w).  With g_t the per-channel cumulative log decay inside
+// the chunk, the decay factor e^{g_t - g_s} of the Gram matrix and of the scores
+// splits per channel into a row and a column factor, so both are plain products of
+// rescaled operands:
+//     A = strictly-lower( U What^T ),  P = lower-incl-diag( Q What^T ),
+//     U = u (.) e^{g_t},  Q = q (.) e^{g_t},  What = w (.) e^{-g_t}
+// (FG2-GDN page, section 3: the factored decay of the chunkwise form).  The factor
+// e^{-g_t} bounds the decay one chunk may accumulate per channel (about e^{-80}).
+// The record carries U, Q and W = w (.) e^{g_C - g_t} as two bf16 terms, Tm and P
+// as for the scalar path, and e^{g_C} per channel.
+template <bool GBF16, bool ACH, bool BVEC>
+__global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, int NT) {
+    // the cumulative log decay g[t][i] is dead once the operands are formed; the
+    // Gram and UT arrays take its place
+    __shared__ __align__(16) float pool[kC * (kC + 4) + kC * (kC + 8)];
+    __shared__ __align__(16) uint16_t Whs[kC][kD + 8], Wls[kC][kD + 8];  // What, two bf16 terms
+    __shared__ __align__(16) float Xs[4][16][20];
+    float(*gs)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(pool);
+    float(*As)[kC + 4] = reinterpret_cast<float(*)[kC + 4]>(pool);
+    float(*Ts)[kC + 8] = reinterpret_cast<float(*)[kC + 8]>(pool + kC * (kC + 4));
+    uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
+    uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
+    static_assert(kC * (kD + 4) <= kC * (kC + 4) + kC * (kC + 8), "pool holds g");
+
+    const int blk = blockIdx.x;
+    const int c = blk % NT, bh = blk / NT;
+    const int b = bh / p.H, h = bh % p.H;
+    const int t0 = c * kC, n = min(kC, p.T - t0);
+    const int tid = threadIdx.x, l = tid & 63, r = l & 15, q = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    auto tok = [&](int t) -> long { return ((long)b * p.T + t0 + min(t, n - 1)) * p.H + h; };
+    const uint16_t *K = static_cast<const uint16_t *>(p.k);
+    const uint16_t *KW = static_cast<const uint16_t *>(p.kw);
+    const uint16_t *Q = static_cast<const uint16_t *>(p.q);
+    char *rec = static_cast<char *>(p.ws) + ((long)bh * NT + c) * kRcBytes;
+
+    // g[t][i]: thread (i, half) scans 32 tokens of channel i; the upper half then adds
+    // the lower half's total.  Tokens past the chunk end decay by 1.
+    {
+        const int i = tid & (kD - 1), hf = tid >> 7;
+        float a[32];
+#pragma unroll
+        for (int j = 0; j < 32; ++j)
+            a[j] = ACH ? ld_gate(p.alpha, tok(32 * hf + j) * kD + i, GBF16) : ld_gate(p.alpha, tok(32 * hf + j), GBF16);
+        float run = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            run += 32 * hf + j < n ? logf(a[j]) : 0.f;
+            gs[32 * hf + j][i] = run;
+        }
+        __syncthreads();
+        if (hf == 1) {
+            const float off = gs[31][i];
+#pragma unroll
+            for (int j = 0; j < 32; ++j) gs[32 + j][i] += off;
+        }
+        __syncthreads();
+        if (tid < kD) reinterpret_cast<float *>(rec + kRcGC)[tid] = __expf(gs[n - 1][tid]);
+    }
+
+    // operands: lane (r, q) of wave w forms keys 32 kk + 8 q .. + 7 of token t = 16 w + r
+    // for U, W, What and of token tp = 16 (3 - w) + r for Q; U and Q stay in registers
+    // as the A fragments of the Gram and score row blocks w and 3 - w
+    const int t = 16 * w + r, tp = 16 * (3 - w) + r;
+    const long rt = tok(t) * kD, rtp = tok(tp) * kD;
+    u32x4 uh[4], ul[4], qh[4], ql[4];
+    {
+        const float bsc = BVEC ? 0.f : ld_gate(p.beta_k, tok(t), GBF16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            const int k0 = 32 * kk + 8 * q;
+            const u32x4 kr = ld16(K + rt + k0), kwr = ld16(KW + rt + k0), qr = ld16(Q + rtp + k0);
+            float u8[8], q8[8], wh8[8], wt8[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const uint32_t kb = kr[j >> 1], kwb = kwr[j >> 1], qb = qr[j >> 1];
+                const float kv = __uint_as_float((j & 1) ? (kb & 0xffff0000u) : (kb << 16));
+                const float kwv = __uint_as_float((j & 1) ? (kwb & 0xffff0000u) : (kwb << 16));
+                const float qv = __uint_as_float((j & 1) ? (qb & 0xffff0000u) : (qb << 16));
+                float u = kv, wv = kwv;
+                if (BVEC) {
+                    const float sb = sqrtf(ld_gate(p.beta_k, rt + k0 + j, GBF16));
+                    u *= sb;
+                    wv *= sb;
+                } else {
+                    wv *= bsc;
+                }
+                const float g = gs[t][k0 + j], gq = gs[tp][k0 + j], gC = gs[n - 1][k0 + j];
+                u8[j] = t < n ? u * __expf(g) : 0.f;
+                wh8[j] = t < n ? wv * __expf(-g) : 0.f;
+                wt8[j] = t < n ? wv * __expf(gC - g) : 0.f;
+                q8[j] = tp < n ? qv * __expf(gq) : 0.f;
+            }
+            bf16x8 h8, l8;
+            split8(u8, h8, l8);
+            uh[kk] = __builtin_bit_cast(u32x4, h8);
+            ul[kk] = __builtin_bit_cast(u32x4, l8);
+            *reinterpret_cast<u32x4 *>(rec + kRcUh + (t * kD + k0) * 2) = uh[kk];
+            *reinterpret_cast<u32x4 *>(rec + kRcUl + (t * kD + k0) * 2) = ul[kk];
+            split8(q8, h8, l8);
+            qh[kk] = __builtin_bit_cast(u32x4, h8);
+            ql[kk] = __builtin_bit_cast(u32x4, l8);
+            *reinterpret_cast<u32x4 *>(rec + kRcQh + (tp * kD + k0) * 2) = qh[kk];
+            *reinterpret_cast<u32x4 *>(rec + kRcQl + (tp * kD + k0) * 2) = ql[kk];
+            split8(wt8, h8, l8);
+            *reinterpret_cast<u32x4 *>(rec + kRcWh + (t * kD + k0) * 2) = __builtin_bit_cast(u32x4, h8);
+            *reinterpret_cast<u32x4 *>(rec + kRcWl + (t * kD + k0) * 2) = __builtin_bit_cast(u32x4, l8);
+            split8(wh8, h8, l8);
+            *reinterpret_cast<u32x4 *>(&Whs[t][k0]) = __builtin_bit_cast(u32x4, h8);
+            *reinterpret_cast<u32x4 *>(&Wls[t][k0]) = __builtin_bit_cast(u32x4, l8);
+        }
+    }
+    __syncthreads();
+
+    // Gram row block IG = w and score row block IP = 3 - w against What (three bf16
+    // products per term pair: hi.hi + hi.lo + lo.hi)
+    const int IG = w, IP = 3 - w;
+    f32x4 accG[4], accP[4];
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+        accG[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+        accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const bf16x8 bh8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Whs[16 * J + r][32 * kk + 8 * q]));
+            const bf16x8 bl8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Wls[16 * J + r][32 * kk + 8 * q]));
+            if (J <= IG) {
+                accG[J] = mfma(as_bf16x8(uh[kk]), bh8, accG[J]);
+                accG[J] = mfma(as_bf16x8(uh[kk]), bl8, accG[J]);
+                accG[J] = mfma(as_bf16x8(ul[kk]), bh8, accG[J]);
+            }
+            if (J <= IP) {
+                accP[J] = mfma(as_bf16x8(qh[kk]), bh8, accP[J]);
+                accP[J] = mfma(as_bf16x8(qh[kk]), bl8, accP[J]);
+                accP[J] = mfma(as_bf16x8(ql[kk]), bh8, accP[J]);
+            }
+        }
+    __syncthreads();  // g is dead: As and Ts take its place
+
+#pragma unroll
+    for (int J = 0; J < 4; ++J) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * J + r;
+            if (J <= IG) {
+                const int tg = 16 * IG + 4 * q + i;
+                As[tg][s] = (s < tg && tg < n) ? accG[J][i] : 0.f;
+            }
+            const int tq = 16 * IP + 4 * q + i;
+            const float pv = (J <= IP && s <= tq && tq < n) ? accP[J][i] : 0.f;
+            const __bf16 hi = (__bf16)pv;
+            const __bf16 lo = (__bf16)(pv - (float)hi);
+            Ph[tq][s] = __builtin_bit_cast(uint16_t, hi);
+            Pl[tq][s] = __builtin_bit_cast(uint16_t, lo);
+        }
+    }
+    __syncthreads();
+    store_p(rec + kRcPh, rec + kRcPl, Ph, Pl, tid);
+    __syncthreads();
+    ut_transform(As, Ts, Xs, w, l);
+    store_ut(rec + kRcT, Ts, tid);
 }
 
 // ---------------------------------------------------------------------------
@@ -1035,19 +1245,356 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
     }
 }
 
+
+// ---------------------------------------------------------------------------
+// state kernel, general gates (wave-specialised, as above)
+// ---------------------------------------------------------------------------
+// The key-side operands come from the general-gate record with their decay and
+// beta applied (U, Q, W as two bf16 terms each), so the products take three bf16
+// terms (hi.hi + hi.lo + lo.hi):
+//     Y = U S,  R = vh - Y,  D = Tm R,  O = Q S + P D,  S <- Diag(e^{g_C}) S + W^T D.
+// vh = sqrt(beta) (.) v for a beta vector over the value channels (VSCALE).  The
+// operand tiles do not fit twice in LDS, so everything is single buffered: after
+// the first barrier of chunk c the side waves copy U, Q, Tm, P, V (and beta) of
+// chunk c + 1 (all consumed before it); after the second, W and e^{g_C}, which the
+// chain waves read between the two barriers.
+struct ChanLds {
+    uint16_t Uh[kC][kD], Ul[kC][kD];  // rows; piece p of row t stored at piece p ^ (t & 15)
+    uint16_t Qh[kC][kD], Ql[kC][kD];
+    uint16_t Wh[kC][kD], Wl[kC][kD];
+    uint16_t T[kC][kC];               // rows; piece p of row t stored at p ^ ((t >> 1) & 7)
+    uint16_t Ph[kC][kC], Pl[kC][kC];
+    uint16_t V[kC][kCW];
+    float Bv[kC][kCW];                // beta over the value channels (fp32 or bf16 bits)
+    float GC[kD];                     // e^{g_C} per key channel
+    u32x4 Sx[2][8][64];
+    u32x4 Dx[2][4][64];
+};
+
+template <bool VSCALE, bool GBF16>
+__global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int NT, int nbh) {
+    __shared__ ChanLds sm;
+    const int x = blockIdx.x;
+    const int xcd = x & 7, rr = x >> 3;
+    const int vb = rr % (kD / kCW), bh = rr / (kD / kCW) * 8 + xcd;
+    if (bh >= nbh) return;
+    const int b = bh / p.H, h = bh % p.H, j0 = vb * kCW;
+    const int wv = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int w = wv & 1;
+    const int l = threadIdx.x & 63, r = l & 15, q = l >> 4;
+    const int cw = j0 + 16 * w;
+    const bool chain = wv < 2;
+    const unsigned rstr = (unsigned)p.H * kD;
+    const void *bvsrc = p.beta_mode == 2 ? p.beta_v : p.beta_k;  // value-side beta (VSCALE)
+
+    // per-lane parts of the copies (see the scalar kernel): key-width record rows
+    // (4 rows per copy), chunk-width rows (8 per copy), the V tile (16 rows of 32)
+    unsigned offR[4], offT[2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int t = 4 * j + (l >> 4);
+        offR[j] = (unsigned)((l >> 4) * kD + 8 * ((l & 15) ^ (t & 15)));
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const int t = 8 * j + (l >> 3);
+        offT[j] = (unsigned)((l >> 3) * kC + 8 * ((l & 7) ^ ((t >> 1) & 7)));
+    }
+    auto rec = [&](int c) -> const char * { return static_cast<const char *>(p.ws) + ((long)bh * NT + c) * kRcBytes; };
+    auto wide = [&](const char *src, uint16_t(*dst)[kD]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 16; ++u) dma16(src + 2 * (512 * u + offR[u & 3]), &dst[4 * u][0]);
+    };
+    auto narrow = [&](const char *src, uint16_t(*dst)[kC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) dma16(src + 2 * (512 * u + offT[u & 1]), &dst[8 * u][0]);
+    };
+    // W and e^{g_C} of chunk c (read by the chain waves between the two barriers)
+    auto issue_w = [&](int c) __attribute__((always_inline)) {
+        const char *rc = rec(c);
+        if (w == 0) {
+            wide(rc + kRcWh, sm.Wh);
+        } else {
+            wide(rc + kRcWl, sm.Wl);
+            if (l < 32) dma16(rc + kRcGC + 16 * l, &sm.GC[0]);
+        }
+    };
+    // everything else of chunk c (read before the first barrier)
+    auto issue_rest = [&](int c) __attribute__((always_inline)) {
+        const char *rc = rec(c);
+        const int t0 = c * kC, n = min(kC, p.T - t0);
+        auto row = [&](int t) -> long { return ((long)b * p.T + t0 + min(t, n - 1)) * p.H + h; };
+        if (w == 0) {
+            wide(rc + kRcUh, sm.Uh);
+            wide(rc + kRcQh, sm.Qh);
+            narrow(rc + kRcT, sm.T);
+            const uint16_t *V = static_cast<const uint16_t *>(p.v);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int t = 16 * u + (l >> 2);
+                dma16(V + row(t) * kD + j0 + 8 * (l & 3), &sm.V[16 * u][0]);
+            }
+        } else {
+            wide(rc + kRcUl, sm.Ul);
+            wide(rc + kRcQl, sm.Ql);
+            narrow(rc + kRcPh, sm.Ph);
+            narrow(rc + kRcPl, sm.Pl);
+            if (VSCALE) {
+                if (GBF16) {  // 64 rows of 32 bf16
+                    const uint16_t *Bsrc = static_cast<const uint16_t *>(bvsrc);
+                    uint16_t *Bdst = reinterpret_cast<uint16_t *>(&sm.Bv[0][0]);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int t = 16 * u + (l >> 2);
+                        dma16(Bsrc + row(t) * kD + j0 + 8 * (l & 3), Bdst + 16 * u * kCW);
+                    }
+                } else {      // 64 rows of 32 fp32
+                    const float *Bsrc = static_cast<const float *>(bvsrc);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const int t = 8 * u + (l >> 3);
+                        dma16(Bsrc + row(t) * kD + j0 + 4 * (l & 7), &sm.Bv[8 * u][0]);
+                    }
+                }
+            }
+        }
+    };
+    auto vbeta = [&](int t, int col) -> float {
+        if (GBF16) return bf16_to_f32(reinterpret_cast<const uint16_t *>(&sm.Bv[0][0])[t * kCW + col]);
+        return sm.Bv[t][col];
+    };
+
+    f32x4 S[8];
+    auto publish_state = [&]() __attribute__((always_inline)) {
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+            u32x4 hi, lo;
+            split_frag(S[2 * kk], S[2 * kk + 1], hi, lo);
+            sm.Sx[w][2 * kk][l] = hi;
+            sm.Sx[w][2 * kk + 1][l] = lo;
+        }
+    };
+    if (chain) {
+        if (p.S0) {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+        } else {
+#pragma unroll
+            for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        publish_state();
+    } else {
+        issue_w(0);
+        issue_rest(0);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    }
+    __syncthreads();
+
+    for (int c = 0; c < NT; ++c) {
+        const int t0 = c * kC, n = min(kC, p.T - t0);
+        if (chain) {
+            // Y = U S
+            f32x4 Y[4];
+            {
+                u32x4 sh[4], sl[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    sh[kk] = sm.Sx[w][2 * kk][l];
+                    sl[kk] = sm.Sx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    u32x4 ah[4], al[4];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        ah[tt] = frag_wide(sm.Uh, 16 * tt + r, kk, q);
+                        al[tt] = frag_wide(sm.Ul, 16 * tt + r, kk, q);
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        Y[tt] = mfma(as_bf16x8(ah[tt]), as_bf16x8(sh[kk]), Y[tt]);
+                        Y[tt] = mfma(as_bf16x8(ah[tt]), as_bf16x8(sl[kk]), Y[tt]);
+                        Y[tt] = mfma(as_bf16x8(al[tt]), as_bf16x8(sh[kk]), Y[tt]);
+                    }
+                }
+            }
+            // R = vh - Y (rows past the chunk end zeroed)
+            u32x4 rh[2], rl[2];
+            {
+                f32x4 R[4];
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) {
+                    f32x4 vf;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int tk = 16 * tt + 4 * q + i;
+                        vf[i] = bf16_to_f32(sm.V[tk][16 * w + r]);
+                        if (VSCALE) vf[i] *= sqrtf(vbeta(tk, 16 * w + r));
+                    }
+                    R[tt] = vf - Y[tt];
+                }
+                if (n < kC) {
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            if (16 * tt + 4 * q + i >= n) R[tt][i] = 0.f;
+                }
+                split_frag(R[0], R[1], rh[0], rl[0]);
+                split_frag(R[2], R[3], rh[1], rl[1]);
+            }
+            // D = Tm R
+            f32x4 D[4];
+            {
+                u32x4 ta[6];
+#pragma unroll
+                for (int tt = 0, f = 0; tt < 4; ++tt) {
+                    const int t = 16 * tt + r, sw = (t >> 1) & 7;
+#pragma unroll
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                        ta[f] = cat(ld8(&sm.T[t][8 * (p1 ^ sw) + hf]), ld8(&sm.T[t][8 * (p2 ^ sw) + hf]));
+                    }
+                }
+#pragma unroll
+                for (int tt = 0, f = 0; tt < 4; ++tt) {
+                    D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rh[kk]), D[tt]);
+                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rl[kk]), D[tt]);
+                    }
+                }
+            }
+            // publish D; it is also the state update's right operand (its weights are in W)
+            u32x4 dh[2], dl[2];
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+                split_frag(D[2 * kk], D[2 * kk + 1], dh[kk], dl[kk]);
+                sm.Dx[w][2 * kk][l] = dh[kk];
+                sm.Dx[w][2 * kk + 1][l] = dl[kk];
+            }
+            lds_barrier();  // B1: D published; U, Q, Tm, P, V of this chunk consumed; W landed
+
+            // S <- Diag(e^{g_C}) S + W^T D; A fragments of W^T by the transposing read
+            {
+                const int a = r & 3, m = r >> 2;
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt) S[kt] *= *reinterpret_cast<const f32x4 *>(&sm.GC[16 * kt + 4 * q]);
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                    for (int kk = 0; kk < 2; ++kk) {
+                        const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
+                        const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
+                        const u32x4 wh = cat(ld_tr(&sm.Wh[t1][8 * (pc ^ (t1 & 15)) + hf]),
+                                             ld_tr(&sm.Wh[t2][8 * (pc ^ (t2 & 15)) + hf]));
+                        const u32x4 wl = cat(ld_tr(&sm.Wl[t1][8 * (pc ^ (t1 & 15)) + hf]),
+                                             ld_tr(&sm.Wl[t2][8 * (pc ^ (t2 & 15)) + hf]));
+                        S[kt] = mfma(as_bf16x8(wh), as_bf16x8(dh[kk]), S[kt]);
+                        S[kt] = mfma(as_bf16x8(wh), as_bf16x8(dl[kk]), S[kt]);
+                        S[kt] = mfma(as_bf16x8(wl), as_bf16x8(dh[kk]), S[kt]);
+                    }
+            }
+            publish_state();
+        } else {
+            if (c > 0) issue_w(c);
+            // O0 = Q S
+            f32x4 O[4];
+            {
+                u32x4 sh[4], sl[4];
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    sh[kk] = sm.Sx[w][2 * kk][l];
+                    sl[kk] = sm.Sx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) {
+                    u32x4 ah[4], al[4];
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        ah[tt] = frag_wide(sm.Qh, 16 * tt + r, kk, q);
+                        al[tt] = frag_wide(sm.Ql, 16 * tt + r, kk, q);
+                    }
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) {
+                        O[tt] = mfma(as_bf16x8(ah[tt]), as_bf16x8(sh[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(ah[tt]), as_bf16x8(sl[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(al[tt]), as_bf16x8(sh[kk]), O[tt]);
+                    }
+                }
+            }
+            u32x4 ph[6], pl[6];
+#pragma unroll
+            for (int tt = 0, f = 0; tt < 4; ++tt) {
+                const int t = 16 * tt + r, sw = (t >> 1) & 7;
+#pragma unroll
+                for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
+                    ph[f] = cat(ld8(&sm.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Ph[t][8 * (p2 ^ sw) + hf]));
+                    pl[f] = cat(ld8(&sm.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Pl[t][8 * (p2 ^ sw) + hf]));
+                }
+            }
+            lds_barrier();  // B1 (also: this wave's copies of W have landed)
+            if (c + 1 < NT) issue_rest(c + 1);
+            {
+                u32x4 dh[2], dl[2];
+#pragma unroll
+                for (int kk = 0; kk < 2; ++kk) {
+                    dh[kk] = sm.Dx[w][2 * kk][l];
+                    dl[kk] = sm.Dx[w][2 * kk + 1][l];
+                }
+#pragma unroll
+                for (int tt = 0, f = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
+                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dh[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dl[kk]), O[tt]);
+                        O[tt] = mfma(as_bf16x8(pl[f]), as_bf16x8(dh[kk]), O[tt]);
+                    }
+                const long tstr = (long)p.H * kD;
+                uint16_t *dst = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i)
+                        if (16 * tt + 4 * q + i < n)
+                            __builtin_nontemporal_store(f32_to_bf16(O[tt][i]), dst + (16 * tt + i) * tstr);
+            }
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's operands have landed
+        }
+        __syncthreads();  // B2
+    }
+
+    if (chain && p.ST) {
+#pragma unroll
+        for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+    }
+}
+
 // State kernel: 1 = the wave-specialised kernel (default), 16 / 32 = the four-wave
 // kernel with that many value columns per workgroup (selected by flags, for testing).
 int state_variant(const ChunkParams &p) { return p.state_cols == 16 || p.state_cols == 32 ? p.state_cols : 1; }
 
 }  // namespace
 
-bool chunk_mfma_supported(const ChunkParams &p) {
-    return p.io_bf16 && p.dk == kD && p.dv == kD && p.C == kC && !p.alpha_ch && p.beta_mode == 0;
-}
+bool chunk_mfma_supported(const ChunkParams &p) { return p.io_bf16 && p.dk == kD && p.dv == kD && p.C == kC; }
+
+// scalar forget gate and scalar beta: the scalar record and kernels; anything else
+// takes the general-gate record and kernels
+static bool general_gates(const ChunkParams &p) { return p.alpha_ch || p.beta_mode != 0; }
 
 size_t chunk_mfma_workspace(const ChunkParams &p) {
     const long NT = (p.T + kC - 1) / kC;
-    return (size_t)p.B * p.H * NT * kRecBytes;
+    return (size_t)p.B * p.H * NT * (general_gates(p) ? kRcBytes : kRecBytes);
 }
 
 hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
@@ -1057,6 +1604,32 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     ChunkParams arg = p;
     int nt = NT;
     int nb = (int)nbh;
+    const long groups = (nbh + 7) / 8;
+    if (general_gates(p)) {
+        const bool g16 = p.gate_bf16 != 0, ach = p.alpha_ch != 0, bvec = p.beta_mode != 0;
+        // prep: <GBF16, ACH, BVEC>
+        const void *preps[8] = {
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, false>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, true>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, false>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, true>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, false>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, true>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, false>),
+            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, true>)};
+        void *pargs[] = {&arg, &nt};
+        const hipError_t e = hipLaunchKernel(preps[(g16 ? 4 : 0) + (ach ? 2 : 0) + (bvec ? 1 : 0)],
+                                             dim3((unsigned)(nbh * NT)), dim3(kThreads), pargs, 0, st);
+        if (e != hipSuccess) return e;
+        // state: <VSCALE, GBF16>
+        const void *states[4] = {reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, false>),
+                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, true>),
+                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, false>),
+                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, true>)};
+        void *sargs[] = {&arg, &nt, &nb};
+        return hipLaunchKernel(states[(bvec ? 2 : 0) + (g16 ? 1 : 0)], dim3((unsigned)(groups * 8 * (kD / kCW))),
+                               dim3(256), sargs, 0, st);
+    }
     {
         void *args[] = {&arg, &nt};
         const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
@@ -1066,7 +1639,6 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     void *args[] = {&arg, &nt, &nb};
-    const long groups = (nbh + 7) / 8;
     const bool sep = p.kw != p.k;
     const int bv = state_variant(p);
     if (bv == 1) {

@@ -136,7 +136,21 @@ def test_empty_batch_is_noop(g):
 
 
 def test_path_selection(g):
+    assert g.gdr_chunk_fwd_path(_desc(g)) == g.PATH_MFMA
+    # channel decay and beta vectors take the matrix-core path too (general-gate record)
+    assert g.gdr_chunk_fwd_path(_desc(g, alpha_mode=g.GDR_ALPHA_CHANNEL, beta_mode=g.GDR_BETA_KV)) == g.PATH_MFMA
+    assert g.gdr_chunk_fwd_path(_desc(g, beta_mode=g.GDR_BETA_SHARED)) == g.PATH_MFMA
+    assert g.gdr_chunk_fwd_path(_desc(g, chunk=32)) == g.PATH_VALU
     assert g.gdr_chunk_fwd_path(_desc(g, io_dtype=g.GDR_F32)) == g.PATH_VALU
+
+
+def test_workspace_sizes(g):
+    """One record per (batch, head, chunk): 25728 bytes for scalar gates, 123392 for the
+    general-gate record (Tm, P, and U, Q, W as two bf16 terms each, e^{g_C})."""
+    nrec = 2 * 3 * 2  # B=2, H=3, T=100 -> 2 chunks of 64
+    assert g.gdr_chunk_fwd_workspace_size(_desc(g)) == nrec * 25728
+    assert g.gdr_chunk_fwd_workspace_size(_desc(g, alpha_mode=g.GDR_ALPHA_CHANNEL)) == nrec * 123392
+    assert g.gdr_chunk_fwd_workspace_size(_desc(g, beta_mode=g.GDR_BETA_SHARED)) == nrec * 123392
     assert g.gdr_chunk_fwd_path(_desc(g, dk=64, dv=64)) == g.PATH_VALU
     assert g.gdr_chunk_fwd_path(_desc(g, flags=g.GDR_FLAG_GENERIC_PATH)) == g.PATH_VALU
 

@@ -125,3 +125,25 @@ def test_state_kernel_variants(name, w, variant):
     assert r["path"] == g.PATH_MFMA
     assert r["finite"]
     assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
+
+
+GENERAL_CASES = [
+    # channel forget gate and / or beta vectors on the matrix-core path
+    ("kda_kv_beta_bf16_gates", gi.KDA_FG2PLUS_PREFILL.scaled(B=2, T=200, H=3, gate=gi.BF16, seed=67)),
+    ("kda_write_key_S0", gi.KDA_FG2PLUS_PREFILL.scaled(B=1, T=150, H=4, write_key=True, s0_std=0.02, seed=68)),
+    ("fg2_shared_beta_bf16_gates", gi.KDA_FG2PLUS_PREFILL.scaled(B=1, T=90, H=3, beta_mode=gi.BETA_SHARED,
+                                                                  gate=gi.BF16, seed=69)),
+    ("scalar_alpha_kv_beta", gi.KDA_FG2PLUS_PREFILL.scaled(B=2, T=128, H=2, alpha_mode=gi.GATE_SCALAR, seed=70)),
+    ("kda_scalar_beta_T_lt_C", gi.KDA_FG2PLUS_PREFILL.scaled(B=3, T=37, H=2, beta_mode=gi.BETA_SCALAR, seed=71)),
+    ("kda_64heads", gi.KDA_FG2PLUS_PREFILL.scaled(B=4, T=70, H=16, seed=72)),
+]
+
+
+@pytest.mark.parametrize("name,w", GENERAL_CASES, ids=[c[0] for c in GENERAL_CASES])
+def test_general_gate_path(name, w):
+    """The general-gate record and kernels (channel decay, beta vectors) against the oracle."""
+    torch, g = gpu()
+    r = run_prefill(w, gi.make_prefill(w))
+    assert r["path"] == g.PATH_MFMA
+    assert r["finite"]
+    assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
