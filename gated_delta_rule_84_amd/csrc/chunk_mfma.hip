@@ -1,33 +1,40 @@
 // chunk_mfma.hip -- chunkwise WY / UT-transform prefill on gfx950 bf16 matrix cores.
 //
-// Serves bf16 q / k / k_w / v, dk == dv == 128, chunk 64, scalar forget gate and
-// scalar beta (Gated DeltaNet; OSDN when a write key k_w is given).  Per chunk
-// of n <= 64 tokens with g_t the cumulative log-decay inside the chunk
-// (u = k, w = beta k_w, vh = v):
-//     A  = strictly-lower( beta_s e^{g_t - g_s} k_t . k_w,s )     block Gram matrix
+// Serves bf16 q / k / k_w / v, dk == dv == 128, chunk 64.  Per chunk of n <= 64
+// tokens with g_t the cumulative log-decay inside the chunk, erase key u, write
+// key w and written value vh (scalar beta: u = k, w = beta k_w, vh = v):
+//     A  = strictly-lower( u_t . (e^{g_t - g_s} (.) w_s) )      block Gram matrix
 //     Tm = (I + A)^{-1}                                          UT transform
-//     P  = lower-incl-diag( beta_s e^{g_t - g_s} q_t . k_w,s )    intra-chunk scores
-//     R  = V - Diag(e^g) K S                                     residual before the chunk
+//     P  = lower-incl-diag( q_t . (e^{g_t - g_s} (.) w_s) )      intra-chunk scores
+//     R  = Vh - (e^{g_t} (.) U) S                                residual before the chunk
 //     D  = Tm R                                                  per-token residuals
-//     O  = Diag(e^g) Q S + P D
-//     S <- e^{g_C} S + sum_s beta_s e^{g_C - g_s} k_w,s D_s^T
-// (the WY factors of the pages' chunk-parallel form are Tm Diag(e^g) K and Tm V;
-// the write key replaces the key in the Gram matrix and the scores exactly as
-// the OSDN page, section 2.1 states; FG2-GDN page, section 3).
+//     O  = (e^{g_t} (.) Q) S + P D
+//     S <- Diag(e^{g_C}) S + sum_s (e^{g_C - g_s} (.) w_s) D_s^T
+// (the WY factors of the pages' chunk-parallel form are Tm (e^g (.) U) and Tm Vh;
+// the write key replaces the key in the Gram matrix and the scores exactly as the
+// OSDN page, section 2.1 states; FG2-GDN page, section 3).  A scalar decay is a
+// per-row / per-column factor applied in fp32 after the product; a decay per key
+// channel is folded into the key-side operands before it.
 //
-// Two kernels:
-//  * prep  -- one 256-thread block per chunk, fully parallel: the two 64 x 64
-//             products on MFMA, the exact-difference decay weights, the UT
-//             transform by blocked forward substitution in fp32, and a
-//             per-chunk record in the workspace: Tm (bf16), P split into two
-//             bf16 terms, e^{g_t}, beta_s e^{g_C - g_s}, e^{g_C}.
-//  * state -- one 256-thread block per (batch*head, block of BV value columns),
-//             walking the chunks in order with the state held transposed
-//             (Z = S^T, BV x 128, fp32) in the accumulators of the four waves.
-//             Every product that touches the state or a residual uses a
-//             two-term bf16 split of the fp32 operand (hi + lo), so the state
-//             path keeps ~16 mantissa bits; raw bf16 inputs are exact MFMA
-//             operands and all decay / beta factors are applied in fp32.
+// Kernels, two per call:
+//  * prep (scalar alpha and beta) -- one 256-thread block per chunk, fully
+//        parallel: the Gram and score products on MFMA from the raw bf16 keys,
+//        exact-difference decay weights, the UT transform (diagonal blocks by
+//        forward substitution, off-diagonal blocks on fp32 MFMA) and a per-chunk
+//        record: Tm (bf16), P as two bf16 terms, e^{g_t}, beta_s e^{g_C - g_s},
+//        e^{g_C}, g_t, beta_t.
+//  * prep (general gates) -- the same for a decay per key channel and / or beta
+//        vectors: it forms U = u (.) e^{g}, Q = q (.) e^{g}, W = w (.) e^{g_C - g}
+//        as two bf16 terms each (the record carries them), takes the Gram and
+//        score products on the factored decay, and the same UT transform.
+//  * state -- one workgroup per (batch * head, 32 value columns), walking the
+//        chunks in order: two chain waves carry Y, R, D and the state update for
+//        16 value columns each, two side waves copy operands into LDS and form the
+//        output (wave-specialised kernels, scalar and general-gate variants; a
+//        four-wave kernel that splits every product over the waves is kept as an
+//        alternative for testing).  Every product that touches the state or a
+//        residual uses a two-term bf16 split of the fp32 operand (hi + lo), so the
+//        state path keeps ~16 mantissa bits.
 //
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, r = l % 16, q = l / 16):
 //   A (16 x 32): lane holds A[r][8q .. 8q+7];  B (32 x 16): B[8q .. 8q+7][r];

@@ -92,11 +92,12 @@ typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_
  *   chunk:  prefill chunk length, 16, 32 or 64              (else GDR_EUNSUPPORTED)
  *   io_dtype:   element type of q, k, k_w, v and o
  *   gate_dtype: element type of alpha, beta_k, beta_v
- * The scalar-gate bf16 kernel on matrix cores serves io_dtype == GDR_BF16,
- * dk == dv == 128, chunk == 64; every other accepted shape runs the fp32
- * vector-ALU kernel.  With alpha_mode == CHANNEL the per-channel cumulative
- * log-decay inside one chunk must stay above about -80 (fp32 exponent range
- * of the factored decay); use a shorter chunk for faster-decaying inputs. */
+ * The bf16 matrix-core kernels serve io_dtype == GDR_BF16, dk == dv == 128,
+ * chunk == 64, for every gate and beta layout (a faster pair for scalar alpha
+ * and scalar beta); every other accepted shape runs the fp32 vector-ALU kernel.
+ * With alpha_mode == CHANNEL the per-channel cumulative log-decay inside one
+ * chunk must stay above about -80 (fp32 exponent range of the factored decay);
+ * use a shorter chunk (vector-ALU kernel) for faster-decaying inputs. */
 typedef struct gdr_desc {
     int32_t B, T, H, dk, dv;
     int32_t chunk;
