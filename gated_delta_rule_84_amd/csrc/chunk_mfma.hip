@@ -885,6 +885,7 @@ constexpr int kGFac = 64, kGGC = 128, kGLog = 160, kGBeta = 224;
 static_assert((kRecBytes - kRecGam) == 288 * 4, "gate block of the record");
 static_assert(kRecFac - kRecGam == 4 * kGFac && kRecGC - kRecGam == 4 * kGGC, "gate block layout");
 static_assert(kRecGlog - kRecGam == 4 * kGLog && kRecBeta - kRecGam == 4 * kGBeta, "gate block layout");
+static_assert(4 * 64 * 16 >= kC * 24 * 2, "a chain wave's D slot holds a 64 x 16 bf16 output tile (pitch 24)");
 
 struct WsLds {
     WsBuf buf[2];          // double buffered: copied one chunk ahead at the chunk start
@@ -1219,24 +1220,25 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                         O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dl[kk]), O[tt]);
                         O[tt] = mfma(as_bf16x8(pl[f]), as_bf16x8(dh[kk]), O[tt]);
                     }
-                const long tstr = (long)p.H * kD;  // tokens are H * 128 elements apart
-                uint16_t *dst = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
-                if (n == kC) {
+                // O goes out as rows: staged (bf16) in this wave's D slot, whose fragments are
+                // already in registers, then 16 bytes per lane and store
+                uint16_t(*Ost)[24] = reinterpret_cast<uint16_t(*)[24]>(&sm.Dx[w][0][0]);
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
+                for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                        for (int i = 0; i < 4; i += 2) {
-                            const uint32_t o2 = pk_bf16(O[tt][i], O[tt][i + 1]);
-                            // the output is never read back here: non-temporal stores
-                            __builtin_nontemporal_store((uint16_t)(o2 & 0xffffu), dst + (16 * tt + i) * tstr);
-                            __builtin_nontemporal_store((uint16_t)(o2 >> 16), dst + (16 * tt + i + 1) * tstr);
-                        }
-                } else {
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t o2 = pk_bf16(O[tt][i], O[tt][i + 1]);
+                        Ost[16 * tt + 4 * q + i][r] = (uint16_t)(o2 & 0xffffu);
+                        Ost[16 * tt + 4 * q + i + 1][r] = (uint16_t)(o2 >> 16);
+                    }
+                uint16_t *Og = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0) * p.H + h) * kD + cw;
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            if (16 * tt + 4 * q + i < n) dst[(16 * tt + i) * tstr] = f32_to_bf16(O[tt][i]);
+                for (int m = 0; m < 2; ++m) {
+                    const int row = (l >> 1) + 32 * m, half = l & 1;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(&Ost[row][8 * half]);
+                    // the output is never read back here: non-temporal stores
+                    if (row < n)
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half));
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
@@ -1565,14 +1567,24 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                         O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dl[kk]), O[tt]);
                         O[tt] = mfma(as_bf16x8(pl[f]), as_bf16x8(dh[kk]), O[tt]);
                     }
-                const long tstr = (long)p.H * kD;
-                uint16_t *dst = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0 + 4 * q) * p.H + h) * kD + cw + r;
+                // O out as rows, staged in this wave's D slot (as in the scalar kernel)
+                uint16_t(*Ost)[24] = reinterpret_cast<uint16_t(*)[24]>(&sm.Dx[w][0][0]);
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        if (16 * tt + 4 * q + i < n)
-                            __builtin_nontemporal_store(f32_to_bf16(O[tt][i]), dst + (16 * tt + i) * tstr);
+                    for (int i = 0; i < 4; i += 2) {
+                        const uint32_t o2 = pk_bf16(O[tt][i], O[tt][i + 1]);
+                        Ost[16 * tt + 4 * q + i][r] = (uint16_t)(o2 & 0xffffu);
+                        Ost[16 * tt + 4 * q + i + 1][r] = (uint16_t)(o2 >> 16);
+                    }
+                uint16_t *Og = static_cast<uint16_t *>(p.o) + (((long)b * p.T + t0) * p.H + h) * kD + cw;
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int row = (l >> 1) + 32 * m, half = l & 1;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(&Ost[row][8 * half]);
+                    if (row < n)
+                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half));
+                }
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's operands have landed
         }
