@@ -118,7 +118,7 @@ __device__ __forceinline__ void lds_barrier() {
 // Tm = (I + A)^{-1} for the strictly lower 64 x 64 A in As, into the lower part of
 // Ts (fp32; the unit diagonal and the upper part are not written).  Ends with a
 // barrier; starts reading As, so the caller has published it with a barrier.
-__device__ __forceinline__ void ut_transform(float (*As)[kC + 4], float (*Ts)[kC + 8], float (*Xs)[16][20],
+__device__ __forceinline__ void ut_transform(float (*As)[kC + 4], float (*Ts)[kC + 8], float (*Xs)[16][16],
                                              const int w, const int l) {
     const int r = l & 15, q = l >> 4;
     // diagonal 16 x 16 blocks of (I + A)^{-1}: wave w, lane c < 16 owns column c;
@@ -197,8 +197,8 @@ __device__ __forceinline__ void ut_transform(float (*As)[kC + 4], float (*Ts)[kC
         __syncthreads();
         {   // T_IJ = -sum_{M=2}^{I} T_IM X_MJ for I = 2 + (w >> 1), J = w & 1
             const int I = 2 + (w >> 1), J = w & 1;
-            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 20, z);
-            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 20, t);
+            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 16, z);
+            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 16, t);
             storeT(I, J, t);
         }
         __syncthreads();
@@ -241,11 +241,11 @@ __device__ __forceinline__ void store_p(char *dh, char *dl, const uint16_t (*Ph)
 // ---------------------------------------------------------------------------
 // GBF16: the gates are bf16 (compile time, so the gate loads carry no branch)
 template <bool GBF16>
-__global__ void __launch_bounds__(kThreads) gdr_prep_kernel(ChunkParams p, int NT) {
+__global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, int NT) {
     __shared__ float gl[kC], bl[kC];
     __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part
     __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform; first holds the two P terms
-    __shared__ __align__(16) float Xs[4][16][20];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
+    __shared__ __align__(16) float Xs[4][16][16];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
     uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
     uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
 
@@ -386,7 +386,7 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
     // Gram and UT arrays take its place
     __shared__ __align__(16) float pool[kC * (kC + 4) + kC * (kC + 8)];
     __shared__ __align__(16) uint16_t Whs[kC][kD + 8], Wls[kC][kD + 8];  // What, two bf16 terms
-    __shared__ __align__(16) float Xs[4][16][20];
+    __shared__ __align__(16) float Xs[4][16][16];
     float(*gs)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(pool);
     float(*As)[kC + 4] = reinterpret_cast<float(*)[kC + 4]>(pool);
     float(*Ts)[kC + 8] = reinterpret_cast<float(*)[kC + 8]>(pool + kC * (kC + 4));
