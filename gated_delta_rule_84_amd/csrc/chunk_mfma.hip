@@ -102,6 +102,16 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ float ld_gate(const void *p, long i, int bf16) { return ld_elem(p, i, bf16); }
 
+typedef __attribute__((address_space(3))) void *lds_void_t;
+typedef __attribute__((address_space(1))) void *gbl_void_t;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_t;
+
+// 16 bytes per lane, global -> LDS; lane l writes dst + 16 l (dst wave-uniform)
+__device__ __forceinline__ void dma16(const void *src, void *dst) {
+    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)dst, 16, 0, 0);
+}
+
 // Workgroup barrier ordered for LDS only: the fences are restricted to the local
 // address space, so the barrier waits for this wave's LDS traffic but not for its
 // outstanding global loads (or copies into LDS), which stay in flight across it.
@@ -243,7 +253,7 @@ __device__ __forceinline__ void store_p(char *dh, char *dl, const uint16_t (*Ph)
 template <bool GBF16>
 __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, int NT) {
     __shared__ float gl[kC], bl[kC];
-    __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part
+    __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part (first: the write keys)
     __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform; first holds the two P terms
     __shared__ __align__(16) float Xs[4][16][16];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
     uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
@@ -278,12 +288,16 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
             qa[kk] = ld16(Q + rowt(tp) + kk * 32 + 8 * q);
         }
     }
-    // all key tiles are loaded before the first product so every load is in flight at once
-    u32x4 kb[4][4];
+    // the write-key tile is copied once into LDS (the space As and Ts take later; wave w
+    // copies rows 16 w .. 16 w + 15, 16-byte pieces of row t stored at piece ^ (t & 15))
+    // and every wave reads its B fragments from there
+    uint16_t(*KWs)[kD] = reinterpret_cast<uint16_t(*)[kD]>(&As[0][0]);
 #pragma unroll
-    for (int J = 0; J < 4; ++J)
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) kb[J][kk] = ld16(KW + rowt(16 * J + r) + kk * 32 + 8 * q);
+    for (int u = 4 * w; u < 4 * w + 4; ++u) {
+        const int t = 4 * u + (l >> 4), pc = (l & 15) ^ (t & 15);
+        dma16(KW + rowt(t) + 8 * pc, &KWs[4 * u][0]);
+    }
+    __syncthreads();  // drains this block's copies and loads
     f32x4 accG[4], accP[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
@@ -291,8 +305,9 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
         accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            if (J <= IG) accG[J] = mfma(as_bf16x8(ka[kk]), as_bf16x8(kb[J][kk]), accG[J]);
-            if (J <= IP) accP[J] = mfma(as_bf16x8(qa[kk]), as_bf16x8(kb[J][kk]), accP[J]);
+            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&KWs[16 * J + r][8 * ((4 * kk + q) ^ r)]));
+            if (J <= IG) accG[J] = mfma(as_bf16x8(ka[kk]), kb, accG[J]);
+            if (J <= IP) accP[J] = mfma(as_bf16x8(qa[kk]), kb, accP[J]);
         }
     }
     // cumulative log decay and beta (wave 0)
@@ -895,16 +910,6 @@ struct WsLds {
     u32x4 Sx[2][8][64];    // per chain wave: state fragments (hi, lo for 4 k steps) of the chunk start
     u32x4 Dx[2][4][64];    // per chain wave: D fragments (hi, lo for 2 k steps)
 };
-
-typedef __attribute__((address_space(3))) void *lds_void_t;
-typedef __attribute__((address_space(1))) void *gbl_void_t;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_t;
-
-// 16 bytes per lane, global -> LDS; lane l writes dst + 16 l (dst wave-uniform)
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)dst, 16, 0, 0);
-}
 
 __device__ __forceinline__ u32x2 ld8(const uint16_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
 
