@@ -1241,9 +1241,9 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                 for (int m = 0; m < 2; ++m) {
                     const int row = (l >> 1) + 32 * m, half = l & 1;
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(&Ost[row][8 * half]);
-                    // the output is never read back here: non-temporal stores
-                    if (row < n)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half));
+                    // plain stores: L2 joins the 32-byte row pieces of the column blocks into whole
+                    // lines before they reach HBM (non-temporal ones went out as partial lines)
+                    if (row < n) *reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half) = v;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's copies have landed
@@ -1587,8 +1587,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                 for (int m = 0; m < 2; ++m) {
                     const int row = (l >> 1) + 32 * m, half = l & 1;
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(&Ost[row][8 * half]);
-                    if (row < n)
-                        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half));
+                    if (row < n) *reinterpret_cast<u32x4 *>(Og + (long)row * p.H * kD + 8 * half) = v;
                 }
             }
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next chunk's operands have landed
