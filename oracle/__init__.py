@@ -53,6 +53,8 @@ def _bind(lib):
     lib.gdr_ref_forward.restype = ctypes.c_int
     lib.gdr_ref_decode_step.argtypes = [ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_int]
     lib.gdr_ref_decode_step.restype = ctypes.c_int
+    lib.gdr_ref_dmem_step.argtypes = [ctypes.c_int] * 4 + [dp] * 7 + [ctypes.c_int]
+    lib.gdr_ref_dmem_step.restype = ctypes.c_int
     lib.gdr_ref_max_threads.argtypes = []
     lib.gdr_ref_max_threads.restype = ctypes.c_int
     return lib
@@ -157,6 +159,21 @@ def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, alpha_mode=
     if rc != 0:
         raise ValueError(f"gdr_ref_decode_step rejected its arguments (status {rc})")
     return o, S
+
+
+def dmem_step(M, q, k, v, lam, beta, nthreads: int = 0):
+    """One delta-mem step in the page's orientation: M [B, H, dv, dk] (predicts M k),
+    lam, beta [B, H]; returns (r [B, H, dv] read before the write, M_new)."""
+    M = np.array(M, dtype=np.float64, order="C", copy=True)
+    q, k, v, lam, beta = map(_c64, (q, k, v, lam, beta))
+    B, H, dk = q.shape
+    dv = v.shape[-1]
+    r = np.empty((B, H, dv))
+    rc = _load().gdr_ref_dmem_step(B, H, dk, dv, _dp(q), _dp(k), _dp(v), _dp(lam), _dp(beta), _dp(M), _dp(r),
+                                   nthreads)
+    if rc != 0:
+        raise ValueError(f"gdr_ref_dmem_step rejected its arguments (status {rc})")
+    return r, M
 
 
 def rel_l2(x, ref) -> float:

@@ -210,6 +210,47 @@ int gdr_ref_decode_step(int B, int H, int dk, int dv, int alpha_mode, int beta_m
     return failed ? REF_EINVAL : REF_OK;
 }
 
+/*
+ * delta-mem step, in the page's own form and orientation [delta-mem page,
+ * section 2.A update rule; section 2.C read]: the memory M (dv x dk, stored
+ * [B, H, dv, dk] row-major) predicts a value from a key as M k.  With forget
+ * gate lambda and write gate beta (one each per (batch, head)):
+ *     r_t = M_{t-1} q_t                                   read, before the write
+ *     M_t = lambda_t M_{t-1} + beta_t (v_t - M_{t-1} k_t) k_t^T
+ * The prediction M_{t-1} k_t uses the state before the forget gate.  M is
+ * updated in place; r is [B, H, dv].
+ */
+int gdr_ref_dmem_step(int B, int H, int dk, int dv, const double *q, const double *k, const double *v,
+                      const double *lam, const double *beta, double *M, double *r, int nthreads)
+{
+    if (B < 0 || H < 0 || dk < 1 || dv < 1) return REF_EINVAL;
+    if (!q || !k || !v || !lam || !beta || !M || !r) return REF_EINVAL;
+    int failed = 0;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        double pred[1024];
+        if (dv > 1024) { failed = 1; continue; }
+        double *Mh = M + (size_t)bh * dv * dk;
+        const double *qh = q + (size_t)bh * dk, *kh = k + (size_t)bh * dk, *vh = v + (size_t)bh * dv;
+        for (int a = 0; a < dv; ++a) {            /* read and prediction from M_{t-1} */
+            double sr = 0.0, sp = 0.0;
+            for (int c = 0; c < dk; ++c) {
+                sr += Mh[(size_t)a * dk + c] * qh[c];
+                sp += Mh[(size_t)a * dk + c] * kh[c];
+            }
+            r[(size_t)bh * dv + a] = sr;
+            pred[a] = sp;
+        }
+        for (int a = 0; a < dv; ++a)              /* M_t = lambda M + beta (v - M k) k^T */
+            for (int c = 0; c < dk; ++c)
+                Mh[(size_t)a * dk + c] = lam[bh] * Mh[(size_t)a * dk + c] + beta[bh] * (vh[a] - pred[a]) * kh[c];
+    }
+    return failed ? REF_EINVAL : REF_OK;
+}
+
 int gdr_ref_max_threads(void)
 {
 #ifdef _OPENMP

@@ -328,3 +328,77 @@ def test_rejects_bad_arguments():
     x = _rand_inputs(rng, 1, 4, 1, 4, 6, beta_mode=1)  # shared beta needs dk == dv
     with pytest.raises(ValueError):
         _run(x)
+
+
+# ---------------------------------------------------------------------------
+# delta-mem step in the page's own form (oracle.dmem_step) [delta-mem page,
+# section 2.A update rule, section 2.C read]
+# ---------------------------------------------------------------------------
+def _unit_rows(n, d, seed):
+    """n orthonormal rows in R^d (QR of a Gaussian), fp64."""
+    q_, _ = np.linalg.qr(np.random.default_rng(seed).normal(size=(d, n)))
+    return q_.T
+
+
+def test_dmem_reads_before_the_write_and_retrieves_exactly():
+    """lambda = beta = 1, orthonormal keys, zero memory: reading k_s after its write returns
+    v_s; reading the key being written at the same step returns 0 (the read sees M_{t-1})."""
+    d, T = 8, 5
+    keys = _unit_rows(T, d, 3)
+    vals = np.random.default_rng(4).normal(size=(T, d))
+    M = np.zeros((1, 1, d, d))
+    one = np.ones((1, 1))
+    for t in range(T):
+        # query the current key: nothing stored along it yet
+        r, M_next = oracle.dmem_step(M, keys[t][None, None], keys[t][None, None], vals[t][None, None], one, one)
+        assert np.allclose(r[0, 0], 0.0, atol=1e-12)
+        M = M_next
+        for s in range(t + 1):  # every earlier write is retrieved exactly
+            r, _ = oracle.dmem_step(M, keys[s][None, None], keys[t][None, None], vals[t][None, None], one, 0 * one)
+            assert np.allclose(r[0, 0], vals[s], atol=1e-12)
+
+
+def test_dmem_zero_write_gate_is_pure_decay():
+    """beta = 0: M_t = lambda_t M_{t-1}, r_t = (prod_{s<t} lambda_s) M_0 q (closed form)."""
+    rng = np.random.default_rng(7)
+    B, H, d = 2, 3, 6
+    M0 = rng.normal(size=(B, H, d, d))
+    M = M0.copy()
+    prod = np.ones((B, H))
+    for t in range(4):
+        q = rng.normal(size=(B, H, d))
+        lam = rng.uniform(0.5, 1.0, size=(B, H))
+        r, M = oracle.dmem_step(M, q, rng.normal(size=(B, H, d)), rng.normal(size=(B, H, d)), lam, np.zeros((B, H)))
+        assert np.allclose(r, np.einsum("bhac,bhc->bha", M0, q) * prod[..., None], atol=1e-12)
+        prod *= lam
+
+
+def test_dmem_one_shot_write():
+    """lambda = 1 and beta = 1 / |k|^2: after the step the memory maps k_t to v_t exactly
+    (the residual v - M k is fully corrected along k)."""
+    rng = np.random.default_rng(9)
+    d = 7
+    M = rng.normal(size=(1, 1, d, d))
+    k = rng.normal(size=(1, 1, d))
+    v = rng.normal(size=(1, 1, d))
+    beta = np.array([[1.0 / float(k[0, 0] @ k[0, 0])]])
+    _, M1 = oracle.dmem_step(M, rng.normal(size=(1, 1, d)), k, v, np.ones((1, 1)), beta)
+    assert np.allclose(M1[0, 0] @ k[0, 0], v[0, 0], atol=1e-12)
+
+
+def test_dmem_equals_gated_step_reparametrised():
+    """Against the independent gated delta-rule oracle (decayed prediction): with
+    alpha = lambda, unit write strength, write key (beta / lambda) k and value lambda v,
+    its state is the transposed delta-mem memory after the step."""
+    rng = np.random.default_rng(11)
+    B, H, dk, dv = 2, 2, 5, 4
+    M = rng.normal(size=(B, H, dv, dk))
+    q, k = rng.normal(size=(B, H, dk)), rng.normal(size=(B, H, dk))
+    v = rng.normal(size=(B, H, dv))
+    lam = rng.uniform(0.3, 1.0, size=(B, H))
+    beta = rng.uniform(0.0, 1.0, size=(B, H))
+    _, M1 = oracle.dmem_step(M, q, k, v, lam, beta)
+    S = np.ascontiguousarray(np.swapaxes(M, -1, -2))
+    _, S1 = oracle.decode_step(S, q, k, lam[..., None] * v, lam, np.ones((B, H)),
+                               k_w=(beta / lam)[..., None] * k)
+    assert np.allclose(np.swapaxes(S1, -1, -2), M1, atol=1e-12)
