@@ -229,8 +229,11 @@ def main():
             dd = {k: gi.to_torch(xd[k], wd.io if k in ("q", "k", "k_w", "v") else (wd.gate if k != "S" else gi.F32))
                   for k in xd}
             S = dd["S"].clone()
+            # the delta-mem workload runs delta-mem's own step (read before the write,
+            # prediction from the undecayed state)
+            fl = (g.GDR_FLAG_READ_BEFORE_WRITE | g.GDR_FLAG_UNDECAYED_PREDICTION) if wd.dk == 8 else 0
             graph = DecodeGraph(S, dd["q"], dd["k"], dd["v"], dd["alpha"], dd["beta_k"], k_w=dd["k_w"],
-                                beta_v=dd["beta_v"])
+                                beta_v=dd["beta_v"], flags=fl)
             graph.replay()
             torch.cuda.synchronize()
             times = []
@@ -245,7 +248,7 @@ def main():
             us_step = ms * 1e3 / wd.steps
             bps = decode_bytes_per_step(wd)
             gbs = bps / (us_step * 1e-6) / 1e9
-            dec[wd.name] = {"us_per_step": us_step, "tokens_per_s": wd.B / (us_step * 1e-6),
+            dec[wd.name] = {"us_per_step": us_step, "flags": fl, "tokens_per_s": wd.B / (us_step * 1e-6),
                             "GBps": gbs, "hbm_frac": gbs / HBM_PEAK_GBS, "steps_per_graph": wd.steps,
                             "bytes_per_step": bps,
                             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",

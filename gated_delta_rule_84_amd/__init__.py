@@ -30,6 +30,8 @@ GDR_FLAG_GENERIC_PATH = 0x1
 GDR_FLAG_STATE_COLS16 = 0x2
 GDR_FLAG_STATE_COLS32 = 0x4
 GDR_FLAG_STATE_WAVECOLS = 0x8
+GDR_FLAG_READ_BEFORE_WRITE = 0x10
+GDR_FLAG_UNDECAYED_PREDICTION = 0x20
 PATH_MFMA, PATH_VALU = 1, 2
 
 
@@ -159,9 +161,10 @@ def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=6
     return o, ST
 
 
-def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, stream=None):
-    """One token for every (b, h); S [B, H, dk, dv] fp32 is updated in place.  Returns o [B, H, dv]."""
-    desc = make_desc(q, v, alpha, beta_k, beta_v, decode=True)
+def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0, stream=None):
+    """One token for every (b, h); S [B, H, dk, dv] fp32 is updated in place.  Returns o [B, H, dv].
+    `flags`: GDR_FLAG_READ_BEFORE_WRITE and / or GDR_FLAG_UNDECAYED_PREDICTION."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, decode=True, flags=flags)
     o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     rc = gdr_decode_step(desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream)
     if rc != GDR_OK:

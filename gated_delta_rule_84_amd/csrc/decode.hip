@@ -8,7 +8,10 @@
 //     o = p_q + delta (w . q)                                = S_new^T q
 //     S_new = Diag(alpha) S + w delta^T                      written back in place
 // This is one step of the gated delta rule [OSDN page, section 1; FG2-GDN page,
-// sections 1 and 2.A] with the read-out taken after the write.
+// sections 1 and 2.A] with the read-out taken after the write.  Two options give
+// the delta-mem step [delta-mem page, section 2.A update rule, section 2.C read]:
+// undecayed prediction (p_u = S^T u, the residual against the state before the
+// gate) and read before write (o = S^T q, the state before the gate and write).
 //
 // The step is bound by HBM: the state is read once and written once (8 bytes
 // per element) and every other operand is O(dk + dv).  Each thread owns float4
@@ -74,8 +77,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_sq_kernel(DecodeParams 
             const float bv = p.beta_mode == 2 ? ld_elem(p.beta_v, vi, p.gate_bf16) : bk;
             vh = sqrtf(bv) * vv;
         }
-        sv[g][0][tg] = a * u;
-        sv[g][1][tg] = a * qq;
+        sv[g][0][tg] = p.undecayed_prediction ? u : a * u;
+        sv[g][1][tg] = p.read_before_write ? qq : a * qq;
         sv[g][2][tg] = w;
         sv[g][3][tg] = a;
         sv[g][4][tg] = vh;
@@ -124,7 +127,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_sq_kernel(DecodeParams 
 #pragma unroll
     for (int c = 0; c < 4; ++c) {
         dl[c] = sv[g][4][cg * 4 + c] - red[c];
-        o[c] = red[4 + c] + dl[c] * red[8];
+        o[c] = p.read_before_write ? red[4 + c] : red[4 + c] + dl[c] * red[8];
     }
     if (rt == 0) {
         const long oi = bh * D + cg * 4;
@@ -181,8 +184,8 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(DecodeParams p) {
             u = sb * kk;
             w = sb * kw;
         }
-        ua[tid] = a * u;
-        qa[tid] = a * qq;
+        ua[tid] = p.undecayed_prediction ? u : a * u;
+        qa[tid] = p.read_before_write ? qq : a * qq;
         ww[tid] = w;
         aa[tid] = a;
         wq = w * qq;
@@ -208,7 +211,7 @@ __global__ void __launch_bounds__(128) decode_generic_kernel(DecodeParams p) {
         pq += s * qa[i];
     }
     const float dl = vh[tid] - pu;
-    st_elem(p.o, bh * dv + tid, pq + dl * wq, p.io_bf16);
+    st_elem(p.o, bh * dv + tid, p.read_before_write ? pq : pq + dl * wq, p.io_bf16);
     for (int i = 0; i < dk; ++i) {
         const long e = (long)i * dv + tid;
         Sh[e] = aa[i] * Sh[e] + ww[i] * dl;

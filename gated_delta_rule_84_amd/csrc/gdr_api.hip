@@ -33,7 +33,8 @@ int check_desc(const gdr_desc *d, bool prefill) {
     if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
     if (d->alpha_mode != GDR_ALPHA_SCALAR && d->alpha_mode != GDR_ALPHA_CHANNEL) return GDR_EINVAL;
     if (d->beta_mode < GDR_BETA_SCALAR || d->beta_mode > GDR_BETA_KV) return GDR_EINVAL;
-    if (d->flags & ~(GDR_FLAG_GENERIC_PATH | GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS))
+    if (d->flags & ~(GDR_FLAG_GENERIC_PATH | GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS |
+                     GDR_FLAG_READ_BEFORE_WRITE | GDR_FLAG_UNDECAYED_PREDICTION))
         return GDR_EINVAL;
     {
         const int sel = d->flags & (GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS);
@@ -43,6 +44,7 @@ int check_desc(const gdr_desc *d, bool prefill) {
     if (d->dk < 8 || d->dk > 128 || (d->dk & 7) || d->dv < 8 || d->dv > 128 || (d->dv & 7))
         return GDR_EUNSUPPORTED;
     if (prefill && d->chunk != 16 && d->chunk != 32 && d->chunk != 64) return GDR_EUNSUPPORTED;
+    if (prefill && (d->flags & (GDR_FLAG_READ_BEFORE_WRITE | GDR_FLAG_UNDECAYED_PREDICTION))) return GDR_EUNSUPPORTED;
     const long long bh = (long long)d->B * d->H;
     if (bh > 0x7fffffffLL) return GDR_EUNSUPPORTED;
     return GDR_OK;
@@ -207,6 +209,8 @@ int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void 
     p.gate_bf16 = d->gate_dtype == GDR_BF16;
     p.alpha_ch = d->alpha_mode == GDR_ALPHA_CHANNEL;
     p.beta_mode = d->beta_mode;
+    p.read_before_write = (d->flags & GDR_FLAG_READ_BEFORE_WRITE) != 0;
+    p.undecayed_prediction = (d->flags & GDR_FLAG_UNDECAYED_PREDICTION) != 0;
     p.q = q; p.k = k; p.kw = k_w ? k_w : k; p.v = v;
     p.alpha = alpha; p.beta_k = beta_k; p.beta_v = beta_v;
     p.S = S; p.o = o;

@@ -26,6 +26,8 @@ struct ChunkParams {
 struct DecodeParams {
     int B, H, dk, dv;
     int io_bf16, gate_bf16, alpha_ch, beta_mode;
+    int read_before_write;     // o = S_{t-1}^T q instead of S_t^T q
+    int undecayed_prediction;  // residual against S_{t-1} instead of Diag(alpha) S_{t-1}
     const void *q, *k, *kw, *v, *alpha, *beta_k, *beta_v;
     float *S;
     void *o;

@@ -16,12 +16,13 @@ from . import GDR_OK, GdrError, gdr_decode_step, make_desc
 class DecodeGraph:
     """Per-step tensors carry a leading step axis: q, k [steps, B, H, dk], ..."""
 
-    def __init__(self, S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None):
+    def __init__(self, S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0):
         self.steps = q.shape[0]
         self.S = S
         self.out = out if out is not None else torch.empty(
             (self.steps,) + q.shape[1:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
-        desc = make_desc(q[0], v[0], alpha[0], beta_k[0], None if beta_v is None else beta_v[0], decode=True)
+        desc = make_desc(q[0], v[0], alpha[0], beta_k[0], None if beta_v is None else beta_v[0], decode=True,
+                         flags=flags)
         self.graph = torch.cuda.CUDAGraph()
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())

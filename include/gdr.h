@@ -85,6 +85,13 @@ typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_
 #define GDR_FLAG_STATE_COLS32 0x4  /* the same with 32 value columns per workgroup (testing aid) */
 #define GDR_FLAG_STATE_WAVECOLS 0x8 /* the wave-specialised state kernel (the default); at most one
                                       of the three STATE flags */
+/* Decode only (gdr_chunk_fwd returns GDR_EUNSUPPORTED for them); together they give the
+ * delta-mem step [delta-mem page, section 2.A update rule, section 2.C read]:
+ *   READ_BEFORE_WRITE:      o = S_{t-1}^T q        (the state before the gate and the write)
+ *   UNDECAYED_PREDICTION:   S_t = Diag(alpha) S_{t-1} + w (vh - S_{t-1}^T u)^T
+ *                           (the residual is taken against the state before the gate) */
+#define GDR_FLAG_READ_BEFORE_WRITE 0x10
+#define GDR_FLAG_UNDECAYED_PREDICTION 0x20
 
 /* Problem descriptor.
  *   B, H  >= 0; T >= 0 (prefill only; ignored by decode).
@@ -138,7 +145,8 @@ int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void
                   void *stream);
 
 /*
- * Decode: one token for every (b, h), applied in place to a resident state.
+ * Decode: one token for every (b, h), applied in place to a resident state
+ * (desc->flags may add GDR_FLAG_READ_BEFORE_WRITE and / or GDR_FLAG_UNDECAYED_PREDICTION).
  *
  *   q, k, k_w [B, H, dk], v [B, H, dv]          io_dtype (k_w NULL means k)
  *   alpha     [B, H] or [B, H, dk]              gate_dtype

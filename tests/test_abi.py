@@ -77,7 +77,8 @@ def _ptrs(start=0x10000000, n=10, step=0x1000000):
     ("dk", 0, -2), ("dk", 12, -2), ("dk", 136, -2), ("dv", 4, -2), ("dv", 256, -2),
     ("chunk", 8, -2), ("chunk", 128, -2), ("chunk", 48, -2),
     ("io_dtype", 7, -1), ("gate_dtype", -3, -1), ("alpha_mode", 2, -1), ("beta_mode", 3, -1),
-    ("flags", 0x10, -1), ("flags", 0x6, -1), ("flags", 0xA, -1),
+    ("flags", 0x40, -1), ("flags", 0x6, -1), ("flags", 0xA, -1),
+    ("flags", 0x10, -2), ("flags", 0x20, -2),  # decode-only options
 ])
 def test_descriptor_validation(g, field, value, status):
     d = _desc(g, **{field: value})
