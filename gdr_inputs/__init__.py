@@ -22,6 +22,8 @@ Layouts (row-major):
            S0: [B, H, dk, dv] fp32 or None
   decode   per-step tensors gain a leading step axis: q [steps, B, H, dk], ...
            S: [B, H, dk, dv] fp32
+  cache read-out  q: [B, T, H, dk] bf16, ckpt: [B, H, N, dk, dv] fp32,
+           gates: [B, T, H, N] fp32 or None, o_in: [B, T, H, dv] bf16 or None
 """
 from __future__ import annotations
 
@@ -150,6 +152,35 @@ class Decode:
         return dataclasses.replace(self, **kw)
 
 
+@dataclasses.dataclass(frozen=True)
+class CacheReadout:
+    """A Memory-Caching read-out: cached segment states read by later tokens.
+
+    gate_kind: "residual" (no gates), "dense" (every gate uniform in (0, 1)), or
+    "topk" (a router keeps `topk` of the earlier segments per token, uniform
+    weights on those, the rest 0)."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    dk: int
+    dv: int
+    seg: int                    # tokens per segment
+    gate_kind: str = "dense"
+    topk: int = 2
+    s_std: float = 0.02         # cached states ~ N(0, s_std)
+    with_o_in: bool = True      # o_in ~ bf16(N(0, 1))
+    seed: int = 0
+
+    @property
+    def N(self) -> int:
+        return self.T // self.seg
+
+    def scaled(self, **kw) -> "CacheReadout":
+        return dataclasses.replace(self, **kw)
+
+
 # The five workloads the library is specified against (named by content).
 TINY_GDN_F32 = Prefill("tiny_gdn_f32_B1H1T64d16C16", B=1, T=64, H=1, dk=16, dv=16, chunk=16,
                        io=F32, gate=F32, alpha_mu=3.0, alpha_sd=0.5, alpha_flip=True, seed=8401)
@@ -163,6 +194,10 @@ OSDN_LONG_PREFILL = Prefill("osdn_bf16_B1H32T65536d128C64", B=1, T=65536, H=32, 
 DECODE_B512 = Decode("decode_bf16_B512H16d128", B=512, H=16, dk=128, dv=128, steps=256, seed=8405)
 DECODE_DMEM_R8 = Decode("decode_deltamem_bf16_B8192H1r8", B=8192, H=1, dk=8, dv=8, steps=256,
                         seed=8406)
+
+# read-out of the long-context batch's segment caches: 16 segments of 4096 tokens
+MC_LONG_GRM = CacheReadout("mc_grm_bf16_B1H32T65536d128seg4096", B=1, T=65536, H=32, dk=128, dv=128,
+                           seg=4096, gate_kind="dense", seed=8407)
 
 PREFILL_WORKLOADS = [TINY_GDN_F32, GDN_PREFILL, KDA_FG2PLUS_PREFILL, OSDN_LONG_PREFILL]
 DECODE_WORKLOADS = [DECODE_B512, DECODE_DMEM_R8]
@@ -215,6 +250,30 @@ def make_decode(w: Decode) -> dict:
         beta_v = store(_sigmoid(rng.standard_normal((n, B, H, dv))), w.gate)
     S = rng.normal(0.0, w.s_std, (B, H, dk, dv)).astype(np.float32)
     return dict(q=q, k=k, k_w=None, v=v, alpha=alpha, beta_k=beta_k, beta_v=beta_v, S=S)
+
+
+def make_cache_readout(w: CacheReadout) -> dict:
+    """Draw a cache read-out.  Draw order: q, ckpt, gates, o_in."""
+    rng = np.random.default_rng(w.seed)
+    B, T, H, dk, dv, N = w.B, w.T, w.H, w.dk, w.dv, w.N
+    q = store(_l2_normalise(rng.standard_normal((B, T, H, dk))), BF16)
+    ckpt = rng.normal(0.0, w.s_std, (B, H, N, dk, dv)).astype(np.float32)
+    gates = None
+    if w.gate_kind == "dense":
+        gates = rng.uniform(0.0, 1.0, (B, T, H, N)).astype(np.float32)
+    elif w.gate_kind == "topk":
+        score = rng.standard_normal((B, T, H, N))
+        seg_of = np.minimum(np.arange(T) // w.seg, N)
+        allowed = np.arange(N)[None, :] < seg_of[:, None]            # [T, N]
+        score = np.where(allowed[None, :, None, :], score, -np.inf)
+        keep = np.argsort(-score, axis=-1)[..., :w.topk]
+        gates = np.zeros((B, T, H, N), dtype=np.float32)
+        np.put_along_axis(gates, keep, 1.0, axis=-1)
+        gates = np.where(allowed[None, :, None, :], gates, 0.0).astype(np.float32)
+    elif w.gate_kind != "residual":
+        raise ValueError(w.gate_kind)
+    o_in = store(rng.standard_normal((B, T, H, dv)), BF16) if w.with_o_in else None
+    return dict(q=q, ckpt=ckpt, gates=gates, o_in=o_in)
 
 
 def prefill_f64(w: Prefill, x: dict) -> dict:

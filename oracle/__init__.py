@@ -11,6 +11,9 @@ Contents:
   * ``chunked``: an independent NumPy evaluation of the same recurrence in the
     chunkwise WY / UT-transform form, used on tiny inputs to pin the sequential
     oracle (and the chunked algebra) against each other.
+  * ``memcache``: Memory Caching -- the state after every segment (the sequential
+    run, one segment at a time) and the residual / gated read-out over those
+    cached states, plain fp64.
 """
 from __future__ import annotations
 
