@@ -5,7 +5,9 @@ One step = one gdr_chunk_fwd over the batch B=4, H=16, T=4096, dk=dv=128,
 chunk 64 (bf16 q/k/v, fp32 scalar gates, zero initial state, o and the final
 state written), inputs resident in HBM.  The decode step (B=512, H=16,
 d=128, 256 steps replayed as one HIP graph, and the r=8 small-state case) is
-timed in the same run and reported under "decode".
+timed in the same run and reported under "decode", and the Memory-Caching
+read-out of the long-context batch's 16 segment states (B=1, H=32, T=65536,
+gated) under "mc_readout".
 
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T per step).
 """
@@ -24,8 +26,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "gdr_device.hpp",
-                  "gdr_internal.hpp"]
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip",
+                  "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
 
 
 def prefill_flops_per_token_head(C, dk, dv):
@@ -57,6 +59,16 @@ def decode_bytes_per_step(w):
     g = 2 if w.gate == "bf16" else 4
     nbh = w.B * w.H
     return nbh * (2 * w.dk * w.dv * 4 + (2 * w.dk + 2 * w.dv) * io + 2 * g)
+
+
+def mc_readout_flops(w):
+    """Algorithmic flops of the cache read-out: every token reads the caches of the
+    segments before its own, 2 * dk * dv per (token, cache) (the split-precision
+    second product is not counted)."""
+    import numpy as np
+
+    caches = np.minimum(np.arange(w.T) // w.seg, w.N).sum()
+    return float(w.B * w.H * caches * 2 * w.dk * w.dv)
 
 
 def kernel_source_digest():
@@ -102,6 +114,47 @@ def cpu_baseline(w, x, budget_heads):
                       f"recurrence, OpenMP over pairs, {dt:.2f} s wall"}
 
 
+def bench_mc_readout(g, gi, stream, reps):
+    """The cache read-out of the long-context batch, inputs resident, events on the
+    launch stream around each call (the small cache-preparation launch included)."""
+    import torch
+
+    w = gi.MC_LONG_GRM
+    x = gi.make_cache_readout(w)
+    q = gi.to_torch(x["q"], gi.BF16)
+    ck = gi.to_torch(x["ckpt"], gi.F32)
+    gates = gi.to_torch(x["gates"], gi.F32)
+    o_in = gi.to_torch(x["o_in"], gi.BF16)
+    out = torch.empty_like(o_in)
+    desc = g.Desc(B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dv, chunk=64, io_dtype=g.GDR_BF16, gate_dtype=g.GDR_F32,
+                  alpha_mode=0, beta_mode=0, flags=0)
+    need = g.gdr_mc_readout_workspace_size(desc, w.N)
+    ws = torch.empty(need, dtype=torch.uint8, device=q.device)
+
+    def call():
+        rc = g.gdr_mc_readout(desc, q, ck, w.N, w.seg, gates, o_in, out, ws, need, stream)
+        if rc != g.GDR_OK:
+            raise g.GdrError(rc, "gdr_mc_readout")
+
+    call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    fl = mc_readout_flops(w)
+    tf = fl / (ms * 1e-3) / 1e12
+    return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "algorithmic_flops": fl, "caches": w.N, "gates": w.gate_kind,
+            "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +166,7 @@ def main():
     ap.add_argument("--cpu-heads", type=int, default=64)
     ap.add_argument("--generic", action="store_true", help="force the fp32 vector-ALU prefill kernel")
     ap.add_argument("--only-prefill", action="store_true")
+    ap.add_argument("--mc-reps", type=int, default=5, help="timed Memory-Caching read-out calls")
     ap.add_argument("--state-kernel", choices=["cols16", "cols32", "wavecols"], default=None,
                     help="matrix-core state kernel (default: the library's choice)")
     ap.add_argument("--workload", choices=["gdn", "kda_fg2plus", "osdn_long"], default="gdn",
@@ -255,6 +309,7 @@ def main():
                                          "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(wd.name, digest)}}
             del graph, dd, S
         out["decode"] = dec
+        out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)

@@ -60,9 +60,17 @@ _lib.gdr_status_string.argtypes = [ctypes.c_int]
 _lib.gdr_status_string.restype = ctypes.c_char_p
 _lib.gdr_version.argtypes = []
 _lib.gdr_version.restype = ctypes.c_int
+_lib.gdr_chunk_fwd_ckpt.argtypes = [_dp] + [_vp] * 10 + [ctypes.c_int32, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gdr_chunk_fwd_ckpt.restype = ctypes.c_int
+_lib.gdr_mc_readout_workspace_size.argtypes = [_dp, ctypes.c_int32]
+_lib.gdr_mc_readout_workspace_size.restype = ctypes.c_size_t
+_lib.gdr_mc_readout.argtypes = [_dp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                ctypes.c_size_t, _vp]
+_lib.gdr_mc_readout.restype = ctypes.c_int
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
-            "gdr_status_string", "gdr_version")
+            "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
+            "gdr_mc_readout")
 
 
 class GdrError(RuntimeError):
@@ -106,6 +114,24 @@ def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, wo
     return int(_lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
                                   _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST),
                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdr_chunk_fwd_ckpt(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg_len: int, ckpt,
+                       workspace, workspace_bytes: int, stream=None) -> int:
+    return int(_lib.gdr_chunk_fwd_ckpt(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
+                                       _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST), int(seg_len),
+                                       _ptr(ckpt), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdr_mc_readout_workspace_size(desc: Desc, n_ckpt: int) -> int:
+    return int(_lib.gdr_mc_readout_workspace_size(ctypes.byref(desc), int(n_ckpt)))
+
+
+def gdr_mc_readout(desc: Desc, q, ckpt, n_ckpt: int, seg_len: int, gates, o_in, o_out, workspace,
+                   workspace_bytes: int, stream=None) -> int:
+    return int(_lib.gdr_mc_readout(ctypes.byref(desc), _ptr(q), _ptr(ckpt), int(n_ckpt), int(seg_len),
+                                   _ptr(gates), _ptr(o_in), _ptr(o_out), _ptr(workspace), int(workspace_bytes),
+                                   _stream(stream)))
 
 
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
@@ -159,6 +185,44 @@ def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=6
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_chunk_fwd")
     return o, ST
+
+
+def chunk_fwd_ckpt(q, k, v, alpha, beta_k, seg_len, *, k_w=None, beta_v=None, S0=None, chunk=64,
+                   want_state=True, workspace=None, generic=False, flags=0, stream=None):
+    """Prefill that also keeps the state after every complete segment of seg_len tokens.
+    Returns (o, ST or None, ckpt [B, H, floor(T / seg_len), dk, dv] fp32)."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic, flags=flags)
+    o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
+    ST = torch.empty((desc.B, desc.H, desc.dk, desc.dv), dtype=torch.float32, device=q.device) if want_state else None
+    n = desc.T // int(seg_len) if seg_len > 0 else 0
+    ckpt = torch.empty((desc.B, desc.H, n, desc.dk, desc.dv), dtype=torch.float32, device=q.device)
+    need = gdr_chunk_fwd_workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = gdr_chunk_fwd_ckpt(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg_len,
+                            ckpt if n > 0 else None, workspace, wbytes, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_chunk_fwd_ckpt")
+    return o, ST, ckpt
+
+
+def mc_readout(q, ckpt, seg_len, *, gates=None, o_in=None, out=None, workspace=None, stream=None):
+    """o_out[t] = o_in[t] + sum_{s < min(t // seg_len, N)} g[t, s] M_s^T q[t] (g = 1 without gates).
+    q [B, T, H, 128] bf16, ckpt [B, H, N, 128, 128] fp32, gates [B, T, H, N] fp32 or None."""
+    B, T, H, dk = q.shape
+    n = ckpt.shape[2]
+    desc = Desc(B=B, T=T, H=H, dk=dk, dv=ckpt.shape[-1], chunk=64, io_dtype=_dtype_code(q), gate_dtype=GDR_F32,
+                alpha_mode=0, beta_mode=0, flags=0)
+    o = out if out is not None else torch.empty(q.shape[:-1] + (ckpt.shape[-1],), dtype=q.dtype, device=q.device)
+    need = gdr_mc_readout_workspace_size(desc, n)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = gdr_mc_readout(desc, q, ckpt, n, seg_len, gates, o_in, o, workspace, wbytes, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_mc_readout")
+    return o
 
 
 def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0, stream=None):

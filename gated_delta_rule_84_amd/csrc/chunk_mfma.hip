@@ -43,14 +43,11 @@
 
 #include "gdr_device.hpp"
 #include "gdr_internal.hpp"
+#include "gdr_mfma.hpp"
 
 namespace gdr {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kC = 64;
 constexpr int kD = 128;
@@ -82,11 +79,6 @@ constexpr int kRcWl = 106496;
 constexpr int kRcGC = 122880;    // f32 [128]       e^{g_C} per key channel
 constexpr int kRcBytes = 123392;
 
-__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
 
 // x = hi + lo with hi = bf16(x) and lo = bf16(x - hi), both round-to-nearest-even.
 __device__ __forceinline__ void split8(const float *x, bf16x8 &hi, bf16x8 &lo) {
@@ -102,19 +94,11 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ float ld_gate(const void *p, long i, int bf16) { return ld_elem(p, i, bf16); }
 
-typedef __attribute__((address_space(3))) void *lds_void_t;
-typedef __attribute__((address_space(1))) void *gbl_void_t;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 *lds_i16x4_t;
-
-// 16 bytes per lane, global -> LDS; lane l writes dst + 16 l (dst wave-uniform)
-__device__ __forceinline__ void dma16(const void *src, void *dst) {
-    __builtin_amdgcn_global_load_lds((gbl_void_t)src, (lds_void_t)dst, 16, 0, 0);
-}
 
 // Workgroup barrier ordered for LDS only: the fences are restricted to the local
 // address space, so the barrier waits for this wave's LDS traffic but not for its
-// outstanding global loads (or copies into LDS), which stay in flight across it.
+// outstanding global loads into registers, which stay in flight across it.  Copies
+// into LDS (global_load_lds) write LDS, so the compiler waits for those too.
 // __syncthreads() would drain every outstanding global load at each barrier.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
@@ -611,13 +595,6 @@ __device__ __forceinline__ void load_chunk(const ChunkParams &p, int NT, int bh,
     if (w == 0) f.gf = ld16(rec + kRecGam + 16 * min(l, 32));
 }
 
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
-// two fp32 -> two bf16 (round to nearest even) in one packed conversion
-__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){a, b}, bf16x2));
-}
 
 // fp32 x = hi + lo, both bf16 round-to-nearest-even, packed four to a u32x2.
 __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
@@ -1166,6 +1143,13 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     }
             }
             publish_state();  // for the next chunk (the side wave read this chunk's before B1)
+            if (ckpt_after(p, c)) {
+                float *Ck = p.ckpt + ((long)bh * p.nck + (c + 1) / p.seg_chunks - 1) * kD * kD;
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Ck[(long)(16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+            }
         } else {
             if (c + 1 < NT) issue(c + 1, bb ^ 1);
             // O0 = Q S from the published state fragments
@@ -1515,6 +1499,13 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                     }
             }
             publish_state();
+            if (ckpt_after(p, c)) {
+                float *Ck = p.ckpt + ((long)bh * p.nck + (c + 1) / p.seg_chunks - 1) * kD * kD;
+#pragma unroll
+                for (int kt = 0; kt < 8; ++kt)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) Ck[(long)(16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+            }
         } else {
             if (c > 0) issue_w(c);
             // O0 = Q S

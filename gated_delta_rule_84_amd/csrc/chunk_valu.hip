@@ -222,6 +222,13 @@ __global__ void __launch_bounds__(kThreads) chunk_valu_kernel(ChunkParams p) {
             }
         }
         __syncthreads();
+        if (ckpt_after(p, c)) {
+            float *Ck = p.ckpt + ((long)bh * p.nck + (c + 1) / p.seg_chunks - 1) * dk * dv;
+            for (int e = tid; e < dk * kVB; e += kThreads) {
+                const int i = e / kVB, j = e % kVB;
+                if (j < nv) Ck[(long)i * dv + j0 + j] = Sb[e];
+            }
+        }
     }
 
     if (p.ST) {

@@ -112,12 +112,15 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_desc *d) {
     return select_path(d, p) == 1 ? chunk_mfma_workspace(p) : 0;
 }
 
-int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
-                  const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
-                  void *o, float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+int gdr_chunk_fwd_ckpt(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                       const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                       void *o, float *ST, int32_t seg_len, float *ckpt, void *workspace,
+                       size_t workspace_bytes, void *stream) {
     int rc = check_desc(d, true);
     if (rc) return rc;
     ChunkParams p = chunk_params(d);
+    if (seg_len <= 0 || seg_len % d->chunk) return GDR_EINVAL;
+    const int nck = d->T / seg_len;
     const long long ntok = (long long)d->B * d->T * d->H;
     const size_t es = p.io_bf16 ? 2 : 4, gs = p.gate_bf16 ? 2 : 4;
     const size_t nq = ntok * d->dk * es, nv = ntok * d->dv * es;
@@ -140,6 +143,14 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k
         if (ST && overlaps(o, nv, ST, ns)) return GDR_EINVAL;
     }
     if ((S0 && !aligned16(S0)) || (ST && !aligned16(ST))) return GDR_EINVAL;
+    if (nck > 0) {
+        if (!ckpt || !aligned16(ckpt)) return GDR_EINVAL;
+        const size_t nc = ns * (size_t)nck;
+        const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST};
+        const size_t lens[] = {nq, nq, nq, nv, na, nbk, nbv, ns, nv, ns};
+        for (int i = 0; i < 10; ++i)
+            if (overlaps(ckpt, nc, ins[i], lens[i])) return GDR_EINVAL;
+    }
     if (ST && S0 && ST != S0 && overlaps(ST, ns, S0, ns)) return GDR_EINVAL;
     if (ST && ntok > 0) {
         const void *ins[] = {q, k, k_w, v, alpha, beta_k, beta_v};
@@ -148,6 +159,7 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k
             if (overlaps(ST, ns, ins[i], lens[i])) return GDR_EINVAL;
     }
     const int path = select_path(d, p);
+    if (nck > 0 && path == 1 && (p.state_cols == 16 || p.state_cols == 32)) return GDR_EUNSUPPORTED;
     const size_t ws_need = path == 1 ? chunk_mfma_workspace(p) : 0;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned16(workspace)))
         return GDR_EWORKSPACE;
@@ -173,7 +185,64 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k
     p.q = q; p.k = k; p.kw = k_w ? k_w : k; p.v = v;
     p.alpha = alpha; p.beta_k = beta_k; p.beta_v = beta_v;
     p.S0 = S0; p.o = o; p.ST = ST; p.ws = workspace;
+    if (nck > 0) {
+        p.ckpt = ckpt;
+        p.seg_chunks = seg_len / d->chunk;
+        p.nck = nck;
+    }
     const hipError_t e = path == 1 ? launch_chunk_mfma(p, st) : launch_chunk_valu(p, st);
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                  const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                  void *o, float *ST, void *workspace, size_t workspace_bytes, void *stream) {
+    // no segment ends are kept: a segment longer than any T
+    const int32_t seg = d && d->chunk > 0 ? (0x7fffffff / d->chunk) * d->chunk : 1;
+    return gdr_chunk_fwd_ckpt(d, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg, nullptr, workspace,
+                              workspace_bytes, stream);
+}
+
+size_t gdr_mc_readout_workspace_size(const gdr_desc *d, int32_t n_ckpt) {
+    if (!d || d->B < 0 || d->H < 0 || n_ckpt < 0) return 0;
+    return mc_readout_workspace(d->B, d->H, n_ckpt);
+}
+
+int gdr_mc_readout(const gdr_desc *d, const void *q, const float *ckpt, int32_t n_ckpt, int32_t seg_len,
+                   const float *gates, const void *o_in, void *o_out, void *workspace, size_t workspace_bytes,
+                   void *stream) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0 || n_ckpt < 0 || seg_len <= 0) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 || d->dk != 128 || d->dv != 128) return GDR_EUNSUPPORTED;
+    const long long nbh = (long long)d->B * d->H, ntok = nbh * d->T;
+    if (nbh > 0x7fffffffLL) return GDR_EUNSUPPORTED;
+    if (ntok == 0) return GDR_OK;
+    if (!q || !o_out || !aligned16(q) || !aligned16(o_out)) return GDR_EINVAL;
+    if (o_in && !aligned16(o_in)) return GDR_EINVAL;
+    const size_t nq = ntok * 128 * 2, nc = (size_t)nbh * n_ckpt * 128 * 128 * sizeof(float);
+    const size_t ng = (size_t)ntok * n_ckpt * sizeof(float);
+    const size_t wneed = mc_readout_workspace(d->B, d->H, n_ckpt);
+    if (n_ckpt > 0) {
+        if (!ckpt || !aligned16(ckpt)) return GDR_EINVAL;
+        if (gates && !aligned_to(gates, 4)) return GDR_EINVAL;
+        if (!workspace || workspace_bytes < wneed || !aligned16(workspace)) return GDR_EWORKSPACE;
+    }
+    // o_out may be o_in itself but overlaps nothing else; the workspace overlaps nothing
+    if (o_in && o_in != o_out && overlaps(o_out, nq, o_in, nq)) return GDR_EINVAL;
+    {
+        const void *ins[] = {q, n_ckpt ? ckpt : nullptr, n_ckpt ? gates : nullptr};
+        const size_t lens[] = {nq, nc, ng};
+        for (int i = 0; i < 3; ++i)
+            if (overlaps(o_out, nq, ins[i], lens[i])) return GDR_EINVAL;
+        if (n_ckpt > 0) {
+            const void *all[] = {q, ckpt, gates, o_in, o_out};
+            const size_t alens[] = {nq, nc, ng, nq, nq};
+            for (int i = 0; i < 5; ++i)
+                if (overlaps(workspace, wneed, all[i], alens[i])) return GDR_EINVAL;
+        }
+    }
+    const hipError_t e = launch_mc_readout(d->B, d->T, d->H, n_ckpt, seg_len, q, ckpt, gates, o_in, o_out,
+                                           workspace, static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 

@@ -19,8 +19,17 @@ struct ChunkParams {
     const float *S0;  // may be NULL (zero state)
     void *o;
     float *ST;        // may be NULL
+    float *ckpt;      // may be NULL: states at segment ends, [B, H, nck, dk, dv]
+    int seg_chunks;   // chunks per segment (ckpt only)
+    int nck;          // segment ends stored per (batch, head): floor(T / segment length)
     void *ws;         // workspace (path dependent)
 };
+
+// True when chunk c (0-based) ends a segment whose state is kept; its slot is then
+// (c + 1) / seg_chunks - 1.
+__device__ __forceinline__ bool ckpt_after(const ChunkParams &p, int c) {
+    return p.ckpt && (c + 1) % p.seg_chunks == 0 && (c + 1) / p.seg_chunks <= p.nck;
+}
 
 // Parameters of one decode step.
 struct DecodeParams {
@@ -40,5 +49,8 @@ size_t chunk_mfma_workspace(const ChunkParams &p);
 bool chunk_mfma_supported(const ChunkParams &p);
 hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t s);
 hipError_t launch_state_copy(const float *S0, float *ST, long n, hipStream_t s);
+size_t mc_readout_workspace(int B, int H, int N);
+hipError_t launch_mc_readout(int B, int T, int H, int N, int seg, const void *q, const float *ckpt,
+                             const float *gates, const void *oin, void *oout, void *ws, hipStream_t s);
 
 }  // namespace gdr

@@ -159,6 +159,53 @@ int gdr_decode_step(const gdr_desc *desc, const void *q, const void *k, const vo
                     const void *v, const void *alpha, const void *beta_k, const void *beta_v,
                     float *S, void *o, void *stream);
 
+/*
+ * Prefill that also keeps the state at every segment end, for Memory Caching
+ * [Memory Caching: RNNs with Growing Memory, section 2 (segmentation, cache of states)]:
+ * the sequence is cut into segments of seg_len tokens and the state after the
+ * last token of each complete segment is stored.
+ *
+ *   seg_len   tokens per segment, a positive multiple of desc->chunk (else GDR_EINVAL)
+ *   ckpt      [B, H, N, dk, dv] fp32, N = floor(T / seg_len): slot s holds the state
+ *             after token (s + 1) * seg_len - 1.  May be NULL when N == 0; must not
+ *             overlap any input, o or ST.
+ * Everything else is exactly gdr_chunk_fwd (same outputs, same workspace size).  The
+ * four-wave state kernels selected by GDR_FLAG_STATE_COLS16 / 32 do not keep segment
+ * states: with those flags the call returns GDR_EUNSUPPORTED.
+ */
+int gdr_chunk_fwd_ckpt(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
+                       const void *v, const void *alpha, const void *beta_k, const void *beta_v,
+                       const float *S0, void *o, float *ST, int32_t seg_len, float *ckpt,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Memory-Caching read-out [Memory Caching: RNNs with Growing Memory, sections 2 (retrieval) and 3
+ * (residual memory, gated residual memory; memory soup equals the gated form for
+ * a linear memory; sparse selective caching is the gated form with most gates 0)]:
+ *
+ *   o_out[t] = o_in[t] + sum over s < min(floor(t / seg_len), n_ckpt) of
+ *              g[t, s] * M_s^T q[t]
+ *
+ * for every (b, h), with M_s = ckpt[b, h, s] (a dk x dv state, M_s^T q reads it
+ * like the online state) and g[t, s] = gates[b, t, h, s], or 1 for every s when
+ * gates is NULL (residual memory).  Token t sees only the segments that end
+ * before its own segment starts.
+ *
+ *   q         [B, T, H, dk] bf16 (required)
+ *   ckpt      [B, H, n_ckpt, dk, dv] fp32 (required when n_ckpt > 0)
+ *   gates     [B, T, H, n_ckpt] fp32 or NULL
+ *   o_in      [B, T, H, dv] bf16, or NULL for zero; may equal o_out (in place)
+ *   o_out     [B, T, H, dv] bf16 (required); the sum is formed in fp32 and rounded once
+ *   workspace at least gdr_mc_readout_workspace_size() bytes
+ * Supported: io_dtype bf16, dk == dv == 128 (else GDR_EUNSUPPORTED).  desc->chunk,
+ * alpha_mode, beta_mode and gate_dtype are not used.  Gate rows that are zero for
+ * a whole 64-token tile skip that cache's products.
+ */
+size_t gdr_mc_readout_workspace_size(const gdr_desc *desc, int32_t n_ckpt);
+int gdr_mc_readout(const gdr_desc *desc, const void *q, const float *ckpt, int32_t n_ckpt,
+                   int32_t seg_len, const float *gates, const void *o_in, void *o_out,
+                   void *workspace, size_t workspace_bytes, void *stream);
+
 /* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
  * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */
 int gdr_chunk_fwd_path(const gdr_desc *desc);

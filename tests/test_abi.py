@@ -167,3 +167,43 @@ def test_binding_fails_loudly_without_library(tmp_path):
     code = "import gated_delta_rule_84_amd"
     r = subprocess.run([sys.executable, "-c", code], cwd=tmp_path, capture_output=True, text=True)
     assert r.returncode != 0 and "ImportError" in r.stderr
+
+
+# ---------------------------------------------------------------------------
+# Memory-Caching entry points: host-side validation (nothing is launched)
+# ---------------------------------------------------------------------------
+def test_chunk_fwd_ckpt_validation(g):
+    d = _desc(g, T=512)
+    q, k, v, a, b, o, st, ck, ws = _ptrs(n=9)
+    call = lambda desc, seg, ckpt, out=o: g.gdr_chunk_fwd_ckpt(desc, q, k, None, v, a, b, None, None, out, st,
+                                                               seg, ckpt, ws, 1 << 30, 0)
+    assert call(d, 0, ck) == g.GDR_EINVAL            # segment length must be positive
+    assert call(d, 96, ck) == g.GDR_EINVAL           # and a multiple of the chunk
+    assert call(d, 128, None) == g.GDR_EINVAL        # 4 segment states need a buffer
+    assert call(d, 128, FakePtr(ck.addr + 4)) == g.GDR_EINVAL  # misaligned
+    assert call(d, 128, o) == g.GDR_EINVAL           # overlaps the output
+    assert call(_desc(g, T=512, flags=g.GDR_FLAG_STATE_COLS16), 128, ck) == g.GDR_EUNSUPPORTED
+    assert call(_desc(g, T=512, chunk=48), 128, ck) == g.GDR_EUNSUPPORTED
+
+
+def test_mc_readout_validation(g):
+    d = _desc(g, T=1024)
+    q, ck, gt, oi, oo, ws = _ptrs(n=6, step=0x10000000)
+    need = g.gdr_mc_readout_workspace_size(d, 4)
+    assert need == 2 * 3 * 4 * 128 * 128 * 4
+    call = lambda desc, **kw: g.gdr_mc_readout(desc, kw.get("q", q), kw.get("ck", ck), kw.get("n", 4),
+                                               kw.get("seg", 256), kw.get("gt", gt), kw.get("oi", oi),
+                                               kw.get("oo", oo), kw.get("ws", ws), kw.get("wb", need), 0)
+    assert call(_desc(g, T=1024, io_dtype=g.GDR_F32)) == g.GDR_EUNSUPPORTED
+    assert call(_desc(g, T=1024, dk=64, dv=64)) == g.GDR_EUNSUPPORTED
+    assert call(d, seg=0) == g.GDR_EINVAL
+    assert call(d, n=-1) == g.GDR_EINVAL
+    assert call(d, ck=None) == g.GDR_EINVAL
+    assert call(d, q=None) == g.GDR_EINVAL
+    assert call(d, oo=FakePtr(oo.addr + 8)) == g.GDR_EINVAL
+    assert call(d, wb=need - 1) == g.GDR_EWORKSPACE
+    assert call(d, ws=None) == g.GDR_EWORKSPACE
+    assert call(d, oo=FakePtr(q.addr + 256)) == g.GDR_EINVAL           # output overlaps q
+    assert call(d, oi=FakePtr(oo.addr + 256)) == g.GDR_EINVAL          # partial overlap of o_in and o_out
+    assert call(d, ws=FakePtr(ck.addr)) == g.GDR_EINVAL                # workspace overlaps the caches
+    assert call(_desc(g, B=0)) == g.GDR_OK                             # empty batch: nothing to do
