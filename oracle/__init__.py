@@ -11,6 +11,8 @@ Contents:
   * ``chunked``: an independent NumPy evaluation of the same recurrence in the
     chunkwise WY / UT-transform form, used on tiny inputs to pin the sequential
     oracle (and the chunked algebra) against each other.
+  * ``osdn_precond``: OSDN phase 1, the preconditioner scan over the key stream
+    (write keys, final preconditioner, geometric-mean loss ratio q_geo).
   * ``memcache``: Memory Caching -- the state after every segment (the sequential
     run, one segment at a time) and the residual / gated read-out over those
     cached states, plain fp64.
@@ -58,6 +60,8 @@ def _bind(lib):
     lib.gdr_ref_decode_step.restype = ctypes.c_int
     lib.gdr_ref_dmem_step.argtypes = [ctypes.c_int] * 4 + [dp] * 7 + [ctypes.c_int]
     lib.gdr_ref_dmem_step.restype = ctypes.c_int
+    lib.gdr_ref_osdn_precond.argtypes = [ctypes.c_int] * 4 + [dp] * 3 + [ctypes.c_double] + [dp] * 4 + [ctypes.c_int]
+    lib.gdr_ref_osdn_precond.restype = ctypes.c_int
     lib.gdr_ref_max_threads.argtypes = []
     lib.gdr_ref_max_threads.restype = ctypes.c_int
     return lib
@@ -177,6 +181,22 @@ def dmem_step(M, q, k, v, lam, beta, nthreads: int = 0):
     if rc != 0:
         raise ValueError(f"gdr_ref_dmem_step rejected its arguments (status {rc})")
     return r, M
+
+
+def osdn_precond(k, beta, eta: float, *, r=None, d0=None, nthreads: int = 0):
+    """OSDN phase 1 in fp64: k [B, T, H, dk], beta [B, T, H], r [B, T, H] or None
+    (retention 1), d0 [B, H, dk] or None (ones).  Returns (kw [B, T, H, dk],
+    dT [B, H, dk], qgeo [B, H])."""
+    k, beta, r, d0 = map(_c64, (k, beta, r, d0))
+    B, T, H, dk = k.shape
+    kw = np.empty((B, T, H, dk))
+    dT = np.empty((B, H, dk))
+    qg = np.empty((B, H))
+    rc = _load().gdr_ref_osdn_precond(B, T, H, dk, _dp(k), _dp(beta), _dp(r), float(eta), _dp(d0), _dp(kw),
+                                      _dp(dT), _dp(qg), nthreads)
+    if rc != 0:
+        raise ValueError(f"gdr_ref_osdn_precond rejected its arguments (status {rc})")
+    return kw, dT, qg
 
 
 def rel_l2(x, ref) -> float:

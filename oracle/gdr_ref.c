@@ -251,6 +251,66 @@ int gdr_ref_dmem_step(int B, int H, int dk, int dv, const double *q, const doubl
     return failed ? REF_EINVAL : REF_OK;
 }
 
+/*
+ * OSDN phase 1: the scan over the key stream that produces the preconditioned
+ * write keys of phase 2 [OSDN page, section 2.2 (hypergradient feedback, the
+ * closed-form surrogate, the two phases) and section 2.3 (retention gate of the
+ * preconditioner, APF)].  For one (batch, head), with d the diagonal
+ * preconditioner (d_0 given, all ones when NULL) and, per token t,
+ *     kw_t = d_t (.) k_t                            write key used at token t
+ *     h_t(d) = ((1 - beta_t <d, k_t^2>)^2 - 1) / (2 |k_t|^2)   surrogate
+ *     grad_t = dh_t/dd at d_t = -beta_t (1 - beta_t <d_t, k_t^2>) k_t^2 / |k_t|^2
+ *     d_{t+1} = r_t d_t - eta grad_t                online gradient descent on
+ *                                                   h_t, retention r_t (1 = OSDN)
+ * (the page prints the APF step with "+ eta grad"; it is read as the descent
+ * step of the online gradient method the section names).  A zero key has no
+ * gradient (0/0 in the formula): d is only multiplied by r_t then.
+ * The per-token loss ratio f_t(S_t) / f_t(S_{t-1}) of phase 2 is
+ * (1 - beta_t <d_t, k_t^2>)^2 (the residual along k_t shrinks by that factor
+ * in one step [OSDN page, section 2.2 surrogate; section 4.2 q_geo]); q_geo is
+ * its geometric mean over the T tokens, exp(mean_t log ratio_t).
+ * Layouts: k, kw [B, T, H, dk]; beta, r [B, T, H] (r may be NULL: all ones);
+ * d0, dT [B, H, dk] (d0 may be NULL: ones; dT may be NULL); qgeo [B, H] (may
+ * be NULL; 1 when T == 0).
+ */
+int gdr_ref_osdn_precond(int B, int T, int H, int dk, const double *k, const double *beta, const double *r,
+                         double eta, const double *d0, double *kw, double *dT, double *qgeo, int nthreads)
+{
+    if (B < 0 || T < 0 || H < 0 || dk < 1 || dk > 1024) return REF_EINVAL;
+    if (!k || !beta || !kw) return REF_EINVAL;
+#ifdef _OPENMP
+    if (nthreads > 0) omp_set_num_threads(nthreads);
+#pragma omp parallel for schedule(static)
+#endif
+    for (int bh = 0; bh < B * H; ++bh) {
+        const int b = bh / H, h = bh % H;
+        double d[1024];
+        for (int i = 0; i < dk; ++i) d[i] = d0 ? d0[(size_t)bh * dk + i] : 1.0;
+        double logsum = 0.0;
+        for (int t = 0; t < T; ++t) {
+            const size_t tok = ((size_t)b * T + t) * H + h;
+            const double *kt = k + tok * dk;
+            const double bt = beta[tok], rt = r ? r[tok] : 1.0;
+            double nk = 0.0, s = 0.0;
+            for (int i = 0; i < dk; ++i) {
+                nk += kt[i] * kt[i];
+                s += d[i] * kt[i] * kt[i];
+                kw[tok * dk + i] = d[i] * kt[i];
+            }
+            const double u = 1.0 - bt * s;          /* residual factor of this step */
+            logsum += log(u * u);
+            for (int i = 0; i < dk; ++i) {
+                const double grad = nk > 0.0 ? -bt * u * kt[i] * kt[i] / nk : 0.0;
+                d[i] = rt * d[i] - eta * grad;
+            }
+        }
+        if (dT)
+            for (int i = 0; i < dk; ++i) dT[(size_t)bh * dk + i] = d[i];
+        if (qgeo) qgeo[bh] = T > 0 ? exp(logsum / T) : 1.0;
+    }
+    return REF_OK;
+}
+
 int gdr_ref_max_threads(void)
 {
 #ifdef _OPENMP
