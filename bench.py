@@ -7,7 +7,8 @@ state written), inputs resident in HBM.  The decode step (B=512, H=16,
 d=128, 256 steps replayed as one HIP graph, and the r=8 small-state case) is
 timed in the same run and reported under "decode", and the Memory-Caching
 read-out of the long-context batch's 16 segment states (B=1, H=32, T=65536,
-gated) under "mc_readout".
+gated) under "mc_readout", and the OSDN phase-1 preconditioner scan of the
+long-context batch's keys (with retention gates) under "osdn_precond".
 
 Prints ONE JSON line.  `value` is prefill tokens/s (B*T per step).
 """
@@ -26,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip",
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip",
                   "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
 
 
@@ -153,6 +154,51 @@ def bench_mc_readout(g, gi, stream, reps):
             "algorithmic_flops": fl, "caches": w.N, "gates": w.gate_kind,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None}}
+
+
+def bench_osdn_precond(g, gi, stream, reps):
+    """OSDN phase 1 over the long-context batch's keys (B=1, H=32, T=65536, retention
+    gates), inputs resident; events on the launch stream around each call (chunk
+    solve + scan).  Algorithmic bytes: k read and k_w written (bf16), beta and r
+    read (fp32), the preconditioner in and out."""
+    import torch
+
+    w = gi.OSDN_LONG_PREFILL
+    x = gi.make_prefill(w)
+    k = gi.to_torch(x["k"], w.io)
+    beta = gi.to_torch(x["beta_k"], w.gate)
+    r = gi.to_torch(gi.make_retention(w), w.gate)
+    desc = g.Desc(B=w.B, T=w.T, H=w.H, dk=w.dk, dv=w.dk, chunk=64, io_dtype=g.GDR_BF16, gate_dtype=g.GDR_F32,
+                  alpha_mode=0, beta_mode=0, flags=0)
+    need = g.gdr_osdn_precond_workspace_size(desc)
+    ws = torch.empty(need, dtype=torch.uint8, device=k.device)
+    kw = torch.empty_like(k)
+    dT = torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=k.device)
+    qg = torch.empty((w.B, w.H), dtype=torch.float32, device=k.device)
+
+    def call():
+        rc = g.gdr_osdn_precond(desc, k, beta, r, 1.0, None, kw, dT, qg, ws, need, stream)
+        if rc != g.GDR_OK:
+            raise g.GdrError(rc, "gdr_osdn_precond")
+
+    call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    ntok = w.B * w.T * w.H
+    nbytes = ntok * (2 * w.dk * 2 + 2 * 4) + 2 * w.B * w.H * w.dk * 4
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": "osdn_precond_bf16_B1H32T65536d128_retention", "ms_per_call": ms,
+            "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "qgeo_mean": float(qg.mean()),
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
 
 def main():
@@ -310,6 +356,7 @@ def main():
             del graph, dd, S
         out["decode"] = dec
         out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps)
+        out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)

@@ -8,7 +8,7 @@ take a ``Desc`` and tensors (or None) and return the C status code;
 ``chunk_fwd`` and ``decode_step`` allocate outputs and raise on a non-OK
 status.
 
-The library must have been built (``python -m gated_delta_rule_84_amd.build``);
+The library must have been built (``python gated_delta_rule_84_amd/build.py``);
 importing this package without it raises ImportError.  There is no fallback.
 """
 from __future__ import annotations
@@ -44,7 +44,7 @@ class Desc(ctypes.Structure):
 
 
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is missing: build it with `python -m gated_delta_rule_84_amd.build`")
+    raise ImportError(f"{LIB_PATH} is missing: build it with `python gated_delta_rule_84_amd/build.py`")
 _lib = ctypes.CDLL(LIB_PATH)
 _vp = ctypes.c_void_p
 _dp = ctypes.POINTER(Desc)
@@ -67,10 +67,14 @@ _lib.gdr_mc_readout_workspace_size.restype = ctypes.c_size_t
 _lib.gdr_mc_readout.argtypes = [_dp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp, _vp,
                                 ctypes.c_size_t, _vp]
 _lib.gdr_mc_readout.restype = ctypes.c_int
+_lib.gdr_osdn_precond_workspace_size.argtypes = [_dp]
+_lib.gdr_osdn_precond_workspace_size.restype = ctypes.c_size_t
+_lib.gdr_osdn_precond.argtypes = [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gdr_osdn_precond.restype = ctypes.c_int
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
-            "gdr_mc_readout")
+            "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond")
 
 
 class GdrError(RuntimeError):
@@ -132,6 +136,16 @@ def gdr_mc_readout(desc: Desc, q, ckpt, n_ckpt: int, seg_len: int, gates, o_in, 
     return int(_lib.gdr_mc_readout(ctypes.byref(desc), _ptr(q), _ptr(ckpt), int(n_ckpt), int(seg_len),
                                    _ptr(gates), _ptr(o_in), _ptr(o_out), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)))
+
+
+def gdr_osdn_precond_workspace_size(desc: Desc) -> int:
+    return int(_lib.gdr_osdn_precond_workspace_size(ctypes.byref(desc)))
+
+
+def gdr_osdn_precond(desc: Desc, k, beta, r, eta: float, d0, k_w, dT, qgeo, workspace, workspace_bytes: int,
+                     stream=None) -> int:
+    return int(_lib.gdr_osdn_precond(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(k_w),
+                                     _ptr(dT), _ptr(qgeo), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
@@ -223,6 +237,25 @@ def mc_readout(q, ckpt, seg_len, *, gates=None, o_in=None, out=None, workspace=N
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_mc_readout")
     return o
+
+
+def osdn_precond(k, beta, eta, *, r=None, d0=None, workspace=None, stream=None):
+    """OSDN phase 1.  k [B, T, H, dk] (bf16 or fp32), beta and r [B, T, H].
+    Returns (k_w like k, dT [B, H, dk] fp32, qgeo [B, H] fp32)."""
+    B, T, H, dk = k.shape
+    desc = Desc(B=B, T=T, H=H, dk=dk, dv=dk, chunk=64, io_dtype=_dtype_code(k), gate_dtype=_dtype_code(beta),
+                alpha_mode=0, beta_mode=0, flags=0)
+    kw = torch.empty_like(k)
+    dT = torch.empty((B, H, dk), dtype=torch.float32, device=k.device)
+    qg = torch.empty((B, H), dtype=torch.float32, device=k.device)
+    need = gdr_osdn_precond_workspace_size(desc)
+    if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    rc = gdr_osdn_precond(desc, k, beta, r, eta, d0, kw, dT, qg, workspace, wbytes, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_osdn_precond")
+    return kw, dT, qg
 
 
 def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0, stream=None):

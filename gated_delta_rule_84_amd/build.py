@@ -1,6 +1,6 @@
 """Build the gated delta-rule HIP library (libgdr.so) for gfx950 with hipcc.
 
-Usage: python -m gated_delta_rule_84_amd.build   (or __graft_entry__.build())
+Usage: python gated_delta_rule_84_amd/build.py   (or __graft_entry__.build())
 Each translation unit is compiled to an object under _build/ in parallel and
 linked into gated_delta_rule_84_amd/libgdr.so.
 """
@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgdr.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["gdr_api.hip", "decode.hip", "chunk_valu.hip", "chunk_mfma.hip", "mc_readout.hip"]
+SOURCES = ["gdr_api.hip", "decode.hip", "chunk_valu.hip", "chunk_mfma.hip", "mc_readout.hip", "osdn_precond.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -246,6 +246,53 @@ int gdr_mc_readout(const gdr_desc *d, const void *q, const float *ckpt, int32_t 
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 
+size_t gdr_osdn_precond_workspace_size(const gdr_desc *d) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0) return 0;
+    return osdn_precond_workspace(d->B, d->T, d->H);
+}
+
+int gdr_osdn_precond(const gdr_desc *d, const void *k, const void *beta, const void *r, float eta, const float *d0,
+                     void *k_w, float *dT, float *qgeo, void *workspace, size_t workspace_bytes, void *stream) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->beta_mode != GDR_BETA_SCALAR) return GDR_EINVAL;
+    if (!(eta == eta)) return GDR_EINVAL;  // NaN
+    if (d->dk < 8 || d->dk > 128 || (d->dk & 7)) return GDR_EUNSUPPORTED;
+    const long long nbh = (long long)d->B * d->H, ntok = nbh * d->T;
+    if (nbh > 0x7fffffffLL) return GDR_EUNSUPPORTED;
+    if (nbh == 0) return GDR_OK;
+    const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;
+    const size_t nk = (size_t)ntok * d->dk * es, ng = (size_t)ntok * gs, nd = (size_t)nbh * d->dk * sizeof(float);
+    if (ntok > 0) {
+        if (!k || !beta || !k_w || !aligned16(k) || !aligned16(k_w)) return GDR_EINVAL;
+        if (!aligned_to(beta, gs) || (r && !aligned_to(r, gs))) return GDR_EINVAL;
+    }
+    if ((d0 && !aligned16(d0)) || (dT && !aligned_to(dT, 4)) || (qgeo && !aligned_to(qgeo, 4))) return GDR_EINVAL;
+    const size_t wneed = osdn_precond_workspace(d->B, d->T, d->H);
+    if (wneed > 0 && (!workspace || workspace_bytes < wneed || !aligned16(workspace))) return GDR_EWORKSPACE;
+    // outputs overlap no input and no other output; the workspace overlaps nothing
+    {
+        const void *outs[] = {ntok ? k_w : nullptr, dT, qgeo};
+        const size_t olens[] = {nk, nd, (size_t)nbh * sizeof(float)};
+        const void *ins[] = {k, beta, r, d0};
+        const size_t ilens[] = {nk, ng, ng, nd};
+        for (int i = 0; i < 3; ++i) {
+            for (int j = 0; j < 4; ++j)
+                if (overlaps(outs[i], olens[i], ins[j], ilens[j])) return GDR_EINVAL;
+            for (int j = i + 1; j < 3; ++j)
+                if (overlaps(outs[i], olens[i], outs[j], olens[j])) return GDR_EINVAL;
+            if (overlaps(workspace, wneed, outs[i], olens[i])) return GDR_EINVAL;
+        }
+        for (int j = 0; j < 4; ++j)
+            if (overlaps(workspace, wneed, ins[j], ilens[j])) return GDR_EINVAL;
+    }
+    const hipError_t e = launch_osdn_precond(d->B, d->T, d->H, d->dk, d->io_dtype == GDR_BF16, d->gate_dtype == GDR_BF16,
+                                             eta, k, beta, r, d0, k_w, dT, qgeo, workspace,
+                                             static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
 int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
                     const void *alpha, const void *beta_k, const void *beta_v, float *S, void *o,
                     void *stream) {

@@ -50,6 +50,10 @@ bool chunk_mfma_supported(const ChunkParams &p);
 hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t s);
 hipError_t launch_state_copy(const float *S0, float *ST, long n, hipStream_t s);
 size_t mc_readout_workspace(int B, int H, int N);
+size_t osdn_precond_workspace(int B, int T, int H);
+hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
+                               const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
+                               void *ws, hipStream_t s);
 hipError_t launch_mc_readout(int B, int T, int H, int N, int seg, const void *q, const float *ckpt,
                              const float *gates, const void *oin, void *oout, void *ws, hipStream_t s);
 

@@ -1,0 +1,543 @@
+// osdn_precond.hip -- OSDN phase 1: the preconditioner scan over the key stream.
+//
+// OSDN page, sections 2.2 (closed-form hypergradient surrogate, two phases) and
+// 2.3 (retention gate of the preconditioner).  For one (batch, head), with the
+// diagonal preconditioner d (d_0 given) and, per token t,
+//     kw_t = d_t (.) k_t,   u_t = 1 - beta_t <d_t, a_t>,   a_t = k_t (.) k_t
+//     d_{t+1} = r_t d_t + e_t a_t,   e_t = c_t u_t,   c_t = eta beta_t / |k_t|^2
+// (the online-gradient-descent step on the surrogate; c_t = 0 for a zero key), and
+// the per-token loss ratio of phase 2 is u_t^2; q_geo = exp(mean_t log u_t^2).
+//
+// The update is affine in d, so a chunk of n <= 64 tokens starting from d_0 obeys
+//     d_t = P_t d_0 + sum_{j<t} (P_t / P_{j+1}) e_j a_j,       P_t = prod_{i<t} r_i
+//     (I + A) e = z,   A_{tj} = c_t beta_t (P_t / P_{j+1}) <a_t, a_j>  (j < t),
+//                      z_t = c_t - c_t beta_t P_t <a_t, d_0>.
+// Four launches:
+//   osdn_chunk_kernel   every chunk in parallel: a, |k|^2, the coefficients, the
+//                       decayed Gram matrix and Tm = (I + A)^{-1} (unit lower
+//                       triangular: the four 16 x 16 diagonal blocks by forward
+//                       substitution, one column per thread, then the off-diagonal
+//                       blocks by distance from the diagonal), into a workspace record.
+//   osdn_chain_kernel   one workgroup per (batch, head), chunks in order, only what
+//                       the next chunk needs: x_t = <a_t, d_0>, e = Tm z and
+//                       d_n = P_n d_0 + sum_j (P_n / P_{j+1}) e_j a_j; d_0 and e of
+//                       every chunk go to its record.
+//   osdn_emit_kernel    every chunk in parallel again: from d_0 and e, d one token at
+//                       a time (a key channel per thread), the write keys, and the
+//                       chunk's sum of log loss ratios.
+//   osdn_qgeo_kernel    q_geo per (batch, head) from the chunk sums, in chunk order.
+// Everything is fp32 (exact products of the stored keys) except the log-ratio
+// sums (fp64).  The chain is the only sequential part: three small matrix-vector
+// products per chunk.
+#include <math.h>
+
+#include "gdr_device.hpp"
+#include "gdr_internal.hpp"
+#include "gdr_mfma.hpp"
+
+namespace gdr {
+namespace {
+
+constexpr int kPL = 64;       // tokens per chunk
+constexpr int kPD = 128;      // largest dk
+constexpr int kPThreads = 256;
+
+// workspace record of one (b, h, chunk), fp32 words
+constexpr int kPrT = 0;                    // [64][64] Tm (row t, column j)
+constexpr int kPrC = kPrT + kPL * kPL;     // [64] c_t
+constexpr int kPrCb = kPrC + kPL;          // [64] c_t beta_t
+constexpr int kPrBeta = kPrCb + kPL;       // [64] beta_t
+constexpr int kPrR = kPrBeta + kPL;        // [64] r_t
+constexpr int kPrP = kPrR + kPL;           // [64] P_t
+constexpr int kPrRho = kPrP + kPL;         // [64] P_n / P_{j+1} (0 past the chunk end)
+constexpr int kPrPn = kPrRho + kPL;        // P_n (slot of 64)
+constexpr int kPrD0 = kPrPn + kPL;         // [128] d at the chunk start      (chain)
+constexpr int kPrE = kPrD0 + kPD;          // [64] e_t                         (chain)
+constexpr int kPrLog = kPrE + kPL;         // fp64: sum of log loss ratios      (emit)
+constexpr int kPrWords = kPrLog + kPL;     // 4800 words = 19,200 bytes
+
+struct PcParams {
+    int B, T, H, dk, io_bf16, gate_bf16, NT;
+    float eta;
+    const void *k, *beta, *r;
+    const float *d0;
+    void *kw;
+    float *dT, *qgeo;
+    float *rec;
+};
+
+// retention gates at or below this act as full forgetting (their logarithm stays finite)
+constexpr float kRMin = 1e-30f;
+
+// keys of one chunk into LDS as fp32 (rows past the chunk end zero): every
+// 16-byte piece of the tile is requested before any is written out.  Loads are
+// unconditional (rows clamped to the chunk) so that the compiler can count them;
+// pieces past row 63 land in the sink row kPL of kf.
+template <bool BF>
+__device__ __forceinline__ void load_keys(const PcParams &p, float (*kf)[kPD + 1], long tok0, int n, int tid) {
+    constexpr int es = BF ? 2 : 4;
+    const int kpieces = p.dk * es / 16;
+    const char *kb = static_cast<const char *>(p.k);
+    u32x4 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int e = tid + kPThreads * u, t = min(e / kpieces, n - 1), pc = e % kpieces;
+        v[u] = *reinterpret_cast<const u32x4 *>(kb + (tok0 + (long)t * p.H) * p.dk * es + 16 * pc);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int e = tid + kPThreads * u, t = e / kpieces, pc = e % kpieces;
+        const int row = min(t, kPL);
+        const bool live = t < n;
+        if (BF) {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                kf[row][8 * pc + 2 * x] = live ? __uint_as_float(v[u][x] << 16) : 0.f;
+                kf[row][8 * pc + 2 * x + 1] = live ? __uint_as_float(v[u][x] & 0xffff0000u) : 0.f;
+            }
+        } else {
+#pragma unroll
+            for (int x = 0; x < 4; ++x) kf[row][4 * pc + x] = live ? __uint_as_float(v[u][x]) : 0.f;
+        }
+    }
+}
+
+// workgroup barrier that waits only for this wave's LDS operations: global loads
+// issued for the next chunk stay in flight across it (the memory clobber keeps the
+// compiler from moving memory operations across)
+__device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <bool BF>
+__global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
+    __shared__ float a[kPL + 1][kPD + 1];  // row kPL: sink of the key copy
+    __shared__ float A[kPL][kPL + 1];    // A (strictly lower)
+    __shared__ float Ti[kPL][kPL + 1];   // Tm, strictly lower part (the unit diagonal is implicit)
+    __shared__ float W[3][16][17];       // off-diagonal block sums
+    __shared__ float nk[kPL], lg[kPL + 1], cb[kPL];
+    const int tid = threadIdx.x;
+    const long blk = blockIdx.x;
+    const int bh = (int)(blk / p.NT), c = (int)(blk % p.NT);
+    const int b = bh / p.H, h = bh % p.H, dk = p.dk;
+    const int t0 = c * kPL, n = min(kPL, p.T - t0);
+    float *rec = p.rec + blk * kPrWords;
+    const long tok0 = ((long)b * p.T + t0) * p.H + h;
+
+    // this token's gates are requested together with the keys
+    float bt = 0.f, rt = 1.f;
+    if (tid < n) {
+        const long tk = tok0 + (long)tid * p.H;
+        bt = ld_elem(p.beta, tk, p.gate_bf16);
+        if (p.r) rt = ld_elem(p.r, tk, p.gate_bf16);
+    }
+    load_keys<BF>(p, a, tok0, n, tid);
+    __syncthreads();
+    {  // |k_t|^2 (4 lanes per row), then a = k^2
+        const int t = tid >> 2, part = tid & 3;
+        float s = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 32; ++ii) {
+            const int i = min(32 * part + ii, dk - 1);
+            const float term = a[t][i] * a[t][i];
+            s += 32 * part + ii < dk ? term : 0.f;
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (part == 0) nk[t] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < kPL * kPD; e += kPThreads) {
+        const int t = e / kPD, i = e % kPD;
+        if (i < dk) a[t][i] *= a[t][i];
+    }
+    if (tid < kPL) {  // one wave: coefficients and the cumulative log retention (scan)
+        const int t = tid;
+        const float ct = nk[t] > 0.f ? p.eta * bt / nk[t] : 0.f;
+        rec[kPrC + t] = ct;
+        rec[kPrCb + t] = ct * bt;
+        rec[kPrBeta + t] = bt;
+        rec[kPrR + t] = rt;
+        cb[t] = ct * bt;
+        float x = logf(fmaxf(rt, kRMin));  // inclusive prefix sum over the 64 lanes
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off);
+            if (t >= off) x += y;
+        }
+        lg[t + 1] = x;  // log P_{t+1}
+        if (t == 0) lg[0] = 0.f;
+    }
+    __syncthreads();
+    if (tid < kPL) {
+        const float ln = lg[n];
+        rec[kPrP + tid] = expf(lg[tid]);
+        rec[kPrRho + tid] = tid < n ? expf(ln - lg[tid + 1]) : 0.f;
+        if (tid == 0) rec[kPrPn] = expf(ln);
+    }
+
+    // A_{tj} = cb_t (P_t / P_{j+1}) <a_t, a_j> for j < t < n, a 4 x 4 block per thread
+    {
+        const int tb = 4 * (tid >> 4), jb = 4 * (tid & 15);
+        float g[4][4] = {};
+        if (jb <= tb + 3) {
+#pragma unroll 8
+            for (int i = 0; i < dk; ++i) {
+                float at[4], aj[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    at[e] = a[tb + e][i];
+                    aj[e] = a[jb + e][i];
+                }
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+#pragma unroll
+                    for (int y = 0; y < 4; ++y) g[x][y] = fmaf(at[x], aj[y], g[x][y]);
+            }
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x)
+#pragma unroll
+            for (int y = 0; y < 4; ++y) {
+                const int t = tb + x, j = jb + y;
+                A[t][j] = (j < t && t < n) ? cb[t] * expf(lg[t] - lg[j + 1]) * g[x][y] : 0.f;
+            }
+    }
+    __syncthreads();
+
+    // Tm = (I + A)^{-1}.  Diagonal 16 x 16 blocks: thread (block I, column j) solves
+    // (I + A_II) x = e_j by forward substitution, x in registers.
+    {
+        float x[16];
+        const int I = tid >> 4, j = tid & 15, base = 16 * I;
+        if (tid < 64) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                float v = t == j ? 1.f : 0.f;
+#pragma unroll
+                for (int s = 0; s < 16; ++s)
+                    if (s < t) v -= A[base + t][base + s] * x[s];
+                x[t] = t < j ? 0.f : v;
+            }
+        }
+        if (tid < 64) {
+#pragma unroll
+            for (int t = 0; t < 16; ++t)
+                if (t > j) Ti[base + t][base + j] = x[t];
+        }
+        __syncthreads();
+    }
+    // off-diagonal blocks, by distance dI = I - J from the diagonal:
+    //     Tm_IJ = - Tm_II * sum_{K = J}^{I - 1} A_IK Tm_KJ      (Tm_JJ's diagonal is 1)
+    // with the original A; every Tm_KJ used (K - J < dI) is final when distance dI runs.
+    auto tm = [&](int r, int c) -> float { return r == c ? 1.f : (c < r ? Ti[r][c] : 0.f); };
+    for (int dI = 1; dI < 4; ++dI) {
+        const int nb = 4 - dI;  // blocks at this distance: (J + dI, J), J < nb
+        for (int e = tid; e < nb * 256; e += kPThreads) {
+            const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + dI;
+            float v = 0.f;
+#pragma unroll
+            for (int dK = 0; dK < 3; ++dK) {
+                const int K = J + dK;
+                if (K < I) {
+#pragma unroll
+                    for (int s = 0; s < 16; ++s) v += A[16 * I + rr][16 * K + s] * tm(16 * K + s, 16 * J + cc);
+                }
+            }
+            W[J][rr][cc] = v;
+        }
+        __syncthreads();
+        for (int e = tid; e < nb * 256; e += kPThreads) {
+            const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + dI;
+            float v = 0.f;
+#pragma unroll
+            for (int s = 0; s < 16; ++s) v += tm(16 * I + rr, 16 * I + s) * W[J][s][cc];
+            Ti[16 * I + rr][16 * J + cc] = -v;
+        }
+        __syncthreads();
+    }
+    for (int e = tid; e < kPL * kPL; e += kPThreads) {
+        const int t = e / kPL, j = e % kPL;
+        rec[kPrT + e] = j < t ? Ti[t][j] : (j == t ? 1.f : 0.f);
+    }
+}
+
+template <bool BF>
+__global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
+    __shared__ float kf[kPL + 1][kPD + 1];   // a = k^2 of the chunk; row kPL: sink
+    __shared__ __attribute__((aligned(16))) float Tm[kPL][kPL + 4];  // 16-byte rows
+    __shared__ __attribute__((aligned(16))) float vc[7][kPL];         // c, cb, beta, r, P, rho, (Pn in [6][0])
+    __shared__ float zs[kPL], es[kPL], we[kPL], d[kPD];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x;
+    const int b = bh / p.H, h = bh % p.H, dk = p.dk;
+    if (tid < dk) d[tid] = p.d0 ? p.d0[(long)bh * dk + tid] : 1.f;
+
+    // register copies of the next two chunks (two sets, used alternately): keys
+    // (16-byte pieces) and the record head (Tm and the vectors: 1,136 pieces)
+    constexpr int ksz = BF ? 2 : 4;  // bytes per key element
+    const int kpieces = dk * ksz / 16;
+    u32x4 kA[8], rA[5], kB[8], rB[5];
+    // this thread's key pieces (row, 16-byte piece) are the same in every chunk
+    int prow[8], ppc[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        const int e = tid + kPThreads * u;
+        prow[u] = e / kpieces;
+        ppc[u] = e - prow[u] * kpieces;
+    }
+    auto load_chunk = [&](int c, u32x4 (&kreg)[8], u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+        const int t0 = c * kPL, n = min(kPL, p.T - t0);
+        const char *kb = static_cast<const char *>(p.k);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {  // unconditional (rows clamped): the compiler counts them
+            const int t = min(prow[u], n - 1);
+            kreg[u] = *reinterpret_cast<const u32x4 *>(kb + ((((long)b * p.T + t0 + t) * p.H + h) * dk) * ksz + 16 * ppc[u]);
+        }
+        const float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int w4 = min(tid + kPThreads * u, kPrD0 / 4 - 1);
+            rreg[u] = *reinterpret_cast<const u32x4 *>(rec + 4 * w4);
+        }
+    };
+    auto store_chunk = [&](int c, const u32x4 (&kreg)[8], const u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+        const int t0 = c * kPL, n = min(kPL, p.T - t0);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int t = prow[u], pc = ppc[u];
+            const int row = min(t, kPL);
+            const bool live = t < n;
+            if (BF) {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float k0 = live ? __uint_as_float(kreg[u][x] << 16) : 0.f;
+                    const float k1 = live ? __uint_as_float(kreg[u][x] & 0xffff0000u) : 0.f;
+                    kf[row][8 * pc + 2 * x] = k0 * k0;
+                    kf[row][8 * pc + 2 * x + 1] = k1 * k1;
+                }
+            } else {
+#pragma unroll
+                for (int x = 0; x < 4; ++x) {
+                    const float k0 = live ? __uint_as_float(kreg[u][x]) : 0.f;
+                    kf[row][4 * pc + x] = k0 * k0;
+                }
+            }
+        }
+        // the record head: Tm rows then the vector rows (one flat LDS view); the
+        // clamped duplicate pieces rewrite the last piece with its own value
+#pragma unroll
+        for (int u = 0; u < 5; ++u) {
+            const int w = 4 * min(tid + kPThreads * u, kPrD0 / 4 - 1);
+            float *dst = w < kPrC ? &Tm[w / kPL][w % kPL] : &vc[(w - kPrC) / kPL][(w - kPrC) % kPL];
+            *reinterpret_cast<f32x4 *>(dst) = __builtin_bit_cast(f32x4, rreg[u]);
+        }
+    };
+
+    // one chunk of the chain; its operands arrive in (kreg, rreg), which are then
+    // refilled with chunk c + 2
+    auto step = [&](int c, u32x4 (&kreg)[8], u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+        float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
+        lds_sync();  // the previous chunk is done with kf, Tm, vc, d
+        store_chunk(c, kreg, rreg);
+        if (c + 2 < p.NT) load_chunk(c + 2, kreg, rreg);
+        if (tid < dk) rec[kPrD0 + tid] = d[tid];
+        lds_sync();
+        // z_t = c_t - cb_t P_t <a_t, d_0>   (4 lanes per token)
+        {
+            const int t = tid >> 2, part = tid & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int ii = 0; ii < 32; ++ii) {  // unconditional loads (clamped), masked terms
+                const int i = min(32 * part + ii, dk - 1);
+                const float term = kf[t][i] * d[i];
+                sum += 32 * part + ii < dk ? term : 0.f;
+            }
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if (part == 0) zs[t] = vc[0][t] - vc[1][t] * vc[4][t] * sum;
+        }
+        lds_sync();
+        // e = Tm z
+        {
+            const int t = tid >> 2, part = tid & 3;
+            float sum = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj) {
+                const int j = 16 * part + jj;  // strictly lower part of Tm (its diagonal is 1)
+                sum = fmaf(j < t ? Tm[t][j] : 0.f, zs[j], sum);
+            }
+            sum += __shfl_xor(sum, 1);
+            sum += __shfl_xor(sum, 2);
+            if (part == 0) {
+                es[t] = zs[t] + sum;
+                we[t] = vc[5][t] * (zs[t] + sum);
+                rec[kPrE + t] = zs[t] + sum;
+            }
+        }
+        lds_sync();
+        // d_n = P_n d_0 + sum_j rho_j e_j a_j   (one key channel per thread)
+        if (tid < dk) {
+            float acc[4] = {vc[6][0] * d[tid], 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < kPL; ++j) acc[j & 3] = fmaf(we[j], kf[j][tid], acc[j & 3]);
+            d[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        }
+    };
+
+    if (p.NT > 0) load_chunk(0, kA, rA);
+    if (p.NT > 1) load_chunk(1, kB, rB);
+    for (int c = 0; c < p.NT; c += 2) {
+        step(c, kA, rA);
+        if (c + 1 < p.NT) step(c + 1, kB, rB);
+    }
+    __syncthreads();
+    if (p.dT && tid < dk) p.dT[(long)bh * dk + tid] = d[tid];
+}
+
+template <bool BF>
+__global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
+    __shared__ float kf[kPL + 1][kPD + 1];  // row kPL: sink of the key copy
+    __shared__ float kw[kPL][kPD + 1];
+    __shared__ float vr[kPL], ve[kPL], vb[kPL];
+    __shared__ double red[kPThreads / 64];
+    const int tid = threadIdx.x;
+    const long blk = blockIdx.x;
+    const int bh = (int)(blk / p.NT), c = (int)(blk % p.NT);
+    const int b = bh / p.H, h = bh % p.H, dk = p.dk;
+    const int t0 = c * kPL, n = min(kPL, p.T - t0);
+    float *rec = p.rec + blk * kPrWords;
+    const long tok0 = ((long)b * p.T + t0) * p.H + h;
+    load_keys<BF>(p, kf, tok0, n, tid);
+    if (tid < kPL) {
+        vr[tid] = rec[kPrR + tid];
+        ve[tid] = rec[kPrE + tid];
+        vb[tid] = rec[kPrBeta + tid];
+    }
+    __syncthreads();
+    // d through the chunk, one key channel per thread; kw_t = d_t (.) k_t
+    if (tid < dk) {
+        float di = rec[kPrD0 + tid];
+        float kc[kPL];
+#pragma unroll
+        for (int t = 0; t < kPL; ++t) kc[t] = kf[t][tid];
+#pragma unroll
+        for (int t = 0; t < kPL; ++t) {
+            if (t < n) {
+                kw[t][tid] = di * kc[t];
+                di = fmaf(vr[t], di, ve[t] * kc[t] * kc[t]);
+            }
+        }
+    }
+    __syncthreads();
+    // u_t = 1 - beta_t <kw_t, k_t>; the chunk's sum of log u_t^2
+    double logsum = 0.0;
+    {
+        const int t = tid >> 2, part = tid & 3;
+        float s = 0.f;
+#pragma unroll
+        for (int ii = 0; ii < 32; ++ii) {
+            const int i = min(32 * part + ii, dk - 1);
+            const float term = kw[t][i] * kf[t][i];
+            s += 32 * part + ii < dk ? term : 0.f;
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (part == 0 && t < n) {
+            const double u = 1.0 - (double)vb[t] * (double)s;
+            logsum = log(u * u);
+        }
+    }
+    for (int off = 32; off > 0; off >>= 1) logsum += __shfl_xor(logsum, off);
+    if ((tid & 63) == 0) red[tid >> 6] = logsum;
+    // write keys out as rows (16 bytes per piece)
+    {
+        constexpr int es = BF ? 2 : 4;
+        const int opieces = dk * es / 16;
+        for (int e = tid; e < n * opieces; e += kPThreads) {
+            const int t = e / opieces, pc = e % opieces;
+            char *dst = static_cast<char *>(p.kw) + (tok0 + (long)t * p.H) * dk * es + 16 * pc;
+            if (BF) {
+                uint32_t w[4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x)
+                    w[x] = (uint32_t)f32_to_bf16(kw[t][8 * pc + 2 * x]) |
+                           ((uint32_t)f32_to_bf16(kw[t][8 * pc + 2 * x + 1]) << 16);
+                *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+                *reinterpret_cast<u32x4 *>(dst) =
+                    u32x4{__float_as_uint(kw[t][4 * pc]), __float_as_uint(kw[t][4 * pc + 1]),
+                          __float_as_uint(kw[t][4 * pc + 2]), __float_as_uint(kw[t][4 * pc + 3])};
+            }
+        }
+    }
+    __syncthreads();
+    if (tid == 0) {
+        double tot = 0.0;
+        for (int w = 0; w < kPThreads / 64; ++w) tot += red[w];
+        *reinterpret_cast<double *>(rec + kPrLog) = tot;
+    }
+}
+
+// q_geo = exp(sum of the chunk sums / T): one workgroup per (batch, head); thread
+// i sums chunks i, i + 256, ... and the 256 partial sums are added in a fixed tree
+// (the same order on every run)
+__global__ void __launch_bounds__(kPThreads) osdn_qgeo_kernel(PcParams p) {
+    __shared__ double part[kPThreads];
+    const int bh = blockIdx.x, tid = threadIdx.x;
+    double tot = 0.0;
+    for (int c = tid; c < p.NT; c += kPThreads)
+        tot += *reinterpret_cast<const double *>(p.rec + ((long)bh * p.NT + c) * kPrWords + kPrLog);
+    part[tid] = tot;
+    __syncthreads();
+    for (int off = kPThreads / 2; off > 0; off >>= 1) {
+        if (tid < off) part[tid] += part[tid + off];
+        __syncthreads();
+    }
+    if (tid == 0) p.qgeo[bh] = p.T > 0 ? (float)exp(part[0] / p.T) : 1.f;
+}
+
+}  // namespace
+
+size_t osdn_precond_workspace(int B, int T, int H) {
+    const long NT = (T + kPL - 1) / kPL;
+    return (size_t)B * H * NT * kPrWords * sizeof(float);
+}
+
+hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
+                               const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
+                               void *ws, hipStream_t st) {
+    const long nbh = (long)B * H;
+    if (nbh == 0) return hipSuccess;
+    PcParams p;
+    p.B = B; p.T = T; p.H = H; p.dk = dk; p.io_bf16 = io_bf16; p.gate_bf16 = gate_bf16;
+    p.NT = (T + kPL - 1) / kPL;
+    p.eta = eta;
+    p.k = k; p.beta = beta; p.r = r; p.d0 = d0; p.kw = kw; p.dT = dT; p.qgeo = qgeo;
+    p.rec = static_cast<float *>(ws);
+    void *args[] = {&p};
+    hipError_t e;
+    if (p.NT > 0) {
+        e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_chunk_kernel<true>)
+                                    : reinterpret_cast<const void *>(&osdn_chunk_kernel<false>),
+                            dim3((unsigned)(nbh * p.NT)),
+                            dim3(kPThreads), args, 0, st);
+        if (e != hipSuccess) return e;
+    }
+    e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_chain_kernel<true>)
+                                : reinterpret_cast<const void *>(&osdn_chain_kernel<false>),
+                        dim3((unsigned)nbh), dim3(kPThreads),
+                        args, 0, st);
+    if (e != hipSuccess) return e;
+    if (p.NT > 0) {
+        e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_emit_kernel<true>)
+                                    : reinterpret_cast<const void *>(&osdn_emit_kernel<false>),
+                            dim3((unsigned)(nbh * p.NT)),
+                            dim3(kPThreads), args, 0, st);
+        if (e != hipSuccess) return e;
+    }
+    if (qgeo)
+        e = hipLaunchKernel(reinterpret_cast<const void *>(&osdn_qgeo_kernel), dim3((unsigned)nbh),
+                            dim3(kPThreads), args, 0, st);
+    return e;
+}
+
+}  // namespace gdr

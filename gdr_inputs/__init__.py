@@ -276,6 +276,13 @@ def make_cache_readout(w: CacheReadout) -> dict:
     return dict(q=q, ckpt=ckpt, gates=gates, o_in=o_in)
 
 
+def make_retention(w: Prefill, mu: float = 4.0, sd: float = 1.0) -> np.ndarray:
+    """Retention gate of the OSDN preconditioner (APF), r = sigmoid(N(mu, sd)) per
+    (b, t, h), stored in the workload's gate dtype; drawn from its own stream."""
+    rng = np.random.default_rng(w.seed + 100000)
+    return store(_sigmoid(rng.normal(mu, sd, (w.B, w.T, w.H))), w.gate)
+
+
 def prefill_f64(w: Prefill, x: dict) -> dict:
     """The exact fp64 values of a prefill batch (what the oracle reads)."""
     out = {}

@@ -206,6 +206,33 @@ int gdr_mc_readout(const gdr_desc *desc, const void *q, const float *ckpt, int32
                    int32_t seg_len, const float *gates, const void *o_in, void *o_out,
                    void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * OSDN phase 1: the preconditioner scan that produces the write keys of the
+ * chunked pass [OSDN page, section 2.2 (hypergradient surrogate, two phases),
+ * section 2.3 (retention gate of the preconditioner)].  For every (b, h), with
+ * the diagonal preconditioner d (d0, or all ones when d0 is NULL) and per token t
+ *
+ *     k_w[t] = d_t (.) k[t]
+ *     d_{t+1} = r[t] d_t + eta beta[t] (1 - beta[t] <d_t, k[t]^2>) k[t]^2 / |k[t]|^2
+ *
+ * (online gradient descent on the surrogate; r == 1 is plain OSDN; a zero key
+ * leaves d scaled by r only).  q_geo[b, h] = exp(mean_t log (1 - beta[t] <d_t,
+ * k[t]^2>)^2), the geometric mean of phase 2's per-token loss ratio.
+ *
+ *   k      [B, T, H, dk] io_dtype (required); k_w [B, T, H, dk] io_dtype output
+ *   beta   [B, T, H] gate_dtype (required; desc->beta_mode must be GDR_BETA_SCALAR)
+ *   r      [B, T, H] gate_dtype retention in [0, 1], or NULL for 1 (values below
+ *          1e-30 act as 0)
+ *   d0     [B, H, dk] fp32 or NULL;  dT [B, H, dk] fp32 final preconditioner or NULL
+ *   qgeo   [B, H] fp32 or NULL (1 when T == 0)
+ *   workspace at least gdr_osdn_precond_workspace_size() bytes
+ * dk: multiple of 8 in [8, 128].  desc->dv, chunk and alpha_mode are not used.
+ */
+size_t gdr_osdn_precond_workspace_size(const gdr_desc *desc);
+int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, const void *r, float eta,
+                     const float *d0, void *k_w, float *dT, float *qgeo, void *workspace,
+                     size_t workspace_bytes, void *stream);
+
 /* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
  * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */
 int gdr_chunk_fwd_path(const gdr_desc *desc);

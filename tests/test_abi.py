@@ -207,3 +207,21 @@ def test_mc_readout_validation(g):
     assert call(d, oi=FakePtr(oo.addr + 256)) == g.GDR_EINVAL          # partial overlap of o_in and o_out
     assert call(d, ws=FakePtr(ck.addr)) == g.GDR_EINVAL                # workspace overlaps the caches
     assert call(_desc(g, B=0)) == g.GDR_OK                             # empty batch: nothing to do
+
+
+def test_osdn_precond_validation(g):
+    d = _desc(g, T=256)
+    k, b, r, kw, dT, qg, ws = _ptrs(n=7, step=0x10000000)
+    need = g.gdr_osdn_precond_workspace_size(d)
+    assert need == 2 * 3 * 4 * 19200
+    call = lambda desc, **kw_: g.gdr_osdn_precond(desc, kw_.get("k", k), kw_.get("b", b), kw_.get("r", r), 1.0,
+                                                 None, kw_.get("kw", kw), kw_.get("dT", dT), kw_.get("qg", qg),
+                                                 kw_.get("ws", ws), kw_.get("wb", need), 0)
+    assert call(_desc(g, T=256, beta_mode=g.GDR_BETA_SHARED)) == g.GDR_EINVAL  # scalar write strength only
+    assert call(_desc(g, T=256, dk=136)) == g.GDR_EUNSUPPORTED
+    assert call(d, k=None) == g.GDR_EINVAL
+    assert call(d, kw=FakePtr(k.addr + 512)) == g.GDR_EINVAL            # output overlaps the keys
+    assert call(d, ws=None) == g.GDR_EWORKSPACE
+    assert call(d, wb=need - 16) == g.GDR_EWORKSPACE
+    assert call(d, ws=FakePtr(b.addr)) == g.GDR_EINVAL                  # workspace overlaps an input
+    assert call(_desc(g, B=0)) == g.GDR_OK
