@@ -22,6 +22,8 @@ Layouts (row-major):
            S0: [B, H, dk, dv] fp32 or None
   decode   per-step tensors gain a leading step axis: q [steps, B, H, dk], ...
            S: [B, H, dk, dv] fp32
+  sparse memory  ks, qs: [B, T, H, 2, n] fp32 half scores, v: [B, T, H, dv],
+           alpha, beta: [B, T, H], M0: [B, H, n * n, dv] fp32
   cache read-out  q: [B, T, H, dk] bf16, ckpt: [B, H, N, dk, dv] fp32,
            gates: [B, T, H, N] fp32 or None, o_in: [B, T, H, dv] bf16 or None
 """
@@ -195,6 +197,39 @@ DECODE_B512 = Decode("decode_bf16_B512H16d128", B=512, H=16, dk=128, dv=128, ste
 DECODE_DMEM_R8 = Decode("decode_deltamem_bf16_B8192H1r8", B=8192, H=1, dk=8, dv=8, steps=256,
                         seed=8406)
 
+@dataclasses.dataclass(frozen=True)
+class SparseMemory:
+    """A Sparse Delta Memory batch: per (b, h) a table of n * n slots x dv, W slots
+    written and R read per token."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    n: int                      # half-score length; N = n * n slots
+    dv: int
+    W: int
+    R: int
+    io: str = BF16              # v, o
+    gate: str = F32             # alpha, beta
+    alpha_mu: float = -4.0      # alpha = sigmoid(-N(mu, sd)), as the dense workloads
+    alpha_sd: float = 1.0
+    m0_std: float = 0.02        # M0 ~ N(0, m0_std) (the learned initial table)
+    seed: int = 0
+
+    @property
+    def N(self) -> int:
+        return self.n * self.n
+
+    def scaled(self, **kw) -> "SparseMemory":
+        return dataclasses.replace(self, **kw)
+
+
+# Sparse Delta Memory at the headline batch's shape: 65,536 slots of 128 values per
+# (b, h) (2 GiB of tables), W = R = 128 (the dense query width)
+SDM_B4H16 = SparseMemory("sdm_bf16_B4H16T4096N65536dv128W128R128", B=4, T=4096, H=16, n=256, dv=128, W=128,
+                         R=128, seed=8408)
+
 # read-out of the long-context batch's segment caches: 16 segments of 4096 tokens
 MC_LONG_GRM = CacheReadout("mc_grm_bf16_B1H32T65536d128seg4096", B=1, T=65536, H=32, dk=128, dv=128,
                            seg=4096, gate_kind="dense", seed=8407)
@@ -250,6 +285,21 @@ def make_decode(w: Decode) -> dict:
         beta_v = store(_sigmoid(rng.standard_normal((n, B, H, dv))), w.gate)
     S = rng.normal(0.0, w.s_std, (B, H, dk, dv)).astype(np.float32)
     return dict(q=q, k=k, k_w=None, v=v, alpha=alpha, beta_k=beta_k, beta_v=beta_v, S=S)
+
+
+def make_sparse_memory(w: SparseMemory) -> dict:
+    """Draw an SDM batch.  Draw order: key half scores, query half scores, v, alpha,
+    beta, M0.  Half scores ~ N(0, 1) fp32 (stand-ins for the projected key / query
+    halves against their sub-key sets)."""
+    rng = np.random.default_rng(w.seed)
+    B, T, H, n, dv = w.B, w.T, w.H, w.n, w.dv
+    ks = rng.standard_normal((B, T, H, 2, n)).astype(np.float32)
+    qs = rng.standard_normal((B, T, H, 2, n)).astype(np.float32)
+    v = store(rng.standard_normal((B, T, H, dv)), w.io)
+    alpha = store(_sigmoid(-rng.normal(w.alpha_mu, w.alpha_sd, (B, T, H))), w.gate)
+    beta = store(_sigmoid(rng.standard_normal((B, T, H))), w.gate)
+    M0 = rng.normal(0.0, w.m0_std, (B, H, n * n, dv)).astype(np.float32)
+    return dict(ks=ks, qs=qs, v=v, alpha=alpha, beta=beta, M0=M0)
 
 
 def make_cache_readout(w: CacheReadout) -> dict:

@@ -13,6 +13,8 @@ Contents:
     oracle (and the chunked algebra) against each other.
   * ``osdn_precond``: OSDN phase 1, the preconditioner scan over the key stream
     (write keys, final preconditioner, geometric-mean loss ratio q_geo).
+  * ``sdm``: Sparse Delta Memory -- product-key slot selection (all slot scores
+    ranked directly), per-slot gated delta writes and the weighted sparse read.
   * ``memcache``: Memory Caching -- the state after every segment (the sequential
     run, one segment at a time) and the residual / gated read-out over those
     cached states, plain fp64.
