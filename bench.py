@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip",
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip",
                   "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
 
 
@@ -201,6 +201,59 @@ def bench_osdn_precond(g, gi, stream, reps):
                          "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
 
 
+def sdm_bytes(w, gi):
+    """Algorithmic HBM bytes of one Sparse Delta Memory call: per (token, head) the two
+    half-score vectors of the key and of the query read (fp32), the selected slots and
+    weights written then read back, W rows gathered and scattered and R rows gathered
+    (fp32, dv values each), v read and o written, alpha and beta read."""
+    es = 2 if w.io == gi.BF16 else 4
+    per = (2 * 2 * w.n * 4 + 2 * (w.W + w.R) * 8 + (2 * w.W + w.R) * w.dv * 4 + 2 * w.dv * es + 2 * 4)
+    return w.B * w.T * w.H * per
+
+
+def bench_sdm(g, gi, stream, reps):
+    """Sparse Delta Memory at B=4 H=16 T=4096, 65,536 slots x 128 per head, W = R = 128,
+    inputs and the 2 GiB of tables resident; events on the launch stream around each call
+    (selection + table pass; the table evolves from call to call, the work does not)."""
+    import torch
+
+    w = gi.SDM_B4H16
+    x = gi.make_sparse_memory(w)
+    ks, qs = gi.to_torch(x["ks"], gi.F32), gi.to_torch(x["qs"], gi.F32)
+    v = gi.to_torch(x["v"], w.io)
+    alpha, beta = gi.to_torch(x["alpha"], w.gate), gi.to_torch(x["beta"], w.gate)
+    M = gi.to_torch(x["M0"], gi.F32)
+    del x
+    o = torch.empty_like(v)
+    desc = g.Desc(B=w.B, T=w.T, H=w.H, dk=w.dv, dv=w.dv, chunk=64, io_dtype=g.GDR_BF16, gate_dtype=g.GDR_F32,
+                  alpha_mode=0, beta_mode=0, flags=0)
+    need = g.gdr_sdm_workspace_size(desc, w.n, w.W, w.R)
+    ws = torch.empty(need, dtype=torch.uint8, device=v.device)
+
+    def call():
+        rc = g.gdr_sdm_fwd(desc, w.n, w.W, w.R, ks, qs, v, alpha, beta, M, o, None, None, ws, need, stream)
+        if rc != g.GDR_OK:
+            raise g.GdrError(rc, "gdr_sdm_fwd")
+
+    call()
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        call()
+        b.record(stream)
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = sorted(times)[len(times) // 2]
+    nbytes = sdm_bytes(w, gi)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
+            "algorithmic_bytes": nbytes,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -357,6 +410,7 @@ def main():
         out["decode"] = dec
         out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps)
         out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps)
+        out["sdm"] = bench_sdm(g, gi, stream, args.mc_reps)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)

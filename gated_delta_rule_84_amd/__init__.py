@@ -71,10 +71,15 @@ _lib.gdr_osdn_precond_workspace_size.argtypes = [_dp]
 _lib.gdr_osdn_precond_workspace_size.restype = ctypes.c_size_t
 _lib.gdr_osdn_precond.argtypes = [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
 _lib.gdr_osdn_precond.restype = ctypes.c_int
+_lib.gdr_sdm_workspace_size.argtypes = [_dp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
+_lib.gdr_sdm_workspace_size.restype = ctypes.c_size_t
+_lib.gdr_sdm_fwd.argtypes = [_dp] + [ctypes.c_int32] * 3 + [_vp] * 10 + [ctypes.c_size_t, _vp]
+_lib.gdr_sdm_fwd.restype = ctypes.c_int
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
-            "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond")
+            "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond",
+            "gdr_sdm_workspace_size", "gdr_sdm_fwd")
 
 
 class GdrError(RuntimeError):
@@ -146,6 +151,17 @@ def gdr_osdn_precond(desc: Desc, k, beta, r, eta: float, d0, k_w, dT, qgeo, work
                      stream=None) -> int:
     return int(_lib.gdr_osdn_precond(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(k_w),
                                      _ptr(dT), _ptr(qgeo), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdr_sdm_workspace_size(desc: Desc, n: int, W: int, R: int) -> int:
+    return int(_lib.gdr_sdm_workspace_size(ctypes.byref(desc), int(n), int(W), int(R)))
+
+
+def gdr_sdm_fwd(desc: Desc, n: int, W: int, R: int, ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace,
+                workspace_bytes: int, stream=None) -> int:
+    return int(_lib.gdr_sdm_fwd(ctypes.byref(desc), int(n), int(W), int(R), _ptr(ks), _ptr(qs), _ptr(v), _ptr(alpha),
+                                _ptr(beta), _ptr(M), _ptr(o), _ptr(w_slots), _ptr(r_slots), _ptr(workspace),
+                                int(workspace_bytes), _stream(stream)))
 
 
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
@@ -256,6 +272,27 @@ def osdn_precond(k, beta, eta, *, r=None, d0=None, workspace=None, stream=None):
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_osdn_precond")
     return kw, dT, qg
+
+
+def sdm_fwd(M, ks, qs, v, alpha, beta, W, R, *, want_slots=False, workspace=None, stream=None):
+    """Sparse Delta Memory over T tokens.  M [B, H, n * n, dv] fp32 is updated in place;
+    ks, qs [B, T, H, 2, n] fp32; v [B, T, H, dv].  Returns o (and the selected write /
+    read slots when want_slots)."""
+    B, T, H, _, n = ks.shape
+    dv = v.shape[-1]
+    desc = Desc(B=B, T=T, H=H, dk=dv, dv=dv, chunk=64, io_dtype=_dtype_code(v), gate_dtype=_dtype_code(alpha),
+                alpha_mode=0, beta_mode=0, flags=0)
+    o = torch.empty_like(v)
+    ws_ = ((torch.empty((B, T, H, W), dtype=torch.int32, device=v.device),
+            torch.empty((B, T, H, R), dtype=torch.int32, device=v.device)) if want_slots else (None, None))
+    need = gdr_sdm_workspace_size(desc, n, W, R)
+    if workspace is None or workspace.numel() * workspace.element_size() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
+    rc = gdr_sdm_fwd(desc, n, W, R, ks, qs, v, alpha, beta, M, o, ws_[0], ws_[1], workspace,
+                     workspace.numel() * workspace.element_size(), stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_sdm_fwd")
+    return (o, ws_[0], ws_[1]) if want_slots else o
 
 
 def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0, stream=None):

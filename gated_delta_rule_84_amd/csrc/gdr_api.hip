@@ -293,6 +293,50 @@ int gdr_osdn_precond(const gdr_desc *d, const void *k, const void *beta, const v
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 
+size_t gdr_sdm_workspace_size(const gdr_desc *d, int32_t n, int32_t W, int32_t R) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0 || W < 1 || R < 1 || n < 1) return 0;
+    return sdm_workspace(d->B, d->T, d->H, W, R);
+}
+
+int gdr_sdm_fwd(const gdr_desc *d, int32_t n, int32_t W, int32_t R, const float *ks, const float *qs, const void *v,
+                const void *alpha, const void *beta, float *M, void *o, int32_t *w_slots, int32_t *r_slots,
+                void *workspace, size_t workspace_bytes, void *stream) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
+    if (n < 1 || W < 1 || R < 1) return GDR_EINVAL;
+    if (d->dv != 128 || n > 1024 || W > 128 || R > 128 || W > n * n || R > n * n) return GDR_EUNSUPPORTED;
+    const long long nbh = (long long)d->B * d->H, ntok = nbh * d->T;
+    if (nbh > 0x7fffffffLL || ntok * 2 > 0x7fffffffLL) return GDR_EUNSUPPORTED;
+    if (ntok == 0) return GDR_OK;
+    const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;
+    const size_t nsc = (size_t)ntok * 2 * n * sizeof(float), nv = (size_t)ntok * 128 * es, ng = (size_t)ntok * gs;
+    const size_t nm = (size_t)nbh * n * n * 128 * sizeof(float);
+    if (!ks || !qs || !v || !alpha || !beta || !M || !o) return GDR_EINVAL;
+    if (!aligned16(M) || !aligned_to(ks, 4) || !aligned_to(qs, 4) || !aligned_to(v, es) || !aligned_to(o, es))
+        return GDR_EINVAL;
+    if (!aligned_to(alpha, gs) || !aligned_to(beta, gs)) return GDR_EINVAL;
+    if ((w_slots && !aligned_to(w_slots, 4)) || (r_slots && !aligned_to(r_slots, 4))) return GDR_EINVAL;
+    const size_t wneed = sdm_workspace(d->B, d->T, d->H, W, R);
+    if (!workspace || workspace_bytes < wneed || !aligned16(workspace)) return GDR_EWORKSPACE;
+    {
+        const void *ins[] = {ks, qs, v, alpha, beta};
+        const size_t il[] = {nsc, nsc, nv, ng, ng};
+        const void *outs[] = {M, o, w_slots, r_slots, workspace};
+        const size_t ol[] = {nm, nv, (size_t)ntok * W * 4, (size_t)ntok * R * 4, wneed};
+        for (int i = 0; i < 5; ++i) {
+            for (int j = 0; j < 5; ++j)
+                if (overlaps(outs[i], ol[i], ins[j], il[j])) return GDR_EINVAL;
+            for (int j = i + 1; j < 5; ++j)
+                if (overlaps(outs[i], ol[i], outs[j], ol[j])) return GDR_EINVAL;
+        }
+    }
+    const hipError_t e = launch_sdm(d->B, d->T, d->H, n, W, R, d->io_dtype == GDR_BF16, d->gate_dtype == GDR_BF16,
+                                    ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace,
+                                    static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
 int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
                     const void *alpha, const void *beta_k, const void *beta_v, float *S, void *o,
                     void *stream) {

@@ -51,6 +51,10 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t s);
 hipError_t launch_state_copy(const float *S0, float *ST, long n, hipStream_t s);
 size_t mc_readout_workspace(int B, int H, int N);
 size_t osdn_precond_workspace(int B, int T, int H);
+size_t sdm_workspace(int B, int T, int H, int W, int R);
+hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
+                      const float *qs, const void *v, const void *alpha, const void *beta, float *M, void *o,
+                      int32_t *wslots, int32_t *rslots, void *ws, hipStream_t s);
 hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
                                const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
                                void *ws, hipStream_t s);

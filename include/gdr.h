@@ -233,6 +233,35 @@ int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, cons
                      const float *d0, void *k_w, float *dT, float *qgeo, void *workspace,
                      size_t workspace_bytes, void *stream);
 
+/*
+ * Sparse Delta Memory [Resumo Técnico: Sparse Delta Memory (SDM), Mecanismo Central
+ * items 1-4]: per (b, h) an explicit table M of N = n * n slots x dv, read and
+ * written sparsely.  For every token t in order, with the slot score of
+ * i = a * n + b equal to s1[a] + s2[b] (fp32) from two half-score vectors:
+ *   - the W best slots by the key scores ks[t] are written:
+ *       M[i] <- alpha[t] M[i] + beta[t] w_i (v[t] - alpha[t] M[i]),  w = softmax of
+ *     their scores; every other slot is left as it is;
+ *   - o[t] = sum_r w'_r M[i_r] over the R best slots by the query scores qs[t]
+ *     (softmax weights), read after the write.
+ * Ranking: higher score first, equal scores by lower slot index.  Selection uses
+ * topk(s1 (+) s2) = topk(topk(s1) (+) topk(s2)).
+ *
+ *   ks, qs    [B, T, H, 2, n] fp32 half scores (required)
+ *   v         [B, T, H, dv] io_dtype; o [B, T, H, dv] io_dtype output
+ *   alpha, beta [B, T, H] gate_dtype
+ *   M         [B, H, n * n, dv] fp32, the initial table (e.g. a learned M_0) on entry,
+ *             the final table on return (updated in place)
+ *   w_slots, r_slots [B, T, H, W] / [B, T, H, R] int32 outputs (selected slots, best
+ *             first) or NULL
+ *   workspace at least gdr_sdm_workspace_size() bytes
+ * Supported: dv == 128, 1 <= n <= 1024, 1 <= W, R <= min(128, n * n) (else
+ * GDR_EUNSUPPORTED).  desc->dk, chunk, alpha_mode and beta_mode are not used.
+ */
+size_t gdr_sdm_workspace_size(const gdr_desc *desc, int32_t n, int32_t W, int32_t R);
+int gdr_sdm_fwd(const gdr_desc *desc, int32_t n, int32_t W, int32_t R, const float *ks, const float *qs,
+                const void *v, const void *alpha, const void *beta, float *M, void *o, int32_t *w_slots,
+                int32_t *r_slots, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
  * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */
 int gdr_chunk_fwd_path(const gdr_desc *desc);

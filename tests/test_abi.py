@@ -225,3 +225,26 @@ def test_osdn_precond_validation(g):
     assert call(d, wb=need - 16) == g.GDR_EWORKSPACE
     assert call(d, ws=FakePtr(b.addr)) == g.GDR_EINVAL                  # workspace overlaps an input
     assert call(_desc(g, B=0)) == g.GDR_OK
+
+
+def test_sdm_validation(g):
+    d = _desc(g, T=50)
+    ks, qs, v, a, b, M, o, ws_, rs_, ws = _ptrs(n=10, step=0x10000000)
+    need = g.gdr_sdm_workspace_size(d, 256, 128, 64)
+    assert need == 2 * 50 * 3 * (128 + 64) * 8
+    call = lambda desc, n=256, W=128, R=64, **kw_: g.gdr_sdm_fwd(
+        desc, n, W, R, kw_.get("ks", ks), kw_.get("qs", qs), v, a, b, kw_.get("M", M), kw_.get("o", o),
+        kw_.get("wsl", ws_), rs_, kw_.get("ws", ws), kw_.get("wb", need), 0)
+    assert call(_desc(g, T=50, dv=64)) == g.GDR_EUNSUPPORTED             # rows of 128 values only
+    assert call(d, n=1025) == g.GDR_EUNSUPPORTED
+    assert call(d, W=129) == g.GDR_EUNSUPPORTED
+    assert call(d, n=8, R=65) == g.GDR_EUNSUPPORTED                      # more slots than the table holds
+    assert call(d, W=0) == g.GDR_EINVAL
+    assert call(d, ks=None) == g.GDR_EINVAL
+    assert call(d, M=FakePtr(M.addr + 2)) == g.GDR_EINVAL                # table must be 16-byte aligned
+    assert call(d, o=FakePtr(v.addr + 256)) == g.GDR_EINVAL              # output overlaps v
+    assert call(d, wsl=FakePtr(M.addr + 64)) == g.GDR_EINVAL             # slot output inside the table
+    assert call(d, ws=None) == g.GDR_EWORKSPACE
+    assert call(d, wb=need - 8) == g.GDR_EWORKSPACE
+    assert call(_desc(g, B=0)) == g.GDR_OK                               # nothing to do
+    assert call(_desc(g, T=50, io_dtype=5)) == g.GDR_EINVAL
