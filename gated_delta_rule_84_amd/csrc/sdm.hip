@@ -18,11 +18,11 @@
 //                      topk(s1 (+) s2) = topk(topk(s1) (+) topk(s2)) [same page, item 2].
 //                      Selection does not depend on the table, so every token runs
 //                      in parallel.
-//   sdm_table_kernel   one workgroup per (batch, head), tokens in order: the W rows are
-//                      gathered, updated and scattered; after a barrier the read rows of
-//                      this token and the write rows of the next token are gathered
-//                      together (both see this token's writes), so each token waits on
-//                      one memory round trip.  HBM bound: 3 x k x dv x 4 bytes per token.
+//   sdm_table_kernel   one workgroup per (batch, head, 32 columns), tokens in order: the
+//                      W rows are gathered, updated and scattered, the R rows gathered
+//                      and summed; the next token's rows are gathered while this one is
+//                      processed, with rows written in between forwarded from LDS.
+//                      HBM bound: (2 W + R) x dv x 4 bytes per token.
 #include <math.h>
 #include <stdint.h>
 
@@ -47,8 +47,10 @@ struct SdmParams {
     const void *v, *alpha, *beta;
     float *M;                   // [B, H, n * n, dv]
     void *o;
-    int32_t *widx, *ridx;       // [B, T, H, W], [B, T, H, R]
+    int32_t *widx, *ridx;       // [B, T, H, Wp], [B, T, H, Rp]: padded to a multiple of 4
     float *wwt, *rwt;
+    int Wp, Rp;
+    int32_t *uw, *ur;           // caller's slot outputs [B, T, H, W] / [B, T, H, R] or null
 };
 
 // Order-preserving integer key of a (sanitised, non-NaN) float: unsigned order ==
@@ -349,92 +351,276 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
     float part = 0.f;
     for (int e = lane; e < k; e += 64) part += expf(w.sv[e] - mx);
     const float tot = wave_fsum(part);
-    int32_t *oi = (which ? p.ridx : p.widx) + tk * k;
-    float *ow = (which ? p.rwt : p.wwt) + tk * k;
-    for (int e = lane; e < k; e += 64) {
-        oi[e] = w.ss[e];
-        ow[e] = expf(w.sv[e] - mx) / tot;
+    const int kp = which ? p.Rp : p.Wp;
+    int32_t *oi = (which ? p.ridx : p.widx) + tk * kp;
+    float *ow = (which ? p.rwt : p.wwt) + tk * kp;
+    int32_t *ou = which ? p.ur : p.uw;
+    for (int e = lane; e < kp; e += 64) {       // padding: a valid slot and weight 0
+        oi[e] = w.ss[min(e, k - 1)];
+        ow[e] = e < k ? expf(w.sv[e] - mx) / tot : 0.f;
+        if (ou && e < k) ou[tk * k + e] = w.ss[e];
     }
 }
 
 // ---------------------------------------------------------------------------
 // table pass
 // ---------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) sdm_table_kernel(SdmParams p) {
-    __shared__ float part[8][kSdmDv];
-    __shared__ float vv[kSdmDv];
-    const int tid = threadIdx.x;
-    const int bh = blockIdx.x, b = bh / p.H, h = bh % p.H;
-    const long N = (long)p.n * p.n;
-    float *Mh = p.M + (long)bh * N * kSdmDv;
-    // write rows: thread -> (row tid / 2, 64 columns); read rows: thread -> (column
-    // quad tid % 32, rows tid / 32 + 8 r)
-    const int wrow = tid >> 1, wcol = 64 * (tid & 1);
-    const int rq = tid & 31, rg = tid >> 5;
-    auto tok = [&](int t) -> long { return ((long)b * p.T + t) * p.H + h; };
-    f32x4 wreg[16];
-    int wsl = 0;          // this thread's write slot of the current token
-    float wc = 0.f;       // its weight
-    auto gather_write = [&](int t) __attribute__((always_inline)) {
-        if (wrow < p.W) {
-            wsl = p.widx[tok(t) * p.W + wrow];
-            wc = p.wwt[tok(t) * p.W + wrow];
-            const float *src = Mh + (long)wsl * kSdmDv + wcol;
+// One workgroup per (batch, head, group of 32 columns): the update and the read-out of a
+// column touch no other column, so the four column groups of a head run independently.
+// Thread (rg = tid / 8, q = tid % 8) holds columns 4q..4q+3 of the group for rows
+// rg + 32 j (j < 4) of the token's write list and of its read list.
+//
+// Tokens are software-pipelined one deep: the rows of token t + 1 are gathered while
+// token t is processed, so they can miss token t's writes (still in flight).  Those are
+// forwarded from LDS: token t's written rows are kept there with a small hash of their
+// slots, and every gathered row of token t + 1 is looked up in it.  Stores of token t - 1
+// are complete before token t + 1's gathers are issued (each wave waits for its own
+// stores, then the workgroup barrier), so one token of forwarding suffices, and each
+// token costs one memory round trip.  Reads of token t see token t's own writes the same
+// way (lookup after the update).
+constexpr int kSdmCols = 32;                 // columns per workgroup
+constexpr int kSdmGroups = kSdmDv / kSdmCols;
+constexpr int kSdmHash = 512;                // >= 4 x the written rows per token
+constexpr int kSdmFilterWords = 2048;        // 65,536-bit filter in front of the hash
+
+__device__ __forceinline__ uint32_t sdm_mix(int slot) { return (uint32_t)slot * 0x9E3779B1u; }
+
+__device__ __forceinline__ void lds_barrier() {  // LDS traffic waited for; global memory not
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+// vmcnt(0) (loads and stores), as the builtin so that the compiler's own wait
+// placement knows every earlier load has landed
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// The rows one token wrote, findable by slot: a filter bit per slot hash (a clear bit
+// means "not written", the common case: one LDS read), then an exact open-addressing
+// hash of slot -> row.
+struct SdmTable {
+    uint32_t filt[kSdmFilterWords];
+    int key[kSdmHash];
+    int row[kSdmHash];
+};
+
+// row of each of the 4 slots in the token's write list, or -1
+__device__ __forceinline__ void sdm_find4(const SdmTable &tb, const int (&slot)[4], int (&res)[4]) {
+    uint32_t f[4];
 #pragma unroll
-            for (int u = 0; u < 16; ++u) wreg[u] = *reinterpret_cast<const f32x4 *>(src + 4 * u);
-        }
-    };
-    if (p.T > 0) gather_write(0);
-    for (int t = 0; t < p.T; ++t) {
-        const long tk = tok(t);
-        // this token's read slots and weights, requested before the write
-        int rsl[16];
-        float rw[16];
+    for (int j = 0; j < 4; ++j) f[j] = tb.filt[sdm_mix(slot[j]) >> 21];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int r = rg + 8 * u;
-            rsl[u] = r < p.R ? p.ridx[tk * p.R + r] : 0;
-            rw[u] = r < p.R ? p.rwt[tk * p.R + r] : 0.f;
-        }
-        const float a = ld_elem(p.alpha, tk, p.gate_bf16), be = ld_elem(p.beta, tk, p.gate_bf16);
-        if (tid < kSdmDv) vv[tid] = ld_elem(p.v, tk * kSdmDv + tid, p.io_bf16);
-        __syncthreads();  // v of this token; the previous token's read partials are consumed
-        if (wrow < p.W) {
-            const float c = be * wc;
-            float *dst = Mh + (long)wsl * kSdmDv + wcol;
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                f32x4 m = wreg[u] * a;
-                const f32x4 vx = *reinterpret_cast<const f32x4 *>(&vv[wcol + 4 * u]);
-                m = m + c * (vx - m);
-                *reinterpret_cast<f32x4 *>(dst + 4 * u) = m;
+    for (int j = 0; j < 4; ++j) {
+        res[j] = -1;
+        const uint32_t m = sdm_mix(slot[j]);
+        if ((f[j] >> ((m >> 16) & 31)) & 1u) {
+            int h = (int)(m >> 23);
+#pragma unroll 1
+            for (int i = 0; i < kSdmHash; ++i) {
+                const int e = tb.key[h];
+                if (e == slot[j]) {
+                    res[j] = tb.row[h];
+                    break;
+                }
+                if (e < 0) break;
+                h = (h + 1) & (kSdmHash - 1);
             }
         }
-        __syncthreads();  // this token's rows are written (and visible to the workgroup)
-        // read rows of this token and write rows of the next one, requested together
-        f32x4 rreg[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u)
-            rreg[u] = *reinterpret_cast<const f32x4 *>(Mh + (long)rsl[u] * kSdmDv + 4 * rq);
-        if (t + 1 < p.T) gather_write(t + 1);
-        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int u = 0; u < 16; ++u) acc += rw[u] * rreg[u];
-        *reinterpret_cast<f32x4 *>(&part[rg][4 * rq]) = acc;
-        __syncthreads();
-        if (tid < kSdmDv) {
-            float s = 0.f;
-#pragma unroll
-            for (int g = 0; g < 8; ++g) s += part[g][tid];
-            st_elem(p.o, tk * kSdmDv + tid, s, p.io_bf16);
+    }
+}
+// returns the hash entry used (kept by the caller to clear it)
+__device__ __forceinline__ int sdm_insert(SdmTable &tb, int slot, int r) {
+    const uint32_t m = sdm_mix(slot);
+    atomicOr(&tb.filt[m >> 21], 1u << ((m >> 16) & 31));
+    int h = (int)(m >> 23);
+#pragma unroll 1
+    for (int i = 0; i < kSdmHash; ++i) {
+        if (atomicCAS(&tb.key[h], -1, slot) == -1) {
+            tb.row[h] = r;
+            return h;
         }
+        h = (h + 1) & (kSdmHash - 1);
+    }
+    return -1;
+}
+__device__ __forceinline__ void sdm_erase(SdmTable &tb, int slot, int h) {
+    const uint32_t m = sdm_mix(slot);
+    atomicAnd(&tb.filt[m >> 21], ~(1u << ((m >> 16) & 31)));
+    if (h >= 0) tb.key[h] = -1;
+}
+
+// ---------------------------------------------------------------------------
+// table pass
+// ---------------------------------------------------------------------------
+// One workgroup per (batch, head, group of 32 columns): the update and the read-out of a
+// column touch no other column, so the four column groups of a head run independently.
+// Thread (rg = tid / 8, q = tid % 8) holds columns 4q..4q+3 of the group for rows
+// 4 rg + j (j < 4) of the token's write list and of its read list.
+//
+// Tokens are software-pipelined one deep: the rows of token t + 1 are gathered while
+// token t is processed, so they can miss token t's writes (still in flight).  Those are
+// forwarded from LDS: token t's written rows are kept there with a table of their
+// slots, and every gathered row of token t + 1 is looked up in it.  Stores of token t - 1
+// are complete before token t + 1's gathers are issued (each wave waits for its own
+// stores, then the workgroup barrier), so one token of forwarding suffices, and each
+// token costs one memory round trip.  Reads of token t see token t's own writes the same
+// way (lookup after the update).
+template <int IO_BF, int GATE_BF>
+__global__ void __launch_bounds__(256) sdm_table_kernel(SdmParams p) {
+    __shared__ __attribute__((aligned(16))) float buf[2][kSdmMaxK][kSdmCols];
+    __shared__ SdmTable tabs[2];
+    __shared__ __attribute__((aligned(16))) float part[4][kSdmCols];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int q = tid & 7, rg = tid >> 3;
+    const int bh = blockIdx.x / kSdmGroups, cg = blockIdx.x % kSdmGroups;
+    const int b = bh / p.H, h = bh % p.H;
+    const int cb = cg * kSdmCols + 4 * q;                       // this thread's first column
+    const long N = (long)p.n * p.n;
+    float *Mh = p.M + (long)bh * N * kSdmDv + cb;
+    auto tok = [&](int t) -> long { return ((long)b * p.T + t) * p.H + h; };
+
+    for (int i = tid; i < kSdmFilterWords; i += 256) {
+        tabs[0].filt[i] = 0u;
+        tabs[1].filt[i] = 0u;
+    }
+    for (int i = tid; i < kSdmHash; i += 256) {
+        tabs[0].key[i] = -1;
+        tabs[1].key[i] = -1;
+    }
+
+    // slots and weights of the 4 consecutive rows this thread holds (the lists are padded
+    // to a multiple of 4 with a valid slot and weight 0; rows 4 rg >= W or R are clamped
+    // to the first 4 and never used)
+    int ws0[4], rs0[4], ws1[4], rs1[4];
+    float ww0[4], rw0[4], ww1[4], rw1[4];
+    const int wo = min(4 * rg, p.Wp - 4), ro = min(4 * rg, p.Rp - 4);
+    auto load_slots = [&](int t, int (&ws)[4], float (&ww)[4], int (&rs)[4], float (&rw)[4]) __attribute__((
+                          always_inline)) {
+        const long tk = tok(t);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(p.widx + tk * p.Wp + wo);
+        const f32x4 c = *reinterpret_cast<const f32x4 *>(p.wwt + tk * p.Wp + wo);
+        const u32x4 d = *reinterpret_cast<const u32x4 *>(p.ridx + tk * p.Rp + ro);
+        const f32x4 e = *reinterpret_cast<const f32x4 *>(p.rwt + tk * p.Rp + ro);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            ws[j] = (int)a[j];
+            ww[j] = c[j];
+            rs[j] = (int)d[j];
+            rw[j] = e[j];
+        }
+    };
+    // v and the gates are kept as loaded (raw bits) and converted only after the wait at
+    // the top of their token: converted at the load, they would make the compiler wait
+    // for the whole gather in flight.
+    struct Rows {
+        f32x4 w[4], r[4], vf;
+        u32x2 vb;
+        uint32_t a, be;
+    };
+    auto gather = [&](int t, const int (&ws)[4], const int (&rs)[4], Rows &x) __attribute__((always_inline)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            x.w[j] = *reinterpret_cast<const f32x4 *>(Mh + (long)ws[j] * kSdmDv);
+            x.r[j] = *reinterpret_cast<const f32x4 *>(Mh + (long)rs[j] * kSdmDv);
+        }
+        const long tk = tok(t);
+        if (IO_BF) x.vb = *reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(p.v) + tk * kSdmDv + cb);
+        else x.vf = *reinterpret_cast<const f32x4 *>(static_cast<const float *>(p.v) + tk * kSdmDv + cb);
+        if (GATE_BF) {
+            x.a = static_cast<const uint16_t *>(p.alpha)[tk];
+            x.be = static_cast<const uint16_t *>(p.beta)[tk];
+        } else {
+            x.a = static_cast<const uint32_t *>(p.alpha)[tk];
+            x.be = static_cast<const uint32_t *>(p.beta)[tk];
+        }
+    };
+    // the hash entry this thread filled for each table (thread q < 4 inserts row 4 rg + q)
+    int ins_slot[2] = {0, 0}, ins_h[2] = {-2, -2};
+    // One token.  (ws, ww, rs, rw) / x: its slots and rows; (wsn, rsn) / xn: the next
+    // token's slots (loaded) and rows (gathered here).  All loads are unconditional (token
+    // indices clamped) into registers whose last use is behind them.
+    auto step = [&](int t, int (&ws)[4], float (&ww)[4], int (&rs)[4], float (&rw)[4], const int (&wsn)[4],
+                    const int (&rsn)[4], Rows &x, Rows &xn, const int cur) __attribute__((always_inline)) {
+        const int prv = cur ^ 1;
+        wait_vmem();          // this token's rows, the next token's slots, own stores of t - 1
+        lds_barrier();        // every wave's stores of t - 1 done; table `cur` is empty
+        gather(min(t + 1, p.T - 1), wsn, rsn, xn);
+        uint32_t vb0 = x.vb[0], vb1 = x.vb[1], ab = x.a, bb = x.be;
+        asm volatile("" : "+v"(vb0), "+v"(vb1), "+v"(ab), "+v"(bb));
+        const f32x4 vv = IO_BF ? f32x4{__uint_as_float(vb0 << 16), __uint_as_float(vb0 & 0xffff0000u),
+                                       __uint_as_float(vb1 << 16), __uint_as_float(vb1 & 0xffff0000u)}
+                               : x.vf;
+        const float a = __uint_as_float(GATE_BF ? ab << 16 : ab), be = __uint_as_float(GATE_BF ? bb << 16 : bb);
+        if (t > 0) {          // rows written by token t - 1 after their gather was issued
+            int pw[4], pr[4];
+            sdm_find4(tabs[prv], ws, pw);
+            sdm_find4(tabs[prv], rs, pr);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (pw[j] >= 0) x.w[j] = *reinterpret_cast<const f32x4 *>(&buf[prv][pw[j]][4 * q]);
+                if (pr[j] >= 0) x.r[j] = *reinterpret_cast<const f32x4 *>(&buf[prv][pr[j]][4 * q]);
+            }
+        }
+        // the gated delta update of the written rows
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * rg + j;
+            if (r < p.W) {
+                const f32x4 m0 = x.w[j] * a;
+                const f32x4 m = m0 + (be * ww[j]) * (vv - m0);
+                *reinterpret_cast<f32x4 *>(Mh + (long)ws[j] * kSdmDv) = m;
+                *reinterpret_cast<f32x4 *>(&buf[cur][r][4 * q]) = m;
+            }
+        }
+        if (q < 4 && 4 * rg + q < p.W) {
+            const int sl = q == 0 ? ws[0] : q == 1 ? ws[1] : q == 2 ? ws[2] : ws[3];
+            ins_slot[cur] = sl;
+            ins_h[cur] = sdm_insert(tabs[cur], sl, 4 * rg + q);
+        }
+        lds_barrier();        // token t's rows and table complete; token t - 1's no longer read
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        {
+            int pr[4];
+            sdm_find4(tabs[cur], rs, pr);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (pr[j] >= 0) x.r[j] = *reinterpret_cast<const f32x4 *>(&buf[cur][pr[j]][4 * q]);
+                if (4 * rg + j < p.R) acc += rw[j] * x.r[j];
+            }
+        }
+        if (ins_h[prv] != -2) {   // empty token t - 1's table: it is token t + 1's
+            sdm_erase(tabs[prv], ins_slot[prv], ins_h[prv]);
+            ins_h[prv] = -2;
+        }
+        load_slots(min(t + 2, p.T - 1), ws, ww, rs, rw);
+        // read-out: sum over the rows of the wave sharing q, then over the four waves
+#pragma unroll
+        for (int off = 8; off < 64; off <<= 1) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) acc[c] += __shfl_xor(acc[c], off);
+        }
+        if (lane < 8) *reinterpret_cast<f32x4 *>(&part[wv][4 * lane]) = acc;
+        lds_barrier();
+        if (tid < kSdmCols) {
+            const float o = part[0][tid] + part[1][tid] + part[2][tid] + part[3][tid];
+            st_elem(p.o, tok(t) * kSdmDv + cg * kSdmCols + tid, o, IO_BF);
+        }
+    };
+    if (p.T <= 0) return;
+    Rows x0, x1;
+    load_slots(0, ws0, ww0, rs0, rw0);
+    gather(0, ws0, rs0, x0);
+    load_slots(min(1, p.T - 1), ws1, ww1, rs1, rw1);
+    for (int t = 0;; t += 2) {
+        step(t, ws0, ww0, rs0, rw0, ws1, rs1, x0, x1, 0);
+        if (t + 1 >= p.T) break;
+        step(t + 1, ws1, ww1, rs1, rw1, ws0, rs0, x1, x0, 1);
+        if (t + 2 >= p.T) break;
     }
 }
 
 }  // namespace
 
 size_t sdm_workspace(int B, int T, int H, int W, int R) {
-    return (size_t)B * T * H * (size_t)(W + R) * (sizeof(int32_t) + sizeof(float));
+    const size_t wp = (size_t)((W + 3) & ~3), rp = (size_t)((R + 3) & ~3);
+    return (size_t)B * T * H * (wp + rp) * (sizeof(int32_t) + sizeof(float));
 }
 
 hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
@@ -445,15 +631,18 @@ hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int
     SdmParams p;
     p.B = B; p.T = T; p.H = H; p.n = n; p.W = W; p.R = R; p.io_bf16 = io_bf16; p.gate_bf16 = gate_bf16;
     p.ks = ks; p.qs = qs; p.v = v; p.alpha = alpha; p.beta = beta; p.M = M; p.o = o;
-    char *w = static_cast<char *>(ws);
-    int32_t *wi = reinterpret_cast<int32_t *>(w);
-    int32_t *ri = wi + ntok * W;
-    float *ww = reinterpret_cast<float *>(ri + ntok * R);
-    float *rw = ww + ntok * W;
-    p.widx = wslots ? wslots : wi;
-    p.ridx = rslots ? rslots : ri;
+    p.Wp = (W + 3) & ~3;
+    p.Rp = (R + 3) & ~3;
+    int32_t *wi = static_cast<int32_t *>(ws);
+    int32_t *ri = wi + ntok * p.Wp;
+    float *ww = reinterpret_cast<float *>(ri + ntok * p.Rp);
+    float *rw = ww + ntok * p.Wp;
+    p.widx = wi;
+    p.ridx = ri;
     p.wwt = ww;
     p.rwt = rw;
+    p.uw = wslots;
+    p.ur = rslots;
     void *args[] = {&p};
     const long items = 2 * ntok;
     const int np = (n + 63) / 64;
@@ -466,8 +655,11 @@ hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int
                                    dim3((unsigned)((items + kSelWaves - 1) / kSelWaves)), dim3(64 * kSelWaves), args, 0,
                                    st);
     if (e != hipSuccess) return e;
-    return hipLaunchKernel(reinterpret_cast<const void *>(&sdm_table_kernel), dim3((unsigned)(B * H)), dim3(256), args,
-                           0, st);
+    const void *tab = io_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(&sdm_table_kernel<1, 1>)
+                                           : reinterpret_cast<const void *>(&sdm_table_kernel<1, 0>))
+                              : (gate_bf16 ? reinterpret_cast<const void *>(&sdm_table_kernel<0, 1>)
+                                           : reinterpret_cast<const void *>(&sdm_table_kernel<0, 0>));
+    return hipLaunchKernel(tab, dim3((unsigned)(B * H * kSdmGroups)), dim3(256), args, 0, st);
 }
 
 }  // namespace gdr
