@@ -72,19 +72,9 @@ __device__ __forceinline__ void wsync() {  // order LDS traffic between the lane
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-__device__ __forceinline__ int wave_sum(int x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
 __device__ __forceinline__ float wave_fsum(float x) {
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) x += __shfl_xor(x, off);
-    return x;
-}
-__device__ __forceinline__ int wave_imin(int x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = min(x, __shfl_xor(x, off));
     return x;
 }
 __device__ __forceinline__ uint32_t wave_umin(uint32_t x) {
@@ -97,57 +87,72 @@ __device__ __forceinline__ uint32_t wave_umax(uint32_t x) {
     for (int off = 32; off > 0; off >>= 1) x = max(x, (uint32_t)__shfl_xor((int)x, off));
     return x;
 }
-__device__ __forceinline__ int wave_excl_scan(int x, int lane) {  // exclusive prefix sum
-    int incl = x;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int y = __shfl_up(incl, off);
-        if (lane >= off) incl += y;
-    }
-    return incl - x;
+__device__ __forceinline__ int popc(uint64_t m) { return __popcll(m); }
+// number of set bits of m below this lane
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // Largest key t with at least k of the keys q at or above it (lo / hi: the smallest and
-// largest valid key; invalid entries hold 0, below every valid key).
+// largest valid key; invalid entries hold 0, below every valid key).  Counts by ballot.
 template <int NQ>
 __device__ __forceinline__ uint32_t kth_key(const uint32_t (&q)[NQ], uint32_t lo, uint32_t hi, int k) {
     while (lo < hi) {
         const uint32_t mid = lo + (uint32_t)(((uint64_t)(hi - lo) + 1u) >> 1);
         int c = 0;
 #pragma unroll
-        for (int u = 0; u < NQ; ++u) c += q[u] >= mid;
-        if (wave_sum(c) >= k) lo = mid;
+        for (int u = 0; u < NQ; ++u) c += popc(__ballot(q[u] >= mid));
+        if (c >= k) lo = mid;
         else hi = mid - 1;
     }
     return lo;
 }
 
+// Sort key of a scored slot: higher score first, then lower slot (unique per slot).
+__device__ __forceinline__ uint64_t skey(uint32_t score_key, int slot) {
+    return ((uint64_t)score_key << 32) | (uint32_t)~(uint32_t)slot;
+}
+__device__ __forceinline__ int skey_slot(uint64_t k) { return (int)~(uint32_t)k; }
+__device__ __forceinline__ uint64_t shfl_xor64(uint64_t x, int m) {
+    const int lo = __shfl_xor((int)(uint32_t)x, m), hi = __shfl_xor((int)(uint32_t)(x >> 32), m);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+// Bitonic sort, descending, of the 128 keys held as element 2 lane + i in k_i.
+__device__ __forceinline__ void bitonic128(uint64_t &k0, uint64_t &k1, int lane) {
+#pragma unroll
+    for (int size = 2; size <= 128; size <<= 1) {
+        const bool up = ((2 * lane) & size) != 0;        // this block sorts ascending
+#pragma unroll
+        for (int d = size >> 1; d >= 1; d >>= 1) {
+            if (d == 1) {
+                const uint64_t mx = max(k0, k1), mn = min(k0, k1);
+                k0 = up ? mn : mx;
+                k1 = up ? mx : mn;
+            } else {
+                const int ld = d >> 1;
+                const uint64_t p0 = shfl_xor64(k0, ld), p1 = shfl_xor64(k1, ld);
+                const bool keep_max = ((lane & ld) == 0) != up;
+                k0 = keep_max ? max(k0, p0) : min(k0, p0);
+                k1 = keep_max ? max(k1, p1) : min(k1, p1);
+            }
+        }
+    }
+}
+
 struct SelWave {
+    uint64_t kk[kSdmMaxK];      // winners' sort keys, staged for the sort
     float hv[2][kSdmMaxK];      // each half's top-k values, best first
     int hi[2][kSdmMaxK];        // and their positions in the half
     uint32_t ck[kCandMax];      // candidate pair keys
     uint16_t cij[kCandMax];     // and their (row, column) in the two top-k lists
-    float cv[kSdmMaxK];         // winners (unsorted), then sorted
-    int cs[kSdmMaxK];
-    float sv[kSdmMaxK];
-    int ss[kSdmMaxK];
 };
 
-// Rank-sort the k entries (cv, cs) into (sv, ss): higher value first, lower slot on ties.
-__device__ __forceinline__ void wave_rank_sort(SelWave &w, int k, int lane) {
+// the k staged keys w.kk[0..k) sorted best first into (k0, k1) of element 2 lane + i
+__device__ __forceinline__ void sort_staged(SelWave &w, int k, int lane, uint64_t &k0, uint64_t &k1) {
     wsync();
-    for (int e = lane; e < k; e += 64) {
-        const float x = w.cv[e];
-        const int sx = w.cs[e];
-        int r = 0;
-        for (int f = 0; f < k; ++f) {
-            const float y = w.cv[f];
-            r += (y > x) || (y == x && w.cs[f] < sx);
-        }
-        w.sv[r] = x;
-        w.ss[r] = sx;
-    }
-    wsync();
+    k0 = 2 * lane < k ? w.kk[2 * lane] : 0ull;
+    k1 = 2 * lane + 1 < k ? w.kk[2 * lane + 1] : 0ull;
+    bitonic128(k0, k1, lane);
 }
 
 // Top-k of one half (m values, x[u] holds position 64 u + lane), sorted into w.hv[h],
@@ -169,38 +174,34 @@ __device__ uint32_t half_topk(SelWave &w, int h, const float (&x)[NP], int m, in
     uint32_t below = 0u;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-        const bool gt = q[u] > th;
-        const int pos = ngt + wave_excl_scan(gt ? 1 : 0, lane);
-        if (gt && pos < k) {
-            w.cv[pos] = x[u];
-            w.cs[pos] = 64 * u + lane;
-        }
-        ngt += wave_sum(gt ? 1 : 0);
-        cge += q[u] >= th;
+        const uint64_t mgt = __ballot(q[u] > th);
+        const int pos = ngt + lanes_below(mgt);
+        if (q[u] > th && pos < k) w.kk[pos] = skey(q[u], 64 * u + lane);
+        ngt += popc(mgt);
+        cge += popc(__ballot(q[u] >= th));
         below = q[u] < th ? max(below, q[u]) : below;
     }
     ngt = min(ngt, k);
-    int need = k - ngt;
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
-        if (need > 0) {
-            const bool eq = q[u] == th;
-            const int pos = wave_excl_scan(eq ? 1 : 0, lane);
-            if (eq && pos < need) {
-                w.cv[ngt + pos] = x[u];
-                w.cs[ngt + pos] = 64 * u + lane;
-            }
-            const int take = min(wave_sum(eq ? 1 : 0), need);
-            ngt += take;
-            need -= take;
+        if (ngt < k) {
+            const uint64_t meq = __ballot(q[u] == th);
+            const int pos = ngt + lanes_below(meq);
+            if (q[u] == th && pos < k) w.kk[pos] = skey(q[u], 64 * u + lane);
+            ngt = min(ngt + popc(meq), k);
         }
     }
-    wave_rank_sort(w, k, lane);
-    for (int e = lane; e < k; e += 64) {
-        w.hv[h][e] = w.sv[e];
-        w.hi[h][e] = w.ss[e];
+    uint64_t k0, k1;
+    sort_staged(w, k, lane, k0, k1);
+    if (2 * lane < k) {
+        w.hv[h][2 * lane] = key_val((uint32_t)(k0 >> 32));
+        w.hi[h][2 * lane] = skey_slot(k0);
     }
-    return wave_sum(cge) > k ? th : wave_umax(below);
+    if (2 * lane + 1 < k) {
+        w.hv[h][2 * lane + 1] = key_val((uint32_t)(k1 >> 32));
+        w.hi[h][2 * lane + 1] = skey_slot(k1);
+    }
+    return cge > k ? th : wave_umax(below);
 }
 
 // number of j < k with A[i] + B[j] at or above key th (a prefix: the row is nonincreasing)
@@ -218,10 +219,10 @@ __device__ __forceinline__ int row_count_ge(const SelWave &w, float ai, int k, u
 // k best pair sums of the two sorted lists lie among the pairs (i, j) with
 // (i + 1)(j + 1) <= k (a pair outside is dominated by more than k pairs that are at least
 // as large), so the k-th largest key is found by bisection over those <= 645 candidates,
-// held in registers.  Pairs above it are all
-// candidates; pairs equal to it are taken by lower slot, from the full rows of the
-// grid -- or from every slot of the table when a pair outside the two top-k lists can
-// reach it (rounding of the fp32 sums, or ties at a half's boundary).
+// held in registers.  Pairs above it are all candidates; pairs equal to it are taken by
+// lower slot, from the full rows of the grid -- or from every slot of the table when a
+// pair outside the two top-k lists can reach it (rounding of the fp32 sums, or ties at a
+// half's boundary).
 template <int NP>
 __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p) {
     __shared__ SelWave sel[kSelWaves];
@@ -251,8 +252,9 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
     int off = 0;
     for (int i = 0; i < r0; ++i) {
         const int L = min(kh, k / (i + 1));
+        const float ai = w.hv[0][i];
         for (int j = lane; j < L; j += 64) {
-            w.ck[off + j] = okey(w.hv[0][i] + w.hv[1][j]);
+            w.ck[off + j] = okey(ai + w.hv[1][j]);
             w.cij[off + j] = (uint16_t)((i << 7) | j);
         }
         off += L;
@@ -261,12 +263,18 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
     for (int u = 0; u < 2; ++u) {
         const int i = r0 + 64 * u + lane;
         const int L = i < kh ? min(kh, k / (i + 1)) : 0;
-        const int o = off + wave_excl_scan(L, lane);
-        for (int j = 0; j < L; ++j) {
-            w.ck[o + j] = okey(w.hv[0][i] + w.hv[1][j]);
-            w.cij[o + j] = (uint16_t)((i << 7) | j);
+        int incl = L;                                            // inclusive scan of L over the lanes
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o);
+            if (lane >= o) incl += y;
         }
-        off += wave_sum(L);
+        const int o0 = off + incl - L;
+        for (int j = 0; j < L; ++j) {
+            w.ck[o0 + j] = okey(w.hv[0][i] + w.hv[1][j]);
+            w.cij[o0 + j] = (uint16_t)((i << 7) | j);
+        }
+        off += __shfl(incl, 63);
     }
     const int nc = off;
     wsync();
@@ -284,17 +292,15 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
     int ngt = 0;
 #pragma unroll
     for (int u = 0; u < kCandRegs; ++u) {
-        const bool gt = cq[u] > th;
-        const int pos = ngt + wave_excl_scan(gt ? 1 : 0, lane);
-        if (gt && pos < k) {
+        const uint64_t mgt = __ballot(cq[u] > th);
+        const int pos = ngt + lanes_below(mgt);
+        if (cq[u] > th && pos < k) {
             const int ij = w.cij[64 * u + lane], i = ij >> 7, j = ij & 127;
-            w.cv[pos] = w.hv[0][i] + w.hv[1][j];
-            w.cs[pos] = w.hi[0][i] * n + w.hi[1][j];
+            w.kk[pos] = skey(cq[u], w.hi[0][i] * n + w.hi[1][j]);
         }
-        ngt += wave_sum(gt ? 1 : 0);
+        ngt += popc(mgt);
     }
     ngt = min(ngt, k);
-    const float tv = key_val(th);
     bool outside = false;
     if (kh < n) {
         if (nx0) outside |= okey(key_val(nx0) + w.hv[1][0]) >= th;
@@ -314,70 +320,54 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
                     if (sl > last) best = min(best, sl);
                 }
             }
-            best = wave_imin(best);
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) best = min(best, __shfl_xor(best, o));
             if (best == 0x7fffffff) best = 0;   // unreachable (the grid holds enough ties); keeps a valid slot
-            if (lane == 0) {
-                w.cs[ngt] = best;
-                w.cv[ngt] = tv;
-            }
+            if (lane == 0) w.kk[ngt] = skey(th, best);
             last = best;
             ++ngt;
         }
     } else {
         // ties at the k-th key over the whole table, in slot order
-        int need = k - ngt;
-        for (int a = 0; a < n && need > 0; ++a) {
+        for (int a = 0; a < n && ngt < k; ++a) {
             const float sa = clean(src[a]);
 #pragma unroll
             for (int u = 0; u < NP; ++u) {
-                if (need > 0) {
-                    const int b = 64 * u + lane;
-                    const bool eq = b < n && okey(sa + x1[u]) == th;
-                    const int pos = wave_excl_scan(eq ? 1 : 0, lane);
-                    if (eq && pos < need) {
-                        w.cs[ngt + pos] = a * n + b;
-                        w.cv[ngt + pos] = tv;
-                    }
-                    const int take = min(wave_sum(eq ? 1 : 0), need);
-                    ngt += take;
-                    need -= take;
+                if (ngt < k) {
+                    const int b2 = 64 * u + lane;
+                    const bool eq = b2 < n && okey(sa + x1[u]) == th;
+                    const uint64_t meq = __ballot(eq);
+                    const int pos = ngt + lanes_below(meq);
+                    if (eq && pos < k) w.kk[pos] = skey(th, a * n + b2);
+                    ngt = min(ngt + popc(meq), k);
                 }
             }
         }
     }
-    wave_rank_sort(w, k, lane);
-    // softmax weights of the sorted winners
-    const float mx = w.sv[0];
-    float part = 0.f;
-    for (int e = lane; e < k; e += 64) part += expf(w.sv[e] - mx);
-    const float tot = wave_fsum(part);
+    uint64_t k0, k1;
+    sort_staged(w, k, lane, k0, k1);
+    // softmax weights of the sorted winners (element 2 lane + i)
+    const float v0 = key_val((uint32_t)(k0 >> 32)), v1 = key_val((uint32_t)(k1 >> 32));
+    const float mx = __shfl(v0, 0);
+    const float e0 = 2 * lane < k ? expf(v0 - mx) : 0.f, e1 = 2 * lane + 1 < k ? expf(v1 - mx) : 0.f;
+    const float inv = 1.f / wave_fsum(e0 + e1);
     const int kp = which ? p.Rp : p.Wp;
     int32_t *oi = (which ? p.ridx : p.widx) + tk * kp;
     float *ow = (which ? p.rwt : p.wwt) + tk * kp;
     int32_t *ou = which ? p.ur : p.uw;
-    for (int e = lane; e < kp; e += 64) {       // padding: a valid slot and weight 0
-        oi[e] = w.ss[min(e, k - 1)];
-        ow[e] = e < k ? expf(w.sv[e] - mx) / tot : 0.f;
-        if (ou && e < k) ou[tk * k + e] = w.ss[e];
+    const int best = __shfl(skey_slot(k0), 0);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {                // padding: a valid slot and weight 0
+        const int e = 2 * lane + i;
+        const int sl = i ? skey_slot(k1) : skey_slot(k0);
+        if (e < kp) {
+            oi[e] = e < k ? sl : best;
+            ow[e] = e < k ? (i ? e1 : e0) * inv : 0.f;
+            if (ou && e < k) ou[tk * k + e] = sl;
+        }
     }
 }
 
-// ---------------------------------------------------------------------------
-// table pass
-// ---------------------------------------------------------------------------
-// One workgroup per (batch, head, group of 32 columns): the update and the read-out of a
-// column touch no other column, so the four column groups of a head run independently.
-// Thread (rg = tid / 8, q = tid % 8) holds columns 4q..4q+3 of the group for rows
-// rg + 32 j (j < 4) of the token's write list and of its read list.
-//
-// Tokens are software-pipelined one deep: the rows of token t + 1 are gathered while
-// token t is processed, so they can miss token t's writes (still in flight).  Those are
-// forwarded from LDS: token t's written rows are kept there with a small hash of their
-// slots, and every gathered row of token t + 1 is looked up in it.  Stores of token t - 1
-// are complete before token t + 1's gathers are issued (each wave waits for its own
-// stores, then the workgroup barrier), so one token of forwarding suffices, and each
-// token costs one memory round trip.  Reads of token t see token t's own writes the same
-// way (lookup after the update).
 constexpr int kSdmCols = 32;                 // columns per workgroup
 constexpr int kSdmGroups = kSdmDv / kSdmCols;
 constexpr int kSdmHash = 512;                // >= 4 x the written rows per token
