@@ -115,7 +115,7 @@ def cpu_baseline(w, x, budget_heads):
                       f"recurrence, OpenMP over pairs, {dt:.2f} s wall"}
 
 
-def bench_mc_readout(g, gi, stream, reps):
+def bench_mc_readout(g, gi, stream, reps, digest=None):
     """The cache read-out of the long-context batch, inputs resident, events on the
     launch stream around each call (the small cache-preparation launch included)."""
     import torch
@@ -153,10 +153,10 @@ def bench_mc_readout(g, gi, stream, reps):
     return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
             "algorithmic_flops": fl, "caches": w.N, "gates": w.gate_kind,
             "roofline": {"bound": "mfma", "achieved": tf, "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": None}}
+                         "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": load_traffic(w.name, digest)}}
 
 
-def bench_osdn_precond(g, gi, stream, reps):
+def bench_osdn_precond(g, gi, stream, reps, digest=None):
     """OSDN phase 1 over the long-context batch's keys (B=1, H=32, T=65536, retention
     gates), inputs resident; events on the launch stream around each call (chunk
     solve + scan).  Algorithmic bytes: k read and k_w written (bf16), beta and r
@@ -195,10 +195,11 @@ def bench_osdn_precond(g, gi, stream, reps):
     ntok = w.B * w.T * w.H
     nbytes = ntok * (2 * w.dk * 2 + 2 * 4) + 2 * w.B * w.H * w.dk * 4
     gbs = nbytes / (ms * 1e-3) / 1e9
-    return {"workload": "osdn_precond_bf16_B1H32T65536d128_retention", "ms_per_call": ms,
+    name = "osdn_precond_bf16_B1H32T65536d128_retention"
+    return {"workload": name, "ms_per_call": ms,
             "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes, "qgeo_mean": float(qg.mean()),
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(name, digest)}}
 
 
 def sdm_bytes(w, gi):
@@ -211,7 +212,7 @@ def sdm_bytes(w, gi):
     return w.B * w.T * w.H * per
 
 
-def bench_sdm(g, gi, stream, reps):
+def bench_sdm(g, gi, stream, reps, digest=None):
     """Sparse Delta Memory at B=4 H=16 T=4096, 65,536 slots x 128 per head, W = R = 128,
     inputs and the 2 GiB of tables resident; events on the launch stream around each call
     (selection + table pass; the table evolves from call to call, the work does not)."""
@@ -251,7 +252,7 @@ def bench_sdm(g, gi, stream, reps):
     return {"workload": w.name, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3),
             "algorithmic_bytes": nbytes,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None}}
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(w.name, digest)}}
 
 
 def main():
@@ -408,9 +409,9 @@ def main():
                                          "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(wd.name, digest)}}
             del graph, dd, S
         out["decode"] = dec
-        out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps)
-        out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps)
-        out["sdm"] = bench_sdm(g, gi, stream, args.mc_reps)
+        out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps, digest)
+        out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps, digest)
+        out["sdm"] = bench_sdm(g, gi, stream, args.mc_reps, digest)
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
