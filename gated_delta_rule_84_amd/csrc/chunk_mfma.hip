@@ -263,25 +263,32 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     // rows past the end of a short chunk read the last valid row; their Gram and
     // score entries are masked below
     auto rowt = [&](int t) -> long { return tok(min(t, n - 1)) * kD; };
-    u32x4 ka[4], qa[4];
+    u32x4 qa[4];
     {
-        const int tg = 16 * IG + r, tp = 16 * IP + r;
+        const int tp = 16 * IP + r;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            ka[kk] = ld16(K + rowt(tg) + kk * 32 + 8 * q);
-            qa[kk] = ld16(Q + rowt(tp) + kk * 32 + 8 * q);
-        }
+        for (int kk = 0; kk < 4; ++kk) qa[kk] = ld16(Q + rowt(tp) + kk * 32 + 8 * q);
     }
-    // the write-key tile is copied once into LDS (the space As and Ts take later; wave w
-    // copies rows 16 w .. 16 w + 15, 16-byte pieces of row t stored at piece ^ (t & 15))
-    // and every wave reads its B fragments from there
+    // the write-key tile is copied once into LDS (the space As takes later; wave w copies
+    // rows 16 w .. 16 w + 15, 16-byte pieces of row t stored at piece ^ (t & 15)) and
+    // every wave reads its B fragments from there; the key tile, when it is a different
+    // tensor, likewise into the space Ts takes later -- each tile is read from HBM once
+    const bool sep = p.kw != p.k;
     uint16_t(*KWs)[kD] = reinterpret_cast<uint16_t(*)[kD]>(&As[0][0]);
+    uint16_t(*Ks)[kD] = sep ? reinterpret_cast<uint16_t(*)[kD]>(&Ts[0][0]) : KWs;
 #pragma unroll
     for (int u = 4 * w; u < 4 * w + 4; ++u) {
         const int t = 4 * u + (l >> 4), pc = (l & 15) ^ (t & 15);
         dma16(KW + rowt(t) + 8 * pc, &KWs[4 * u][0]);
+        if (sep) dma16(K + rowt(t) + 8 * pc, &Ks[4 * u][0]);
     }
     __syncthreads();  // drains this block's copies and loads
+    u32x4 ka[4];
+    {
+        const int tg = 16 * IG + r;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) ka[kk] = *reinterpret_cast<const u32x4 *>(&Ks[tg][8 * ((4 * kk + q) ^ (tg & 15))]);
+    }
     f32x4 accG[4], accP[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
