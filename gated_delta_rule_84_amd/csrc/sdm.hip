@@ -26,6 +26,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "gdr_device.hpp"
 #include "gdr_internal.hpp"
 #include "gdr_mfma.hpp"
@@ -51,6 +53,7 @@ struct SdmParams {
     float *wwt, *rwt;
     int Wp, Rp;
     int32_t *uw, *ur;           // caller's slot outputs [B, T, H, W] / [B, T, H, R] or null
+    int t0, t1;                 // the launch covers tokens t0 .. t1 - 1 of every (batch, head)
 };
 
 // Order-preserving integer key of a (sanitised, non-NaN) float: unsigned order ==
@@ -228,9 +231,10 @@ __global__ void __launch_bounds__(64 * kSelWaves) sdm_select_kernel(SdmParams p)
     __shared__ SelWave sel[kSelWaves];
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const long item = (long)blockIdx.x * kSelWaves + wv;        // (token-head) * 2 + which
-    const long ntok = (long)p.B * p.T * p.H;
-    if (item >= 2 * ntok) return;
-    const long tk = item >> 1;
+    const int len = p.t1 - p.t0;
+    if (item >= 2L * p.B * len * p.H) return;
+    const long il = item >> 1, bt = il / p.H;                    // (batch, token in range), head
+    const long tk = ((bt / len) * p.T + p.t0 + bt % len) * p.H + il % p.H;
     const int which = (int)(item & 1);                           // 0 write (key), 1 read (query)
     const int k = which ? p.R : p.W, n = p.n;
     const int kh = min(k, n);                                    // length of each half's list
@@ -531,14 +535,14 @@ __global__ void __launch_bounds__(256) sdm_table_kernel(SdmParams p) {
         const int prv = cur ^ 1;
         wait_vmem();          // this token's rows, the next token's slots, own stores of t - 1
         lds_barrier();        // every wave's stores of t - 1 done; table `cur` is empty
-        gather(min(t + 1, p.T - 1), wsn, rsn, xn);
+        gather(min(t + 1, p.t1 - 1), wsn, rsn, xn);
         uint32_t vb0 = x.vb[0], vb1 = x.vb[1], ab = x.a, bb = x.be;
         asm volatile("" : "+v"(vb0), "+v"(vb1), "+v"(ab), "+v"(bb));
         const f32x4 vv = IO_BF ? f32x4{__uint_as_float(vb0 << 16), __uint_as_float(vb0 & 0xffff0000u),
                                        __uint_as_float(vb1 << 16), __uint_as_float(vb1 & 0xffff0000u)}
                                : x.vf;
         const float a = __uint_as_float(GATE_BF ? ab << 16 : ab), be = __uint_as_float(GATE_BF ? bb << 16 : bb);
-        if (t > 0) {          // rows written by token t - 1 after their gather was issued
+        if (t > p.t0) {       // rows written by token t - 1 after their gather was issued
             int pw[4], pr[4];
             sdm_find4(tabs[prv], ws, pw);
             sdm_find4(tabs[prv], rs, pr);
@@ -579,7 +583,7 @@ __global__ void __launch_bounds__(256) sdm_table_kernel(SdmParams p) {
             sdm_erase(tabs[prv], ins_slot[prv], ins_h[prv]);
             ins_h[prv] = -2;
         }
-        load_slots(min(t + 2, p.T - 1), ws, ww, rs, rw);
+        load_slots(min(t + 2, p.t1 - 1), ws, ww, rs, rw);
         // read-out: sum over the rows of the wave sharing q, then over the four waves
 #pragma unroll
         for (int off = 8; off < 64; off <<= 1) {
@@ -593,16 +597,16 @@ __global__ void __launch_bounds__(256) sdm_table_kernel(SdmParams p) {
             st_elem(p.o, tok(t) * kSdmDv + cg * kSdmCols + tid, o, IO_BF);
         }
     };
-    if (p.T <= 0) return;
+    if (p.t1 <= p.t0) return;
     Rows x0, x1;
-    load_slots(0, ws0, ww0, rs0, rw0);
-    gather(0, ws0, rs0, x0);
-    load_slots(min(1, p.T - 1), ws1, ww1, rs1, rw1);
-    for (int t = 0;; t += 2) {
+    load_slots(p.t0, ws0, ww0, rs0, rw0);
+    gather(p.t0, ws0, rs0, x0);
+    load_slots(min(p.t0 + 1, p.t1 - 1), ws1, ww1, rs1, rw1);
+    for (int t = p.t0;; t += 2) {
         step(t, ws0, ww0, rs0, rw0, ws1, rs1, x0, x1, 0);
-        if (t + 1 >= p.T) break;
+        if (t + 1 >= p.t1) break;
         step(t + 1, ws1, ww1, rs1, rw1, ws0, rs0, x1, x0, 1);
-        if (t + 2 >= p.T) break;
+        if (t + 2 >= p.t1) break;
     }
 }
 
@@ -612,6 +616,35 @@ size_t sdm_workspace(int B, int T, int H, int W, int R) {
     const size_t wp = (size_t)((W + 3) & ~3), rp = (size_t)((R + 3) & ~3);
     return (size_t)B * T * H * (wp + rp) * (sizeof(int32_t) + sizeof(float));
 }
+
+// The selection of a block of tokens runs on a side stream while the table pass works
+// through the blocks before it on the caller's stream: the table pass holds one
+// workgroup per CU and is latency bound, so the selection's blocks fill the rest of
+// each CU.  The table pass of block j waits for the selection of block j only.  The
+// side stream and its events are created once per device (default priority) and
+// reused; the host-side enqueue is serialised per device by a mutex.  The fork / join
+// through events also keeps the call capturable in a HIP graph of the caller's stream.
+namespace {
+constexpr int kSdmMaxDev = 64;
+constexpr int kSdmBlocks = 64;    // most token blocks of a call (blocks of >= 128 tokens)
+struct SdmSide {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t side = nullptr;
+    hipEvent_t fork = nullptr, done[kSdmBlocks] = {};
+};
+SdmSide g_side[kSdmMaxDev];
+
+hipError_t sdm_side_init(SdmSide &sd) {
+    if (sd.ready) return hipSuccess;
+    hipError_t e = hipStreamCreateWithFlags(&sd.side, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
+    for (int j = 0; j < kSdmBlocks && e == hipSuccess; ++j) e = hipEventCreateWithFlags(&sd.done[j], hipEventDisableTiming);
+    if (e == hipSuccess) sd.ready = true;
+    return e;
+}
+}  // namespace
 
 hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
                       const float *qs, const void *v, const void *alpha, const void *beta, float *M, void *o,
@@ -633,23 +666,50 @@ hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int
     p.rwt = rw;
     p.uw = wslots;
     p.ur = rslots;
-    void *args[] = {&p};
-    const long items = 2 * ntok;
     const int np = (n + 63) / 64;
     const void *sel = np <= 1 ? reinterpret_cast<const void *>(&sdm_select_kernel<1>)
                       : np <= 2 ? reinterpret_cast<const void *>(&sdm_select_kernel<2>)
                       : np <= 4 ? reinterpret_cast<const void *>(&sdm_select_kernel<4>)
                       : np <= 8 ? reinterpret_cast<const void *>(&sdm_select_kernel<8>)
                                 : reinterpret_cast<const void *>(&sdm_select_kernel<16>);
-    hipError_t e = hipLaunchKernel(sel,
-                                   dim3((unsigned)((items + kSelWaves - 1) / kSelWaves)), dim3(64 * kSelWaves), args, 0,
-                                   st);
-    if (e != hipSuccess) return e;
     const void *tab = io_bf16 ? (gate_bf16 ? reinterpret_cast<const void *>(&sdm_table_kernel<1, 1>)
                                            : reinterpret_cast<const void *>(&sdm_table_kernel<1, 0>))
                               : (gate_bf16 ? reinterpret_cast<const void *>(&sdm_table_kernel<0, 1>)
                                            : reinterpret_cast<const void *>(&sdm_table_kernel<0, 0>));
-    return hipLaunchKernel(tab, dim3((unsigned)(B * H * kSdmGroups)), dim3(256), args, 0, st);
+    auto launch = [&](const void *fn, int t0, int t1, hipStream_t s) -> hipError_t {
+        SdmParams a = p;
+        a.t0 = t0;
+        a.t1 = t1;
+        void *args[] = {&a};
+        if (fn == tab) return hipLaunchKernel(fn, dim3((unsigned)(B * H * kSdmGroups)), dim3(256), args, 0, s);
+        const long items = 2L * B * (t1 - t0) * H;
+        return hipLaunchKernel(fn, dim3((unsigned)((items + kSelWaves - 1) / kSelWaves)), dim3(64 * kSelWaves), args,
+                               0, s);
+    };
+    const int nblk = T >= 1024 ? min(kSdmBlocks, T / 128) : 1;
+    if (nblk == 1) {
+        const hipError_t e = launch(sel, 0, T, st);
+        return e != hipSuccess ? e : launch(tab, 0, T, st);
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kSdmMaxDev) return hipErrorInvalidDevice;
+    SdmSide &sd = g_side[dev];
+    std::lock_guard<std::mutex> lock(sd.mu);
+    if ((e = sdm_side_init(sd)) != hipSuccess) return e;
+    auto bound = [&](int j) { return (int)((long)T * j / nblk); };
+    if ((e = hipEventRecord(sd.fork, st)) != hipSuccess) return e;           // inputs ready on st
+    if ((e = hipStreamWaitEvent(sd.side, sd.fork, 0)) != hipSuccess) return e;
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = launch(sel, bound(j), bound(j + 1), sd.side)) != hipSuccess) return e;
+        if ((e = hipEventRecord(sd.done[j], sd.side)) != hipSuccess) return e;
+    }
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = hipStreamWaitEvent(st, sd.done[j], 0)) != hipSuccess) return e;
+        if ((e = launch(tab, bound(j), bound(j + 1), st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdr

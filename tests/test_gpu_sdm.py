@@ -51,6 +51,8 @@ CASES = [
     ("headline_widths_n256", BASE.scaled(B=1, H=2, T=20, n=256, W=128, R=128, seed=97)),
     ("n1024_np16", BASE.scaled(B=1, H=1, T=6, n=1024, W=128, R=100, seed=98)),
     ("widths_over_64", BASE.scaled(B=1, H=2, T=10, n=128, W=65, R=127, seed=99)),
+    # T >= 1024: selection and table pass in eight token blocks on two streams
+    ("token_blocks_T1100", BASE.scaled(B=2, H=2, T=1100, n=16, W=6, R=5, seed=100)),
 ]
 
 
