@@ -115,6 +115,72 @@ def cpu_baseline(w, x, budget_heads):
                       f"recurrence, OpenMP over pairs, {dt:.2f} s wall"}
 
 
+def cpu_baseline_detail(gi):
+    """The fp64 oracle on bounded samples of the other configurations (a few seconds
+    each), and single-threaded on the headline batch: wall time and tokens/s."""
+    import numpy as np
+
+    import oracle
+
+    oracle.build(force=False)
+    cores = min(os.cpu_count() or 1, 16)
+    out = {"cores_available": os.cpu_count(), "threads_cap": 16}
+
+    def prefill(w, heads, threads, label):
+        x = gi.make_prefill(w)
+        f = gi.prefill_f64(w, x)
+        hs = list(range(min(heads, w.B * w.H)))
+        t0 = time.perf_counter()
+        oracle.forward(f["q"], f["k"], f["v"], f["alpha"], f["beta_k"], k_w=f["k_w"], beta_v=f["beta_v"],
+                       S0=f["S0"], heads=hs, nthreads=threads)
+        dt = time.perf_counter() - t0
+        return {"tokens_per_s": w.T * len(hs) / w.H / dt, "head_tokens_per_s": w.T * len(hs) / dt, "wall_s": dt,
+                "threads": threads, "sample": f"{label}: {len(hs)} (batch, head) pairs x {w.T} tokens"}
+
+    out[gi.TINY_GDN_F32.name] = prefill(gi.TINY_GDN_F32, 1, 1, "the whole workload")
+    w2 = gi.GDN_PREFILL
+    out[w2.name + "_single_thread"] = prefill(w2, 4, 1, "4 of 64 pairs, one thread")
+    out[gi.KDA_FG2PLUS_PREFILL.name] = prefill(gi.KDA_FG2PLUS_PREFILL, 16, min(16, cores), "16 of 64 pairs")
+    w4 = gi.OSDN_LONG_PREFILL.scaled(H=4)
+    out[gi.OSDN_LONG_PREFILL.name] = prefill(w4, 4, min(4, cores), "4 of 32 heads (drawn as an H=4 batch)")
+    for wd, label in ((gi.DECODE_B512.scaled(B=16), "16 of 512 batch rows x 16 heads"),
+                      (gi.DECODE_DMEM_R8, "the whole workload")):
+        x = gi.make_decode(wd)
+        f = gi.decode_f64(wd, x)
+        S = f["S"]
+        t0 = time.perf_counter()
+        for t in range(wd.steps):
+            _, S = oracle.decode_step(S, f["q"][t], f["k"][t], f["v"][t], f["alpha"][t], f["beta_k"][t],
+                                      nthreads=cores)
+        dt = time.perf_counter() - t0
+        name = gi.DECODE_B512.name if wd.B == 16 else wd.name
+        out[name] = {"tokens_per_s": wd.B * wd.steps / dt, "us_per_step": dt / wd.steps * 1e6, "wall_s": dt,
+                     "threads": cores, "sample": f"{label}, {wd.steps} steps"}
+    return out
+
+
+def copy_bandwidth(reps=5):
+    """Attainable HBM bandwidth for context: a plain 1 GiB device-to-device copy,
+    bytes read + written / time (median of `reps`)."""
+    import torch
+
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2]
+    del a, b
+    return {"bytes_per_copy": 2 << 30, "ms": ms, "GBps": (2 << 30) / (ms * 1e-3) / 1e9}
+
+
 def bench_mc_readout(g, gi, stream, reps, digest=None):
     """The cache read-out of the long-context batch, inputs resident, events on the
     launch stream around each call (the small cache-preparation launch included)."""
@@ -412,9 +478,12 @@ def main():
         out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps, digest)
         out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps, digest)
         out["sdm"] = bench_sdm(g, gi, stream, args.mc_reps, digest)
+        out["copy_bandwidth"] = copy_bandwidth()
 
     if not args.no_cpu:
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
+        if not args.only_prefill:
+            out["cpu_baseline_detail"] = cpu_baseline_detail(gi)
     print(json.dumps(out), flush=True)
 
 
