@@ -30,8 +30,11 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates nothing, keeps no pointer after a call returns and has no
- *     global mutable state (calls from several host threads are safe).
+ *     allocates no device memory, keeps no pointer after a call returns and has
+ *     no global mutable state, with one exception: gdr_sdm_fwd creates, on its first
+ *     long call on a device, one side stream (default priority) and a few events that
+ *     it keeps until the process ends; their use is serialised by a mutex.  Calls
+ *     from several host threads are safe.
  *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
  *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
  *     alignment (so per-step slices of a gate array are accepted).
@@ -256,6 +259,9 @@ int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, cons
  *   workspace at least gdr_sdm_workspace_size() bytes
  * Supported: dv == 128, 1 <= n <= 1024, 1 <= W, R <= min(128, n * n) (else
  * GDR_EUNSUPPORTED).  desc->dk, chunk, alpha_mode and beta_mode are not used.
+ * With T >= 1024 the selection of later token blocks runs on a side stream of the
+ * current device, forked from and joined back into `stream` through events (the call
+ * stays in stream order and capturable); `stream` must belong to the current device.
  */
 size_t gdr_sdm_workspace_size(const gdr_desc *desc, int32_t n, int32_t W, int32_t R);
 int gdr_sdm_fwd(const gdr_desc *desc, int32_t n, int32_t W, int32_t R, const float *ks, const float *qs,
