@@ -262,17 +262,22 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
 
 template <bool BF>
 __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
-    __shared__ float kf[kPL + 1][kPD + 1];   // a = k^2 of the chunk; row kPL: sink
-    __shared__ __attribute__((aligned(16))) float Tm[kPL][kPL + 4];  // 16-byte rows
-    __shared__ __attribute__((aligned(16))) float vc[7][kPL];         // c, cb, beta, r, P, rho, (Pn in [6][0])
-    __shared__ float zs[kPL], es[kPL], we[kPL], d[kPD];
+    // chunk operands, double buffered: a = k^2 (rows of 132 floats: 16-byte aligned,
+    // zero past dk; row kPL is a sink), Tm and the vector rows of the record
+    constexpr int kKP = kPD + 4;
+    __shared__ __attribute__((aligned(16))) float kf[2][kPL + 1][kKP];
+    __shared__ __attribute__((aligned(16))) float Tm[2][kPL][kPL + 4];
+    __shared__ __attribute__((aligned(16))) float vc[2][7][kPL];  // c, cb, beta, r, P, rho, (Pn in [6][0])
+    __shared__ __attribute__((aligned(16))) float d[kPD];
+    __shared__ float zs[kPL], we[kPL];
     const int tid = threadIdx.x;
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh % p.H, dk = p.dk;
-    if (tid < dk) d[tid] = p.d0 ? p.d0[(long)bh * dk + tid] : 1.f;
+    for (int i = tid; i < 2 * (kPL + 1) * kKP; i += kPThreads) (&kf[0][0][0])[i] = 0.f;
+    if (tid < kPD) d[tid] = tid < dk ? (p.d0 ? p.d0[(long)bh * dk + tid] : 1.f) : 0.f;
 
-    // register copies of the next two chunks (two sets, used alternately): keys
-    // (16-byte pieces) and the record head (Tm and the vectors: 1,136 pieces)
+    // register copies of two chunks ahead (two sets, used alternately): keys (16-byte
+    // pieces) and the record head (Tm and the vectors: 1,136 pieces)
     constexpr int ksz = BF ? 2 : 4;  // bytes per key element
     const int kpieces = dk * ksz / 16;
     u32x4 kA[8], rA[5], kB[8], rB[5];
@@ -299,7 +304,7 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
             rreg[u] = *reinterpret_cast<const u32x4 *>(rec + 4 * w4);
         }
     };
-    auto store_chunk = [&](int c, const u32x4 (&kreg)[8], const u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+    auto store_chunk = [&](int c, int bf, const u32x4 (&kreg)[8], const u32x4 (&rreg)[5]) __attribute__((always_inline)) {
         const int t0 = c * kPL, n = min(kPL, p.T - t0);
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
@@ -307,53 +312,62 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
             const int row = min(t, kPL);
             const bool live = t < n;
             if (BF) {
+                f32x4 lo, hi;
 #pragma unroll
-                for (int x = 0; x < 4; ++x) {
+                for (int x = 0; x < 2; ++x) {
                     const float k0 = live ? __uint_as_float(kreg[u][x] << 16) : 0.f;
                     const float k1 = live ? __uint_as_float(kreg[u][x] & 0xffff0000u) : 0.f;
-                    kf[row][8 * pc + 2 * x] = k0 * k0;
-                    kf[row][8 * pc + 2 * x + 1] = k1 * k1;
+                    const float k2 = live ? __uint_as_float(kreg[u][x + 2] << 16) : 0.f;
+                    const float k3 = live ? __uint_as_float(kreg[u][x + 2] & 0xffff0000u) : 0.f;
+                    lo[2 * x] = k0 * k0;
+                    lo[2 * x + 1] = k1 * k1;
+                    hi[2 * x] = k2 * k2;
+                    hi[2 * x + 1] = k3 * k3;
                 }
+                *reinterpret_cast<f32x4 *>(&kf[bf][row][8 * pc]) = lo;
+                *reinterpret_cast<f32x4 *>(&kf[bf][row][8 * pc + 4]) = hi;
             } else {
+                f32x4 v;
 #pragma unroll
                 for (int x = 0; x < 4; ++x) {
                     const float k0 = live ? __uint_as_float(kreg[u][x]) : 0.f;
-                    kf[row][4 * pc + x] = k0 * k0;
+                    v[x] = k0 * k0;
                 }
+                *reinterpret_cast<f32x4 *>(&kf[bf][row][4 * pc]) = v;
             }
         }
-        // the record head: Tm rows then the vector rows (one flat LDS view); the
-        // clamped duplicate pieces rewrite the last piece with its own value
+        // the record head: Tm rows then the vector rows; the clamped duplicate pieces
+        // rewrite the last piece with its own value
 #pragma unroll
         for (int u = 0; u < 5; ++u) {
             const int w = 4 * min(tid + kPThreads * u, kPrD0 / 4 - 1);
-            float *dst = w < kPrC ? &Tm[w / kPL][w % kPL] : &vc[(w - kPrC) / kPL][(w - kPrC) % kPL];
+            float *dst = w < kPrC ? &Tm[bf][w / kPL][w % kPL] : &vc[bf][(w - kPrC) / kPL][(w - kPrC) % kPL];
             *reinterpret_cast<f32x4 *>(dst) = __builtin_bit_cast(f32x4, rreg[u]);
         }
     };
 
-    // one chunk of the chain; its operands arrive in (kreg, rreg), which are then
-    // refilled with chunk c + 2
-    auto step = [&](int c, u32x4 (&kreg)[8], u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+    // One chunk of the chain from buffer bf (filled during the previous chunk); at its
+    // end the next chunk is staged into the other buffer from (kn, rn), which are then
+    // refilled with the chunk after that.  Three barriers.
+    auto step = [&](int c, int bf, u32x4 (&kn)[8], u32x4 (&rn)[5]) __attribute__((always_inline)) {
         float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
-        lds_sync();  // the previous chunk is done with kf, Tm, vc, d
-        store_chunk(c, kreg, rreg);
-        if (c + 2 < p.NT) load_chunk(c + 2, kreg, rreg);
+        lds_sync();  // this chunk's operands staged; d of its start complete
         if (tid < dk) rec[kPrD0 + tid] = d[tid];
-        lds_sync();
-        // z_t = c_t - cb_t P_t <a_t, d_0>   (4 lanes per token)
+        // z_t = c_t - cb_t P_t <a_t, d_0>   (4 lanes per token, 32 channels each)
         {
             const int t = tid >> 2, part = tid & 3;
-            float sum = 0.f;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int ii = 0; ii < 32; ++ii) {  // unconditional loads (clamped), masked terms
-                const int i = min(32 * part + ii, dk - 1);
-                const float term = kf[t][i] * d[i];
-                sum += 32 * part + ii < dk ? term : 0.f;
+            for (int m = 0; m < 8; ++m) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&kf[bf][t][32 * part + 4 * m]);
+                const f32x4 dv = *reinterpret_cast<const f32x4 *>(&d[32 * part + 4 * m]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) s4[x] = fmaf(av[x], dv[x], s4[x]);
             }
+            float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
             sum += __shfl_xor(sum, 1);
             sum += __shfl_xor(sum, 2);
-            if (part == 0) zs[t] = vc[0][t] - vc[1][t] * vc[4][t] * sum;
+            if (part == 0) zs[t] = vc[bf][0][t] - vc[bf][1][t] * vc[bf][4][t] * sum;
         }
         lds_sync();
         // e = Tm z
@@ -363,31 +377,46 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
 #pragma unroll
             for (int jj = 0; jj < 16; ++jj) {
                 const int j = 16 * part + jj;  // strictly lower part of Tm (its diagonal is 1)
-                sum = fmaf(j < t ? Tm[t][j] : 0.f, zs[j], sum);
+                sum = fmaf(j < t ? Tm[bf][t][j] : 0.f, zs[j], sum);
             }
             sum += __shfl_xor(sum, 1);
             sum += __shfl_xor(sum, 2);
             if (part == 0) {
-                es[t] = zs[t] + sum;
-                we[t] = vc[5][t] * (zs[t] + sum);
+                we[t] = vc[bf][5][t] * (zs[t] + sum);
                 rec[kPrE + t] = zs[t] + sum;
             }
         }
         lds_sync();
-        // d_n = P_n d_0 + sum_j rho_j e_j a_j   (one key channel per thread)
-        if (tid < dk) {
-            float acc[4] = {vc[6][0] * d[tid], 0.f, 0.f, 0.f};
+        // d_n = P_n d_0 + sum_j rho_j e_j a_j: two lanes per key channel, even and odd j
+        {
+            const int i = tid >> 1, hf = tid & 1;
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int j = 0; j < kPL; ++j) acc[j & 3] = fmaf(we[j], kf[j][tid], acc[j & 3]);
-            d[tid] = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            for (int jj = 0; jj < kPL / 2; ++jj) {
+                const int j = 2 * jj + hf;
+                acc[jj & 3] = fmaf(we[j], kf[bf][j][i], acc[jj & 3]);
+            }
+            float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            sum += __shfl_xor(sum, 1);
+            if (hf == 0 && i < dk) d[i] = vc[bf][6][0] * d[i] + sum;
+        }
+        // stage the next chunk into the other buffer (read last in the previous chunk)
+        if (c + 1 < p.NT) {
+            store_chunk(c + 1, bf ^ 1, kn, rn);
+            if (c + 3 < p.NT) load_chunk(c + 3, kn, rn);
         }
     };
 
-    if (p.NT > 0) load_chunk(0, kA, rA);
-    if (p.NT > 1) load_chunk(1, kB, rB);
+    if (p.NT > 0) {
+        load_chunk(0, kA, rA);
+        if (p.NT > 1) load_chunk(1, kB, rB);
+        __syncthreads();  // the buffers are zeroed
+        store_chunk(0, 0, kA, rA);
+        if (p.NT > 2) load_chunk(2, kA, rA);
+    }
     for (int c = 0; c < p.NT; c += 2) {
-        step(c, kA, rA);
-        if (c + 1 < p.NT) step(c + 1, kB, rB);
+        step(c, 0, kB, rB);
+        if (c + 1 < p.NT) step(c + 1, 1, kA, rA);
     }
     __syncthreads();
     if (p.dT && tid < dk) p.dT[(long)bh * dk + tid] = d[tid];
