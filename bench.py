@@ -27,7 +27,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip",
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip", "gdr_ut.hpp",
                   "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
 
 

@@ -44,6 +44,7 @@
 #include "gdr_device.hpp"
 #include "gdr_internal.hpp"
 #include "gdr_mfma.hpp"
+#include "gdr_ut.hpp"
 
 namespace gdr {
 namespace {
@@ -109,97 +110,6 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // pieces shared by the two prep kernels (256 threads, four waves)
 // ---------------------------------------------------------------------------
-// Tm = (I + A)^{-1} for the strictly lower 64 x 64 A in As, into the lower part of
-// Ts (fp32; the unit diagonal and the upper part are not written).  Ends with a
-// barrier; starts reading As, so the caller has published it with a barrier.
-__device__ __forceinline__ void ut_transform(float (*As)[kC + 4], float (*Ts)[kC + 8], float (*Xs)[16][16],
-                                             const int w, const int l) {
-    const int r = l & 15, q = l >> 4;
-    // diagonal 16 x 16 blocks of (I + A)^{-1}: wave w, lane c < 16 owns column c;
-    // row rr of the block is read as four 16-byte loads
-    if (l < 16) {
-        const int base = 16 * w, cc = l;
-        float col[16];
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) {
-            float a[16];
-#pragma unroll
-            for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&As[base + rr][base + 4 * m4]);
-                a[4 * m4] = x[0];
-                a[4 * m4 + 1] = x[1];
-                a[4 * m4 + 2] = x[2];
-                a[4 * m4 + 3] = x[3];
-            }
-            float v = rr == cc ? 1.f : 0.f;
-#pragma unroll
-            for (int m = 0; m < rr; ++m) v -= a[m] * col[m];
-            col[rr] = v;
-        }
-#pragma unroll
-        for (int rr = 0; rr < 16; ++rr) Ts[base + rr][base + cc] = col[rr];
-    }
-    __syncthreads();
-    // Off-diagonal 16 x 16 blocks on fp32 matrix cores (v_mfma_f32_16x16x4_f32; lane
-    // (r, q) supplies A[r][k] and B[k][r] of k step s, C tiles as for bf16), by the
-    // 2 x 2 block inverse [[T_a, 0], [L, T_b]]^-1 lower-left = -T_b L T_a, first on the
-    // two 32 x 32 diagonal halves, then on the 64 x 64 matrix.
-    {
-        // C = M1 M2 for 16 x 16 blocks of LDS matrices (row pitch ld1, ld2)
-        auto mm = [&](const float *M1, int ld1, const float *M2, int ld2, f32x4 acc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * s4 + q], M2[(4 * s4 + q) * ld2 + r], acc, 0, 0, 0);
-            return acc;
-        };
-        // C = M1 X with X a C tile held in registers: k step s4 takes row 4 q + s4 of X
-        auto mmr = [&](const float *M1, int ld1, f32x4 X, f32x4 acc) __attribute__((always_inline)) {
-#pragma unroll
-            for (int s4 = 0; s4 < 4; ++s4)
-                acc = __builtin_amdgcn_mfma_f32_16x16x4f32(M1[r * ld1 + 4 * q + s4], X[s4], acc, 0, 0, 0);
-            return acc;
-        };
-        auto Ab = [&](int I, int J) { return &As[16 * I][16 * J]; };
-        auto Tb = [&](int I, int J) { return &Ts[16 * I][16 * J]; };
-        constexpr int LA = kC + 4, LT = kC + 8;
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        auto storeT = [&](int I, int J, f32x4 v) __attribute__((always_inline)) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) Ts[16 * I + 4 * q + i][16 * J + r] = -v[i];
-        };
-        // level 1: T_10 (wave 0), T_32 (wave 1); waves 2, 3 start the 64 x 64 level
-        f32x4 xa = z, xb = z;
-        if (w < 2) {
-            const int o = 2 * w;  // block offset of this 32 x 32 half
-            const f32x4 x = mm(Ab(o + 1, o), LA, Tb(o, o), LT, z);
-            storeT(o + 1, o, mmr(Tb(o + 1, o + 1), LT, x, z));
-        } else {
-            const int I = w;      // X_I0 (partial) and X_I1 = A_I1 T_11 for block row I = 2, 3
-            xa = mm(Ab(I, 0), LA, Tb(0, 0), LT, z);
-            xb = mm(Ab(I, 1), LA, Tb(1, 1), LT, z);
-        }
-        __syncthreads();
-        if (w >= 2) {  // X_I0 += A_I1 T_10; publish X_I0, X_I1
-            const int I = w;
-            xa = mm(Ab(I, 1), LA, Tb(1, 0), LT, xa);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                Xs[2 * (I - 2)][4 * q + i][r] = xa[i];
-                Xs[2 * (I - 2) + 1][4 * q + i][r] = xb[i];
-            }
-        }
-        __syncthreads();
-        {   // T_IJ = -sum_{M=2}^{I} T_IM X_MJ for I = 2 + (w >> 1), J = w & 1
-            const int I = 2 + (w >> 1), J = w & 1;
-            f32x4 t = mm(Tb(I, 2), LT, &Xs[J][0][0], 16, z);
-            if (I == 3) t = mm(Tb(3, 3), LT, &Xs[2 + J][0][0], 16, t);
-            storeT(I, J, t);
-        }
-        __syncthreads();
-    }
-
-}
-
 // The lower-triangular Tm (fp32 rows in Ts, unit diagonal implied) to the record as
 // bf16 rows of 64, 16 bytes per store.
 __device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[kC + 8], const int tid) {

@@ -34,6 +34,7 @@
 #include "gdr_device.hpp"
 #include "gdr_internal.hpp"
 #include "gdr_mfma.hpp"
+#include "gdr_ut.hpp"
 
 namespace gdr {
 namespace {
@@ -73,8 +74,10 @@ constexpr float kRMin = 1e-30f;
 // 16-byte piece of the tile is requested before any is written out.  Loads are
 // unconditional (rows clamped to the chunk) so that the compiler can count them;
 // pieces past row 63 land in the sink row kPL of kf.
-template <bool BF>
-__device__ __forceinline__ void load_keys(const PcParams &p, float (*kf)[kPD + 1], long tok0, int n, int tid) {
+template <bool BF, int PITCH, bool SQ = false>
+__device__ __forceinline__ void load_keys(const PcParams &p, float (*kf)[PITCH], long tok0, int n, int tid) {
+    // the keys of one chunk into rows of kf (k^2 when SQ); rows past the chunk end and
+    // pieces past the 64 rows go to row kPL (the sink) as zeros
     constexpr int es = BF ? 2 : 4;
     const int kpieces = p.dk * es / 16;
     const char *kb = static_cast<const char *>(p.k);
@@ -89,15 +92,21 @@ __device__ __forceinline__ void load_keys(const PcParams &p, float (*kf)[kPD + 1
         const int e = tid + kPThreads * u, t = e / kpieces, pc = e % kpieces;
         const int row = min(t, kPL);
         const bool live = t < n;
-        if (BF) {
+        constexpr int nv = BF ? 8 : 4;
+        float x[nv];
 #pragma unroll
-            for (int x = 0; x < 4; ++x) {
-                kf[row][8 * pc + 2 * x] = live ? __uint_as_float(v[u][x] << 16) : 0.f;
-                kf[row][8 * pc + 2 * x + 1] = live ? __uint_as_float(v[u][x] & 0xffff0000u) : 0.f;
-            }
+        for (int j = 0; j < nv; ++j) {
+            const uint32_t wd = v[u][BF ? j >> 1 : j];
+            const float f = BF ? __uint_as_float((j & 1) ? (wd & 0xffff0000u) : (wd << 16)) : __uint_as_float(wd);
+            x[j] = live ? (SQ ? f * f : f) : 0.f;
+        }
+        if (PITCH % 4 == 0) {  // 16-byte rows: vector writes
+#pragma unroll
+            for (int j = 0; j < nv; j += 4)
+                *reinterpret_cast<f32x4 *>(&kf[row][nv * pc + j]) = f32x4{x[j], x[j + 1], x[j + 2], x[j + 3]};
         } else {
 #pragma unroll
-            for (int x = 0; x < 4; ++x) kf[row][4 * pc + x] = live ? __uint_as_float(v[u][x]) : 0.f;
+            for (int j = 0; j < nv; ++j) kf[row][nv * pc + j] = x[j];
         }
     }
 }
@@ -109,10 +118,12 @@ __device__ __forceinline__ void lds_sync() { asm volatile("s_waitcnt lgkmcnt(0)\
 
 template <bool BF>
 __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
-    __shared__ float a[kPL + 1][kPD + 1];  // row kPL: sink of the key copy
-    __shared__ float A[kPL][kPL + 1];    // A (strictly lower)
-    __shared__ float Ti[kPL][kPL + 1];   // Tm, strictly lower part (the unit diagonal is implicit)
-    __shared__ float W[3][16][17];       // off-diagonal block sums
+    // row kPL: sink of the key copy; a row pitch of 4 mod 64 words keeps the
+    // 16 x 4 fragment reads of the Gram products free of bank conflicts
+    __shared__ __attribute__((aligned(16))) float a[kPL + 1][kPD + 4];
+    __shared__ __attribute__((aligned(16))) float A[kPL][kPL + 4];   // A (strictly lower)
+    __shared__ __attribute__((aligned(16))) float Ti[kPL][kPL + 8];  // Tm, strictly lower part (unit diagonal implicit)
+    __shared__ __attribute__((aligned(16))) float Xs[4][16][16];     // UT transform scratch
     __shared__ float nk[kPL], lg[kPL + 1], cb[kPL];
     const int tid = threadIdx.x;
     const long blk = blockIdx.x;
@@ -129,26 +140,24 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
         bt = ld_elem(p.beta, tk, p.gate_bf16);
         if (p.r) rt = ld_elem(p.r, tk, p.gate_bf16);
     }
-    load_keys<BF>(p, a, tok0, n, tid);
+    load_keys<BF, kPD + 4, true>(p, a, tok0, n, tid);
     __syncthreads();
-    {  // |k_t|^2 (4 lanes per row), then a = k^2
+    {  // |k_t|^2 = sum of the row of a = k^2 (4 lanes per row, 16-byte reads)
         const int t = tid >> 2, part = tid & 3;
-        float s = 0.f;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ii = 0; ii < 32; ++ii) {
-            const int i = min(32 * part + ii, dk - 1);
-            const float term = a[t][i] * a[t][i];
-            s += 32 * part + ii < dk ? term : 0.f;
+        for (int m = 0; m < 8; ++m) {
+            const int i0 = 32 * part + 4 * m;
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(&a[t][min(i0, kPD - 4)]);
+#pragma unroll
+            for (int y = 0; y < 4; ++y) s4[y] += i0 + y < dk ? x[y] : 0.f;
         }
+        float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         if (part == 0) nk[t] = s;
     }
-    __syncthreads();
-    for (int e = tid; e < kPL * kPD; e += kPThreads) {
-        const int t = e / kPD, i = e % kPD;
-        if (i < dk) a[t][i] *= a[t][i];
-    }
+    __syncthreads();  // nk is read by wave 0 below
     if (tid < kPL) {  // one wave: coefficients and the cumulative log retention (scan)
         const int t = tid;
         const float ct = nk[t] > 0.f ? p.eta * bt / nk[t] : 0.f;
@@ -174,86 +183,50 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
         if (tid == 0) rec[kPrPn] = expf(ln);
     }
 
-    // A_{tj} = cb_t (P_t / P_{j+1}) <a_t, a_j> for j < t < n, a 4 x 4 block per thread
+    // A_{tj} = cb_t (P_t / P_{j+1}) <a_t, a_j> for j < t < n.  The Gram products on fp32
+    // matrix cores (v_mfma_f32_16x16x4_f32: lane (r, q) supplies A[r][q] and B[q][r] of a
+    // 4-channel step, C tiles hold C[4q .. 4q+3][r]): the ten 16 x 16 tiles on or below
+    // the diagonal, three or two per wave, each pass over the channels reading one
+    // fragment per tile row and column.
     {
-        const int tb = 4 * (tid >> 4), jb = 4 * (tid & 15);
-        float g[4][4] = {};
-        if (jb <= tb + 3) {
-#pragma unroll 8
-            for (int i = 0; i < dk; ++i) {
-                float at[4], aj[4];
+        const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
+        // tiles (I, J) of wave w: 0: (0,0) (1,0) (1,1); 1: (2,0) (2,1) (2,2); 2: (3,0) (3,1); 3: (3,2) (3,3)
+        const int I0 = w == 0 ? 0 : w == 1 ? 2 : 3;
+        const int J0 = w < 2 ? 0 : w == 2 ? 0 : 2;
+        const int nt = w < 2 ? 3 : 2;
+        // tile k of the wave: row I, column J
+        auto tI = [&](int k) { return w == 0 ? (k == 0 ? 0 : 1) : I0; };
+        auto tJ = [&](int k) { return w == 0 ? (k == 2 ? 1 : 0) : J0 + k; };
+        f32x4 acc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const int ksteps = (dk + 3) / 4;
+        for (int st = 0; st < ksteps; ++st) {
+            const int ch = 4 * st + q;  // dk is a multiple of 8
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    at[e] = a[tb + e][i];
-                    aj[e] = a[jb + e][i];
+            for (int k = 0; k < 3; ++k) {
+                if (k < nt) {
+                    const float av = a[16 * tI(k) + r][ch];
+                    const float bv = a[16 * tJ(k) + r][ch];
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[k], 0, 0, 0);
                 }
-#pragma unroll
-                for (int x = 0; x < 4; ++x)
-#pragma unroll
-                    for (int y = 0; y < 4; ++y) g[x][y] = fmaf(at[x], aj[y], g[x][y]);
             }
         }
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int k = 0; k < 3; ++k) {
+            if (k < nt) {
 #pragma unroll
-            for (int y = 0; y < 4; ++y) {
-                const int t = tb + x, j = jb + y;
-                A[t][j] = (j < t && t < n) ? cb[t] * expf(lg[t] - lg[j + 1]) * g[x][y] : 0.f;
+                for (int i = 0; i < 4; ++i) {
+                    const int t = 16 * tI(k) + 4 * q + i, j = 16 * tJ(k) + r;
+                    A[t][j] = (j < t && t < n) ? cb[t] * expf(lg[t] - lg[j + 1]) * acc[k][i] : 0.f;
+                }
             }
+        }
+        // the tiles above the diagonal are never read (A is strictly lower)
     }
     __syncthreads();
 
-    // Tm = (I + A)^{-1}.  Diagonal 16 x 16 blocks: thread (block I, column j) solves
-    // (I + A_II) x = e_j by forward substitution, x in registers.
-    {
-        float x[16];
-        const int I = tid >> 4, j = tid & 15, base = 16 * I;
-        if (tid < 64) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                float v = t == j ? 1.f : 0.f;
-#pragma unroll
-                for (int s = 0; s < 16; ++s)
-                    if (s < t) v -= A[base + t][base + s] * x[s];
-                x[t] = t < j ? 0.f : v;
-            }
-        }
-        if (tid < 64) {
-#pragma unroll
-            for (int t = 0; t < 16; ++t)
-                if (t > j) Ti[base + t][base + j] = x[t];
-        }
-        __syncthreads();
-    }
-    // off-diagonal blocks, by distance dI = I - J from the diagonal:
-    //     Tm_IJ = - Tm_II * sum_{K = J}^{I - 1} A_IK Tm_KJ      (Tm_JJ's diagonal is 1)
-    // with the original A; every Tm_KJ used (K - J < dI) is final when distance dI runs.
-    auto tm = [&](int r, int c) -> float { return r == c ? 1.f : (c < r ? Ti[r][c] : 0.f); };
-    for (int dI = 1; dI < 4; ++dI) {
-        const int nb = 4 - dI;  // blocks at this distance: (J + dI, J), J < nb
-        for (int e = tid; e < nb * 256; e += kPThreads) {
-            const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + dI;
-            float v = 0.f;
-#pragma unroll
-            for (int dK = 0; dK < 3; ++dK) {
-                const int K = J + dK;
-                if (K < I) {
-#pragma unroll
-                    for (int s = 0; s < 16; ++s) v += A[16 * I + rr][16 * K + s] * tm(16 * K + s, 16 * J + cc);
-                }
-            }
-            W[J][rr][cc] = v;
-        }
-        __syncthreads();
-        for (int e = tid; e < nb * 256; e += kPThreads) {
-            const int J = e >> 8, rr = (e >> 4) & 15, cc = e & 15, I = J + dI;
-            float v = 0.f;
-#pragma unroll
-            for (int s = 0; s < 16; ++s) v += tm(16 * I + rr, 16 * I + s) * W[J][s][cc];
-            Ti[16 * I + rr][16 * J + cc] = -v;
-        }
-        __syncthreads();
-    }
+    // Tm = (I + A)^{-1}: diagonal 16 x 16 blocks by forward substitution, the others by
+    // the 2 x 2 block-inverse rule on fp32 matrix cores
+    ut_transform(A, Ti, Xs, tid >> 6, tid & 63);
     for (int e = tid; e < kPL * kPL; e += kPThreads) {
         const int t = e / kPL, j = e % kPL;
         rec[kPrT + e] = j < t ? Ti[t][j] : (j == t ? 1.f : 0.f);
@@ -435,7 +408,7 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
     const int t0 = c * kPL, n = min(kPL, p.T - t0);
     float *rec = p.rec + blk * kPrWords;
     const long tok0 = ((long)b * p.T + t0) * p.H + h;
-    load_keys<BF>(p, kf, tok0, n, tid);
+    load_keys<BF, kPD + 1>(p, kf, tok0, n, tid);
     if (tid < kPL) {
         vr[tid] = rec[kPrR + tid];
         ve[tid] = rec[kPrE + tid];
