@@ -191,6 +191,9 @@ __global__ void __launch_bounds__(256) mc_readout_kernel(McParams p, int ntb, in
                 bf[0][kk] = mt_frag(Mh, r, kk, q);
                 bf[0][4 + kk] = mt_frag(Ml, r, kk, q);
             }
+            // the products of tile ct go to tmp[ct & 1]; tile ct - 1's gated add runs on the
+            // vector ALU while they execute
+            f32x4 tmp[2][4];
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
                 const int cur = ct & 1;
@@ -202,19 +205,22 @@ __global__ void __launch_bounds__(256) mc_readout_kernel(McParams p, int ntb, in
                     }
                 }
                 __builtin_amdgcn_sched_barrier(0);
-                f32x4 tmp[4];
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) tmp[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int tt = 0; tt < 4; ++tt) tmp[cur][tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
-                        tmp[tt] = mfma(as_bf16x8(qa[tt][kk]), as_bf16x8(bf[cur][kk]), tmp[tt]);
-                        tmp[tt] = mfma(as_bf16x8(qa[tt][kk]), as_bf16x8(bf[cur][4 + kk]), tmp[tt]);
+                        tmp[cur][tt] = mfma(as_bf16x8(qa[tt][kk]), as_bf16x8(bf[cur][kk]), tmp[cur][tt]);
+                        tmp[cur][tt] = mfma(as_bf16x8(qa[tt][kk]), as_bf16x8(bf[cur][4 + kk]), tmp[cur][tt]);
                     }
+                if (ct > 0) {
 #pragma unroll
-                for (int tt = 0; tt < 4; ++tt) acc[tt][ct] += wt[tt] * tmp[tt];
+                    for (int tt = 0; tt < 4; ++tt) acc[tt][ct - 1] += wt[tt] * tmp[cur ^ 1][tt];
+                }
             }
+#pragma unroll
+            for (int tt = 0; tt < 4; ++tt) acc[tt][7] += wt[tt] * tmp[1][tt];
         }
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the next matrix has landed
         __syncthreads();                     // and this buffer is free again
