@@ -397,8 +397,11 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
 
 template <bool BF>
 __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
-    __shared__ float kf[kPL + 1][kPD + 1];  // row kPL: sink of the key copy
-    __shared__ float kw[kPL][kPD + 1];
+    // rows of 132 floats (16-byte aligned, 4 mod 64 words: a column read by 64 lanes
+    // touches 64 banks); row kPL of kf is the sink of the key copy
+    constexpr int kKP = kPD + 4;
+    __shared__ __attribute__((aligned(16))) float kf[kPL + 1][kKP];
+    __shared__ __attribute__((aligned(16))) float kw[kPL][kKP];
     __shared__ float vr[kPL], ve[kPL], vb[kPL];
     __shared__ double red[kPThreads / 64];
     const int tid = threadIdx.x;
@@ -408,7 +411,7 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
     const int t0 = c * kPL, n = min(kPL, p.T - t0);
     float *rec = p.rec + blk * kPrWords;
     const long tok0 = ((long)b * p.T + t0) * p.H + h;
-    load_keys<BF, kPD + 1>(p, kf, tok0, n, tid);
+    load_keys<BF, kKP>(p, kf, tok0, n, tid);
     if (tid < kPL) {
         vr[tid] = rec[kPrR + tid];
         ve[tid] = rec[kPrE + tid];
@@ -434,13 +437,16 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
     double logsum = 0.0;
     {
         const int t = tid >> 2, part = tid & 3;
-        float s = 0.f;
+        float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ii = 0; ii < 32; ++ii) {
-            const int i = min(32 * part + ii, dk - 1);
-            const float term = kw[t][i] * kf[t][i];
-            s += 32 * part + ii < dk ? term : 0.f;
+        for (int m = 0; m < 8; ++m) {
+            const int i0 = 32 * part + 4 * m, ic = min(i0, kPD - 4);
+            const f32x4 x = *reinterpret_cast<const f32x4 *>(&kw[t][ic]);
+            const f32x4 y = *reinterpret_cast<const f32x4 *>(&kf[t][ic]);
+#pragma unroll
+            for (int z = 0; z < 4; ++z) s4[z] += i0 + z < dk ? x[z] * y[z] : 0.f;
         }
+        float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
         s += __shfl_xor(s, 1);
         s += __shfl_xor(s, 2);
         if (part == 0 && t < n) {
@@ -458,16 +464,17 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
             const int t = e / opieces, pc = e % opieces;
             char *dst = static_cast<char *>(p.kw) + (tok0 + (long)t * p.H) * dk * es + 16 * pc;
             if (BF) {
+                const f32x4 lo = *reinterpret_cast<const f32x4 *>(&kw[t][8 * pc]);
+                const f32x4 hi = *reinterpret_cast<const f32x4 *>(&kw[t][8 * pc + 4]);
                 uint32_t w[4];
 #pragma unroll
-                for (int x = 0; x < 4; ++x)
-                    w[x] = (uint32_t)f32_to_bf16(kw[t][8 * pc + 2 * x]) |
-                           ((uint32_t)f32_to_bf16(kw[t][8 * pc + 2 * x + 1]) << 16);
+                for (int x = 0; x < 2; ++x) {
+                    w[x] = (uint32_t)f32_to_bf16(lo[2 * x]) | ((uint32_t)f32_to_bf16(lo[2 * x + 1]) << 16);
+                    w[x + 2] = (uint32_t)f32_to_bf16(hi[2 * x]) | ((uint32_t)f32_to_bf16(hi[2 * x + 1]) << 16);
+                }
                 *reinterpret_cast<u32x4 *>(dst) = u32x4{w[0], w[1], w[2], w[3]};
             } else {
-                *reinterpret_cast<u32x4 *>(dst) =
-                    u32x4{__float_as_uint(kw[t][4 * pc]), __float_as_uint(kw[t][4 * pc + 1]),
-                          __float_as_uint(kw[t][4 * pc + 2]), __float_as_uint(kw[t][4 * pc + 3])};
+                *reinterpret_cast<u32x4 *>(dst) = __builtin_bit_cast(u32x4, *reinterpret_cast<const f32x4 *>(&kw[t][4 * pc]));
             }
         }
     }
