@@ -89,7 +89,17 @@ class GdrError(RuntimeError):
 
 
 def _ptr(t: Optional[torch.Tensor]):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a tensor for the library, which reads every tensor as dense
+    row-major device memory: a view with other strides or a host tensor is refused
+    here (ValueError) instead of being read wrongly or faulting on the device."""
+    if t is None:
+        return None
+    if isinstance(t, torch.Tensor):
+        if not t.is_contiguous():
+            raise ValueError("expected a contiguous (dense row-major) tensor")
+        if t.device.type != "cuda":
+            raise ValueError(f"expected a device tensor, got one on {t.device}")
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream(stream) -> ctypes.c_void_p:

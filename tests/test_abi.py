@@ -248,3 +248,17 @@ def test_sdm_validation(g):
     assert call(d, wb=need - 8) == g.GDR_EWORKSPACE
     assert call(_desc(g, B=0)) == g.GDR_OK                               # nothing to do
     assert call(_desc(g, T=50, io_dtype=5)) == g.GDR_EINVAL
+
+
+def test_binding_refuses_host_and_strided_tensors(g):
+    """The binding passes raw addresses: a host tensor or a non-contiguous view is
+    refused before any call reaches the library."""
+    import torch
+
+    d = _desc(g, B=1, T=4, H=1, dk=8, dv=8, io_dtype=g.GDR_F32)
+    host = torch.zeros((1, 1, 8))
+    with pytest.raises(ValueError, match="device tensor"):
+        g.gdr_decode_step(d, host, host, None, host, host, host, None, host, host, 0)
+    with pytest.raises(ValueError, match="contiguous"):
+        g._ptr(torch.zeros((4, 4)).t())
+    assert g._ptr(None) is None
