@@ -5,7 +5,41 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace gdr {
+
+// A side stream of one module on one device, with events for forking work off the
+// caller's stream and joining it back.  Created on the module's first call on the
+// device (default priority, non-blocking) and kept until the process ends; the
+// host-side enqueue of a call is serialised by `mu`.  The fork / join through events
+// keeps a call capturable in a HIP graph of the caller's stream.
+constexpr int kSideMaxDevices = 64;
+constexpr int kSideEvents = 66;
+struct SideStream {
+    std::mutex mu;
+    bool ready = false;
+    hipStream_t stream = nullptr;
+    hipEvent_t ev[kSideEvents] = {};
+};
+
+// The entry of `table` for the current device, created if needed.  The caller holds
+// `side->mu` while it enqueues (locked here on success).
+inline hipError_t side_stream_acquire(SideStream (&table)[kSideMaxDevices], SideStream *&side,
+                                      std::unique_lock<std::mutex> &lock) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kSideMaxDevices) return hipErrorInvalidDevice;
+    side = &table[dev];
+    lock = std::unique_lock<std::mutex>(side->mu);
+    if (side->ready) return hipSuccess;
+    e = hipStreamCreateWithFlags(&side->stream, hipStreamNonBlocking);
+    for (int j = 0; j < kSideEvents && e == hipSuccess; ++j)
+        e = hipEventCreateWithFlags(&side->ev[j], hipEventDisableTiming);
+    if (e == hipSuccess) side->ready = true;
+    return e;
+}
 
 // Parameters of one prefill call, already validated by the host API.
 struct ChunkParams {

@@ -28,7 +28,12 @@
 //   osdn_qgeo_kernel    q_geo per (batch, head) from the chunk sums, in chunk order.
 // Everything is fp32 (exact products of the stored keys) except the log-ratio
 // sums (fp64).  The chain is the only sequential part: three small matrix-vector
-// products per chunk.
+// products per chunk, on one workgroup per (batch, head).  For a long sequence the
+// chunks are cut into blocks: the chunk solve of every block and the emission of
+// each finished block run on a side stream while the chain works through the
+// blocks in order on the caller's stream (it occupies one CU per sequence, so the
+// parallel passes fill the others); the chain carries d from one block to the next
+// through the next chunk's record.
 #include <math.h>
 
 #include "gdr_device.hpp"
@@ -59,6 +64,7 @@ constexpr int kPrWords = kPrLog + kPL;     // 4800 words = 19,200 bytes
 
 struct PcParams {
     int B, T, H, dk, io_bf16, gate_bf16, NT;
+    int c0, c1;  // the launch covers chunks c0 .. c1 - 1 of every (batch, head)
     float eta;
     const void *k, *beta, *r;
     const float *d0;
@@ -126,11 +132,11 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
     __shared__ __attribute__((aligned(16))) float Xs[4][16][16];     // UT transform scratch
     __shared__ float nk[kPL], lg[kPL + 1], cb[kPL];
     const int tid = threadIdx.x;
-    const long blk = blockIdx.x;
-    const int bh = (int)(blk / p.NT), c = (int)(blk % p.NT);
+    const int nc = p.c1 - p.c0;
+    const int bh = (int)(blockIdx.x / nc), c = p.c0 + (int)(blockIdx.x % nc);
     const int b = bh / p.H, h = bh % p.H, dk = p.dk;
     const int t0 = c * kPL, n = min(kPL, p.T - t0);
-    float *rec = p.rec + blk * kPrWords;
+    float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
     const long tok0 = ((long)b * p.T + t0) * p.H + h;
 
     // this token's gates are requested together with the keys
@@ -247,7 +253,15 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh % p.H, dk = p.dk;
     for (int i = tid; i < 2 * (kPL + 1) * kKP; i += kPThreads) (&kf[0][0][0])[i] = 0.f;
-    if (tid < kPD) d[tid] = tid < dk ? (p.d0 ? p.d0[(long)bh * dk + tid] : 1.f) : 0.f;
+    // d at the start of chunk c0: the initial preconditioner, or (a later block of
+    // chunks) what the launch for the block before left in chunk c0's record
+    if (tid < kPD) {
+        float v = 0.f;
+        if (tid < dk)
+            v = p.c0 > 0 ? p.rec[((long)bh * p.NT + p.c0) * kPrWords + kPrD0 + tid]
+                         : (p.d0 ? p.d0[(long)bh * dk + tid] : 1.f);
+        d[tid] = v;
+    }
 
     // register copies of two chunks ahead (two sets, used alternately): keys (16-byte
     // pieces) and the record head (Tm and the vectors: 1,136 pieces)
@@ -374,25 +388,29 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
             if (hf == 0 && i < dk) d[i] = vc[bf][6][0] * d[i] + sum;
         }
         // stage the next chunk into the other buffer (read last in the previous chunk)
-        if (c + 1 < p.NT) {
+        if (c + 1 < p.c1) {
             store_chunk(c + 1, bf ^ 1, kn, rn);
-            if (c + 3 < p.NT) load_chunk(c + 3, kn, rn);
+            if (c + 3 < p.c1) load_chunk(c + 3, kn, rn);
         }
     };
 
-    if (p.NT > 0) {
-        load_chunk(0, kA, rA);
-        if (p.NT > 1) load_chunk(1, kB, rB);
+    const int c0 = p.c0, c1 = p.c1;
+    if (c1 > c0) {
+        load_chunk(c0, kA, rA);
+        if (c0 + 1 < c1) load_chunk(c0 + 1, kB, rB);
         __syncthreads();  // the buffers are zeroed
-        store_chunk(0, 0, kA, rA);
-        if (p.NT > 2) load_chunk(2, kA, rA);
+        store_chunk(c0, 0, kA, rA);
+        if (c0 + 2 < c1) load_chunk(c0 + 2, kA, rA);
     }
-    for (int c = 0; c < p.NT; c += 2) {
+    for (int c = c0; c < c1; c += 2) {
         step(c, 0, kB, rB);
-        if (c + 1 < p.NT) step(c + 1, 1, kA, rA);
+        if (c + 1 < c1) step(c + 1, 1, kA, rA);
     }
     __syncthreads();
-    if (p.dT && tid < dk) p.dT[(long)bh * dk + tid] = d[tid];
+    if (tid < dk) {
+        if (c1 < p.NT) p.rec[((long)bh * p.NT + c1) * kPrWords + kPrD0 + tid] = d[tid];  // the next block's start
+        else if (p.dT) p.dT[(long)bh * dk + tid] = d[tid];
+    }
 }
 
 template <bool BF>
@@ -405,11 +423,11 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
     __shared__ float vr[kPL], ve[kPL], vb[kPL];
     __shared__ double red[kPThreads / 64];
     const int tid = threadIdx.x;
-    const long blk = blockIdx.x;
-    const int bh = (int)(blk / p.NT), c = (int)(blk % p.NT);
+    const int nc = p.c1 - p.c0;
+    const int bh = (int)(blockIdx.x / nc), c = p.c0 + (int)(blockIdx.x % nc);
     const int b = bh / p.H, h = bh % p.H, dk = p.dk;
     const int t0 = c * kPL, n = min(kPL, p.T - t0);
-    float *rec = p.rec + blk * kPrWords;
+    float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
     const long tok0 = ((long)b * p.T + t0) * p.H + h;
     load_keys<BF, kKP>(p, kf, tok0, n, tid);
     if (tid < kPL) {
@@ -511,6 +529,12 @@ size_t osdn_precond_workspace(int B, int T, int H) {
     return (size_t)B * H * NT * kPrWords * sizeof(float);
 }
 
+namespace {
+constexpr int kOsdnBlocks = 32;  // most chunk blocks of a call
+static_assert(2 + 2 * kOsdnBlocks <= kSideEvents, "events of one call");
+SideStream g_osdn_side[kSideMaxDevices];
+}  // namespace
+
 hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
                                const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
                                void *ws, hipStream_t st) {
@@ -519,34 +543,65 @@ hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gat
     PcParams p;
     p.B = B; p.T = T; p.H = H; p.dk = dk; p.io_bf16 = io_bf16; p.gate_bf16 = gate_bf16;
     p.NT = (T + kPL - 1) / kPL;
+    p.c0 = 0;
+    p.c1 = p.NT;
     p.eta = eta;
     p.k = k; p.beta = beta; p.r = r; p.d0 = d0; p.kw = kw; p.dT = dT; p.qgeo = qgeo;
     p.rec = static_cast<float *>(ws);
-    void *args[] = {&p};
+    const void *chunk_fn = io_bf16 ? reinterpret_cast<const void *>(&osdn_chunk_kernel<true>)
+                                   : reinterpret_cast<const void *>(&osdn_chunk_kernel<false>);
+    const void *chain_fn = io_bf16 ? reinterpret_cast<const void *>(&osdn_chain_kernel<true>)
+                                   : reinterpret_cast<const void *>(&osdn_chain_kernel<false>);
+    const void *emit_fn = io_bf16 ? reinterpret_cast<const void *>(&osdn_emit_kernel<true>)
+                                  : reinterpret_cast<const void *>(&osdn_emit_kernel<false>);
+    // chunks c0 .. c1 - 1: one block per (batch, head, chunk), or (the chain) one per (batch, head)
+    auto launch = [&](const void *fn, int c0, int c1, hipStream_t s) -> hipError_t {
+        PcParams a = p;
+        a.c0 = c0;
+        a.c1 = c1;
+        void *args[] = {&a};
+        const long grid = fn == chain_fn ? nbh : nbh * (c1 - c0);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kPThreads), args, 0, s);
+    };
+    auto finish = [&]() -> hipError_t {
+        if (!qgeo) return hipSuccess;
+        void *args[] = {&p};
+        return hipLaunchKernel(reinterpret_cast<const void *>(&osdn_qgeo_kernel), dim3((unsigned)nbh),
+                               dim3(kPThreads), args, 0, st);
+    };
     hipError_t e;
-    if (p.NT > 0) {
-        e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_chunk_kernel<true>)
-                                    : reinterpret_cast<const void *>(&osdn_chunk_kernel<false>),
-                            dim3((unsigned)(nbh * p.NT)),
-                            dim3(kPThreads), args, 0, st);
-        if (e != hipSuccess) return e;
+    const int nblk = p.NT >= 256 ? min(kOsdnBlocks, p.NT / 64) : 1;
+    if (nblk == 1) {
+        if (p.NT > 0 && (e = launch(chunk_fn, 0, p.NT, st)) != hipSuccess) return e;
+        if ((e = launch(chain_fn, 0, p.NT, st)) != hipSuccess) return e;  // with no chunk: dT = d0
+        if (p.NT > 0 && (e = launch(emit_fn, 0, p.NT, st)) != hipSuccess) return e;
+        return finish();
     }
-    e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_chain_kernel<true>)
-                                : reinterpret_cast<const void *>(&osdn_chain_kernel<false>),
-                        dim3((unsigned)nbh), dim3(kPThreads),
-                        args, 0, st);
-    if (e != hipSuccess) return e;
-    if (p.NT > 0) {
-        e = hipLaunchKernel(io_bf16 ? reinterpret_cast<const void *>(&osdn_emit_kernel<true>)
-                                    : reinterpret_cast<const void *>(&osdn_emit_kernel<false>),
-                            dim3((unsigned)(nbh * p.NT)),
-                            dim3(kPThreads), args, 0, st);
-        if (e != hipSuccess) return e;
+    SideStream *sd = nullptr;
+    std::unique_lock<std::mutex> lock;
+    if ((e = side_stream_acquire(g_osdn_side, sd, lock)) != hipSuccess) return e;
+    hipEvent_t fork = sd->ev[0], join = sd->ev[1], *solved = sd->ev + 2, *chained = sd->ev + 2 + kOsdnBlocks;
+    auto bound = [&](int j) { return (int)((long)p.NT * j / nblk); };
+    // side: every block's chunk solve; caller's stream: the chain, block by block, each
+    // after its block's solve; side again: each block's emission after its chain
+    if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;  // inputs ready on st
+    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = launch(chunk_fn, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(solved[j], sd->stream)) != hipSuccess) return e;
     }
-    if (qgeo)
-        e = hipLaunchKernel(reinterpret_cast<const void *>(&osdn_qgeo_kernel), dim3((unsigned)nbh),
-                            dim3(kPThreads), args, 0, st);
-    return e;
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = hipStreamWaitEvent(st, solved[j], 0)) != hipSuccess) return e;
+        if ((e = launch(chain_fn, bound(j), bound(j + 1), st)) != hipSuccess) return e;
+        if ((e = hipEventRecord(chained[j], st)) != hipSuccess) return e;
+    }
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = hipStreamWaitEvent(sd->stream, chained[j], 0)) != hipSuccess) return e;
+        if ((e = launch(emit_fn, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
+    }
+    if ((e = hipEventRecord(join, sd->stream)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(st, join, 0)) != hipSuccess) return e;
+    return finish();
 }
 
 }  // namespace gdr

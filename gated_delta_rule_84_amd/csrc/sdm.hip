@@ -620,30 +620,11 @@ size_t sdm_workspace(int B, int T, int H, int W, int R) {
 // The selection of a block of tokens runs on a side stream while the table pass works
 // through the blocks before it on the caller's stream: the table pass holds one
 // workgroup per CU and is latency bound, so the selection's blocks fill the rest of
-// each CU.  The table pass of block j waits for the selection of block j only.  The
-// side stream and its events are created once per device (default priority) and
-// reused; the host-side enqueue is serialised per device by a mutex.  The fork / join
-// through events also keeps the call capturable in a HIP graph of the caller's stream.
+// each CU.  The table pass of block j waits for the selection of block j only.
 namespace {
-constexpr int kSdmMaxDev = 64;
 constexpr int kSdmBlocks = 64;    // most token blocks of a call (blocks of >= 128 tokens)
-struct SdmSide {
-    std::mutex mu;
-    bool ready = false;
-    hipStream_t side = nullptr;
-    hipEvent_t fork = nullptr, done[kSdmBlocks] = {};
-};
-SdmSide g_side[kSdmMaxDev];
-
-hipError_t sdm_side_init(SdmSide &sd) {
-    if (sd.ready) return hipSuccess;
-    hipError_t e = hipStreamCreateWithFlags(&sd.side, hipStreamNonBlocking);
-    if (e != hipSuccess) return e;
-    e = hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming);
-    for (int j = 0; j < kSdmBlocks && e == hipSuccess; ++j) e = hipEventCreateWithFlags(&sd.done[j], hipEventDisableTiming);
-    if (e == hipSuccess) sd.ready = true;
-    return e;
-}
+static_assert(kSdmBlocks + 1 <= kSideEvents, "events of one call");
+SideStream g_sdm_side[kSideMaxDevices];
 }  // namespace
 
 hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
@@ -691,22 +672,20 @@ hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int
         const hipError_t e = launch(sel, 0, T, st);
         return e != hipSuccess ? e : launch(tab, 0, T, st);
     }
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
+    SideStream *sd = nullptr;
+    std::unique_lock<std::mutex> lock;
+    hipError_t e = side_stream_acquire(g_sdm_side, sd, lock);
     if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kSdmMaxDev) return hipErrorInvalidDevice;
-    SdmSide &sd = g_side[dev];
-    std::lock_guard<std::mutex> lock(sd.mu);
-    if ((e = sdm_side_init(sd)) != hipSuccess) return e;
+    hipEvent_t fork = sd->ev[0], *done = sd->ev + 1;
     auto bound = [&](int j) { return (int)((long)T * j / nblk); };
-    if ((e = hipEventRecord(sd.fork, st)) != hipSuccess) return e;           // inputs ready on st
-    if ((e = hipStreamWaitEvent(sd.side, sd.fork, 0)) != hipSuccess) return e;
+    if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;           // inputs ready on st
+    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
     for (int j = 0; j < nblk; ++j) {
-        if ((e = launch(sel, bound(j), bound(j + 1), sd.side)) != hipSuccess) return e;
-        if ((e = hipEventRecord(sd.done[j], sd.side)) != hipSuccess) return e;
+        if ((e = launch(sel, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
+        if ((e = hipEventRecord(done[j], sd->stream)) != hipSuccess) return e;
     }
     for (int j = 0; j < nblk; ++j) {
-        if ((e = hipStreamWaitEvent(st, sd.done[j], 0)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(st, done[j], 0)) != hipSuccess) return e;
         if ((e = launch(tab, bound(j), bound(j + 1), st)) != hipSuccess) return e;
     }
     return hipSuccess;

@@ -31,10 +31,13 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates no device memory, keeps no pointer after a call returns and has
- *     no global mutable state, with one exception: gdr_sdm_fwd creates, on its first
- *     long call on a device, one side stream (default priority) and a few events that
- *     it keeps until the process ends; their use is serialised by a mutex.  Calls
- *     from several host threads are safe.
+ *     no global mutable state, with one exception: gdr_sdm_fwd and gdr_osdn_precond
+ *     each create, on their first long call on a device, one side stream (default
+ *     priority, non-blocking) and a few events that they keep until the process
+ *     ends; the use of each is serialised by a mutex.  Calls from several host
+ *     threads are safe; work forked onto a side stream is joined back to `stream`
+ *     through events before the call's last launch, so a call captured from
+ *     `stream` into a HIP graph takes all of it in.
  *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
  *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
  *     alignment (so per-step slices of a gate array are accepted).
@@ -230,6 +233,9 @@ int gdr_mc_readout(const gdr_desc *desc, const void *q, const float *ckpt, int32
  *   qgeo   [B, H] fp32 or NULL (1 when T == 0)
  *   workspace at least gdr_osdn_precond_workspace_size() bytes
  * dk: multiple of 8 in [8, 128].  desc->dv, chunk and alpha_mode are not used.
+ * From T >= 16,384 (256 chunks of 64) the chunk solve and the emission of the
+ * write keys run on the library's side stream beside the sequential scan, block
+ * by block (see the conventions above); the results are the same bit for bit.
  */
 size_t gdr_osdn_precond_workspace_size(const gdr_desc *desc);
 int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, const void *r, float eta,

@@ -73,15 +73,18 @@ def test_checkpointed_prefill_graph_replays_equal_eager():
     _replay_and_compare(torch, graph, res, lambda: g.chunk_fwd_ckpt(*args), "ckpt")
 
 
-def test_osdn_precond_graph_replays_equal_eager():
+# T = 16,500: the chunks are cut into blocks, with the chunk solve and the emission
+# forked onto the library's side stream and joined back through events
+@pytest.mark.parametrize("T", [700, 16500])
+def test_osdn_precond_graph_replays_equal_eager(T):
     torch, g = gpu()
-    w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=700, H=3, seed=125)
+    w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=T, H=3, seed=125)
     x = gi.make_prefill(w)
     k = gi.to_torch(x["k"], w.io)
     beta = gi.to_torch(x["beta_k"], w.gate)
     r = gi.to_torch(gi.make_retention(w), w.gate)
     graph, res = _capture(torch, lambda: g.osdn_precond(k, beta, 0.05, r=r))
-    _replay_and_compare(torch, graph, res, lambda: g.osdn_precond(k, beta, 0.05, r=r), "osdn_precond")
+    _replay_and_compare(torch, graph, res, lambda: g.osdn_precond(k, beta, 0.05, r=r), f"osdn_precond T={T}")
 
 
 def test_mc_readout_graph_replays_equal_eager():

@@ -39,6 +39,10 @@ CASES = [
     ("osdn_apf_strong_eta", BASE.scaled(T=640, seed=93), 4.0, True, 0.0),
     ("f32_io_dk24", BASE.scaled(T=300, dk=24, dv=24, io=gi.F32, seed=94), 1.0, True, 0.2),
     ("bf16_dk8_bf16_gates", BASE.scaled(T=200, dk=8, dv=8, gate=gi.BF16, seed=95), 0.5, True, 0.0),
+    # 256 chunks and more are cut into blocks that the chain walks in order while the
+    # parallel passes of other blocks run beside it (here 4 blocks, the last ragged)
+    ("chunk_blocks_ragged", BASE.scaled(B=1, T=16500, H=2, seed=97), 1.0, True, 0.3),
+    ("chunk_blocks_f32_dk24", BASE.scaled(B=2, T=16384, H=1, dk=24, dv=24, io=gi.F32, seed=98), 1.0, False, 0.0),
 ]
 
 
