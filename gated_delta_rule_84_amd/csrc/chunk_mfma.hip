@@ -153,8 +153,8 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
     uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
 
-    const int blk = blockIdx.x;
-    const int c = blk % NT, bh = blk / NT;
+    const int blk = blockIdx.x, nc = p.c1 - p.c0;  // chunks c0 .. c1 - 1 of every (batch, head)
+    const int c = p.c0 + blk % nc, bh = blk / nc;
     const int b = bh / p.H, h = bh % p.H;
     const int t0 = c * kC, n = min(kC, p.T - t0);
     const int tid = threadIdx.x, l = tid & 63, r = l & 15, q = l >> 4;
@@ -941,14 +941,16 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
         }
         publish_state();
     } else {
-        issue(0, 0);
-        issue_late(0);
+        issue(p.c0, 0);
+        issue_late(p.c0);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     }
     __syncthreads();
 
-    for (int c = 0; c < NT; ++c) {
-        const int bb = c & 1;
+    // chunks c0 .. c1 - 1 (a later block of chunks starts from the state the launch for
+    // the block before left in ST, passed as S0)
+    for (int c = p.c0; c < p.c1; ++c) {
+        const int bb = (c - p.c0) & 1;
         const WsBuf &B = sm.buf[bb];
         const int t0 = c * kC, n = min(kC, p.T - t0);
         if (chain) {
@@ -1068,7 +1070,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     for (int i = 0; i < 4; ++i) Ck[(long)(16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
             }
         } else {
-            if (c + 1 < NT) issue(c + 1, bb ^ 1);
+            if (c + 1 < p.c1) issue(c + 1, bb ^ 1);
             // O0 = Q S from the published state fragments
             f32x4 O[4];
             {
@@ -1108,7 +1110,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                 }
             }
             lds_barrier();  // B1: D published; V and the P terms of this chunk consumed
-            if (c + 1 < NT) issue_late(c + 1);
+            if (c + 1 < p.c1) issue_late(c + 1);
 
             // O += P D, then stored per lane (4 tokens of one value column per tile)
             {
@@ -1528,11 +1530,59 @@ size_t chunk_mfma_workspace(const ChunkParams &p) {
     return (size_t)p.B * p.H * NT * (general_gates(p) ? kRcBytes : kRecBytes);
 }
 
+namespace {
+constexpr int kPrefillBlocks = 8;   // most chunk blocks of a call (8 measured best: 16 and 4 both slower)
+static_assert(1 + kPrefillBlocks <= kSideEvents, "events of one call");
+SideStream g_prefill_side[kSideMaxDevices];
+
+// Scalar gates, wave-specialised state kernel, chunks cut into nblk blocks: the prep of
+// every block on the side stream, the state kernel block by block on the caller's
+// stream, each launch after its block's prep; the launches after the first start from
+// the state the one before left in ST.
+hipError_t launch_blocked(const ChunkParams &p, int NT, int nblk, const void *ws_fn, unsigned ws_grid,
+                          hipStream_t st) {
+    SideStream *sd = nullptr;
+    std::unique_lock<std::mutex> lock;
+    hipError_t e = side_stream_acquire(g_prefill_side, sd, lock);
+    if (e != hipSuccess) return e;
+    hipEvent_t fork = sd->ev[0], *prepped = sd->ev + 1;
+    const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
+                                   : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
+    const long nbh = (long)p.B * p.H;
+    int nt = NT, nb = (int)nbh;
+    auto bound = [&](int j) { return (int)((long)NT * j / nblk); };
+    if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;  // inputs ready on st
+    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
+    for (int j = 0; j < nblk; ++j) {
+        ChunkParams a = p;
+        a.c0 = bound(j);
+        a.c1 = bound(j + 1);
+        void *args[] = {&a, &nt};
+        if ((e = hipLaunchKernel(prep, dim3((unsigned)(nbh * (a.c1 - a.c0))), dim3(kThreads), args, 0,
+                                 sd->stream)) != hipSuccess)
+            return e;
+        if ((e = hipEventRecord(prepped[j], sd->stream)) != hipSuccess) return e;
+    }
+    for (int j = 0; j < nblk; ++j) {
+        ChunkParams a = p;
+        a.c0 = bound(j);
+        a.c1 = bound(j + 1);
+        if (j > 0) a.S0 = a.ST;  // in place: each workgroup reads and writes only its own columns
+        void *args[] = {&a, &nt, &nb};
+        if ((e = hipStreamWaitEvent(st, prepped[j], 0)) != hipSuccess) return e;
+        if ((e = hipLaunchKernel(ws_fn, dim3(ws_grid), dim3(256), args, 0, st)) != hipSuccess) return e;
+    }
+    return hipSuccess;
+}
+}  // namespace
+
 hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     const long nbh = (long)p.B * p.H;
     const int NT = (p.T + kC - 1) / kC;
     if (nbh == 0 || NT == 0) return hipSuccess;
     ChunkParams arg = p;
+    arg.c0 = 0;
+    arg.c1 = NT;
     int nt = NT;
     int nb = (int)nbh;
     const long groups = (nbh + 7) / 8;
@@ -1561,6 +1611,17 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
         return hipLaunchKernel(states[(bvec ? 2 : 0) + (g16 ? 1 : 0)], dim3((unsigned)(groups * 8 * (kD / kCW))),
                                dim3(256), sargs, 0, st);
     }
+    const int bv = state_variant(p);
+    const bool sep = p.kw != p.k;
+    const void *ws_fn = sep ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
+                            : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
+    const unsigned ws_grid = (unsigned)(groups * 8 * (kD / kCW));
+    // Few heads and many chunks: the state kernel holds one CU per workgroup (all of its
+    // LDS) on at most three quarters of the CUs, so the prep of later blocks of chunks
+    // runs beside it on a side stream; the state kernel walks the blocks in order, one
+    // launch per block, carrying the state through ST.
+    const int nblk = (bv == 1 && p.ST && NT >= 256 && ws_grid <= 192) ? min(kPrefillBlocks, NT / 64) : 1;
+    if (nblk > 1) return launch_blocked(arg, NT, nblk, ws_fn, ws_grid, st);
     {
         void *args[] = {&arg, &nt};
         const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
@@ -1570,13 +1631,7 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
         if (e != hipSuccess) return e;
     }
     void *args[] = {&arg, &nt, &nb};
-    const bool sep = p.kw != p.k;
-    const int bv = state_variant(p);
-    if (bv == 1) {
-        const void *fn = sep ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
-                             : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
-        return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(256), args, 0, st);
-    }
+    if (bv == 1) return hipLaunchKernel(ws_fn, dim3(ws_grid), dim3(256), args, 0, st);
     const void *fn = bv == 32 ? (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<32, true>)
                                      : reinterpret_cast<const void *>(&gdr_state_kernel<32, false>))
                               : (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<16, true>)

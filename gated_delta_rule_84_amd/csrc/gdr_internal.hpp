@@ -57,6 +57,8 @@ struct ChunkParams {
     int seg_chunks;   // chunks per segment (ckpt only)
     int nck;          // segment ends stored per (batch, head): floor(T / segment length)
     void *ws;         // workspace (path dependent)
+    int c0, c1;       // matrix-core prep and wave-specialised state kernels: the launch covers
+                      // chunks c0 .. c1 - 1 (set by the launcher)
 };
 
 // True when chunk c (0-based) ends a segment whose state is kept; its slot is then

@@ -31,13 +31,14 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates no device memory, keeps no pointer after a call returns and has
- *     no global mutable state, with one exception: gdr_sdm_fwd and gdr_osdn_precond
- *     each create, on their first long call on a device, one side stream (default
- *     priority, non-blocking) and a few events that they keep until the process
- *     ends; the use of each is serialised by a mutex.  Calls from several host
- *     threads are safe; work forked onto a side stream is joined back to `stream`
- *     through events before the call's last launch, so a call captured from
- *     `stream` into a HIP graph takes all of it in.
+ *     no global mutable state, with one exception: gdr_sdm_fwd, gdr_osdn_precond
+ *     and gdr_chunk_fwd (few heads, long sequences, final state requested) each
+ *     create, on their first such call on a device, one side stream (default
+ *     priority, non-blocking) and a few events, kept until the process ends; the
+ *     use of each is serialised by a mutex.  Calls from several host threads are
+ *     safe.  Work forked onto a side stream is joined back to `stream` through
+ *     events before the call's last launch, so a call captured from `stream` into
+ *     a HIP graph takes all of it in.
  *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
  *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
  *     alignment (so per-step slices of a gate array are accepted).

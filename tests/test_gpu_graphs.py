@@ -44,6 +44,8 @@ PREFILL_CASES = {
     "kda_fg2plus_general_gates": dict(base=gi.KDA_FG2PLUS_PREFILL, B=1, T=200, H=2, seed=121),
     "osdn_write_key_S0": dict(base=gi.OSDN_LONG_PREFILL, B=1, T=257, H=2, seed=122),
     "valu_f32_d64": dict(base=gi.GDN_PREFILL, B=1, T=130, H=2, dk=64, dv=64, io=gi.F32, seed=123),
+    # few heads, 258 chunks: the prep of later chunk blocks forked onto the side stream
+    "osdn_blocked_T16500": dict(base=gi.OSDN_LONG_PREFILL, B=1, T=16500, H=2, seed=127),
 }
 
 

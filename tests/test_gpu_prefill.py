@@ -57,6 +57,32 @@ def test_full_size_prefill(w):
     assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
 
 
+# With few heads and 256 chunks or more (and the final state requested), the prep of
+# later blocks of chunks runs beside the state recurrence, which is launched once per
+# block and carries the state through ST.  Against the oracle, and bit for bit against
+# the single-launch schedule (taken when no final state is requested).
+BLOCKED = [
+    ("gdn_T16500_ragged", gi.GDN_PREFILL.scaled(B=1, T=16500, H=2, seed=41)),
+    ("osdn_kw_S0_T16384", gi.OSDN_LONG_PREFILL.scaled(B=2, T=16384, H=1, seed=42)),
+]
+
+
+@pytest.mark.parametrize("name,w", BLOCKED, ids=[c[0] for c in BLOCKED])
+def test_blocked_long_sequence(name, w):
+    x = gi.make_prefill(w)
+    r = run_prefill(w, x)
+    assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
+    torch, g = gpu()
+    d = upload(x, w)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta_k"])
+    o_blk, _ = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"])
+    o_one, none = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"], want_state=False)
+    torch.cuda.synchronize()
+    assert none is None
+    log(f"[prefill blocked] {name}: o equal to the single-launch schedule: {torch.equal(o_blk, o_one)}")
+    assert torch.equal(o_blk, o_one)
+
+
 def test_full_size_long_context():
     """B=1 H=32 T=65536 with write key and nonzero S0; oracle on 4 sampled heads."""
     w = gi.OSDN_LONG_PREFILL
