@@ -35,6 +35,10 @@
 //        alternative for testing).  Every product that touches the state or a
 //        residual uses a two-term bf16 split of the fp32 operand (hi + lo), so the
 //        state path keeps ~16 mantissa bits.
+// For few heads and long sequences (the state kernel then leaves CUs free) the
+// chunks are cut into blocks: the prep of every block runs on a side stream and the
+// state kernel is launched once per block on the caller's stream, after its block's
+// prep, carrying the state through S_T (launch_blocked below).
 //
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, r = l % 16, q = l / 16):
 //   A (16 x 32): lane holds A[r][8q .. 8q+7];  B (32 x 16): B[8q .. 8q+7][r];
