@@ -83,6 +83,28 @@ def test_blocked_long_sequence(name, w):
     assert torch.equal(o_blk, o_one)
 
 
+def test_blocked_in_place_and_checkpoints():
+    """The blocked schedule with S0 and S_T in one buffer (in-place resume), and with
+    segment states kept: both bit for bit against the single-launch schedule."""
+    torch, g = gpu()
+    w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=16500, H=2, seed=43)
+    d = upload(gi.make_prefill(w), w)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta_k"])
+    o_ref, S_ref = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"])
+    S_io = d["S0"].clone()
+    o_io, S_out = g.chunk_fwd(*args, k_w=d["k_w"], S0=S_io, final_state=S_io)
+    torch.cuda.synchronize()
+    assert S_out.data_ptr() == S_io.data_ptr()
+    same_io = torch.equal(o_io, o_ref) and torch.equal(S_io, S_ref)
+    o_c, S_c, ck = g.chunk_fwd_ckpt(*args, 4096, k_w=d["k_w"], S0=d["S0"])
+    o_c1, none, ck1 = g.chunk_fwd_ckpt(*args, 4096, k_w=d["k_w"], S0=d["S0"], want_state=False)
+    torch.cuda.synchronize()
+    assert none is None and ck.shape[2] == 4
+    same_ck = torch.equal(o_c, o_ref) and torch.equal(S_c, S_ref) and torch.equal(o_c1, o_ref) and torch.equal(ck, ck1)
+    log(f"[prefill blocked] in place equal {same_io}; checkpoints equal {same_ck}")
+    assert same_io and same_ck
+
+
 def test_full_size_long_context():
     """B=1 H=32 T=65536 with write key and nonzero S0; oracle on 4 sampled heads."""
     w = gi.OSDN_LONG_PREFILL
