@@ -43,6 +43,7 @@ CASES = [
     # parallel passes of other blocks run beside it (here 4 blocks, the last ragged)
     ("chunk_blocks_ragged", BASE.scaled(B=1, T=16500, H=2, seed=97), 1.0, True, 0.3),
     ("chunk_blocks_f32_dk24", BASE.scaled(B=2, T=16384, H=1, dk=24, dv=24, io=gi.F32, seed=98), 1.0, False, 0.0),
+    ("chunk_blocks_bf16_gates", BASE.scaled(B=1, T=20000, H=1, gate=gi.BF16, seed=99), 0.7, True, 0.2),
 ]
 
 

@@ -64,6 +64,7 @@ def test_full_size_prefill(w):
 BLOCKED = [
     ("gdn_T16500_ragged", gi.GDN_PREFILL.scaled(B=1, T=16500, H=2, seed=41)),
     ("osdn_kw_S0_T16384", gi.OSDN_LONG_PREFILL.scaled(B=2, T=16384, H=1, seed=42)),
+    ("gdn_bf16_gates_T16400", gi.GDN_PREFILL.scaled(B=1, T=16400, H=1, gate=gi.BF16, seed=44)),
 ]
 
 
