@@ -102,6 +102,58 @@ def _ptr(t: Optional[torch.Tensor]):
     return ctypes.c_void_p(t.data_ptr())
 
 
+_TORCH_DTYPE = {GDR_BF16: torch.bfloat16, GDR_F32: torch.float32}
+
+
+def _check_all(specs) -> None:
+    """The library trusts the descriptor: every tensor handed to it must hold exactly
+    the element count and dtype the descriptor implies, on the current device, else
+    ValueError before the call (a short or mistyped buffer would be read or written
+    past its end on the device).  `specs` is a list of (name, tensor or None, count,
+    dtype); sizes and dtypes are checked for all before devices.  An object that is not
+    a tensor but has data_ptr() is a raw device address: it is passed as it is, and
+    the caller answers for its size."""
+    specs = [s for s in specs if isinstance(s[1], torch.Tensor)]
+    for name, t, count, dtype in specs:
+        if t.dtype != dtype:
+            raise ValueError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+        if t.numel() != count:
+            raise ValueError(f"{name}: expected {count} elements for this descriptor, got {t.numel()} "
+                             f"(shape {tuple(t.shape)})")
+    for name, t, _, _ in specs:
+        if t.device.type != "cuda":
+            raise ValueError(f"{name}: expected a device tensor, got one on {t.device}")
+        if t.device.index is not None and t.device.index != torch.cuda.current_device():
+            raise ValueError(f"{name}: tensor on {t.device}, current device is cuda:{torch.cuda.current_device()}")
+
+
+def _check_workspace(workspace, workspace_bytes: int) -> None:
+    if workspace is None or not isinstance(workspace, torch.Tensor):
+        return
+    have = workspace.numel() * workspace.element_size()
+    if int(workspace_bytes) > have:
+        raise ValueError(f"workspace_bytes = {int(workspace_bytes)} exceeds the workspace tensor ({have} bytes)")
+
+
+def _io(desc: Desc):
+    if desc.io_dtype not in _TORCH_DTYPE or desc.gate_dtype not in _TORCH_DTYPE:
+        return None, None
+    return _TORCH_DTYPE[desc.io_dtype], _TORCH_DTYPE[desc.gate_dtype]
+
+
+def _prefill_specs(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST) -> list:
+    io, gt = _io(desc)
+    if io is None or min(desc.B, desc.T, desc.H, desc.dk, desc.dv) < 0:
+        return []  # the library rejects the descriptor itself
+    n = desc.B * desc.T * desc.H
+    st = desc.B * desc.H * desc.dk * desc.dv
+    return [("q", q, n * desc.dk, io), ("k", k, n * desc.dk, io), ("k_w", k_w, n * desc.dk, io),
+            ("v", v, n * desc.dv, io), ("o", o, n * desc.dv, io),
+            ("alpha", alpha, n * (desc.dk if desc.alpha_mode == GDR_ALPHA_CHANNEL else 1), gt),
+            ("beta_k", beta_k, n * (desc.dk if desc.beta_mode in (GDR_BETA_SHARED, GDR_BETA_KV) else 1), gt),
+            ("beta_v", beta_v, n * desc.dv, gt), ("S0", S0, st, torch.float32), ("ST", ST, st, torch.float32)]
+
+
 def _stream(stream) -> ctypes.c_void_p:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -130,6 +182,8 @@ def gdr_chunk_fwd_path(desc: Desc) -> int:
 
 def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace,
                   workspace_bytes: int, stream=None) -> int:
+    _check_all(_prefill_specs(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST))
+    _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
                                   _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST),
                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))
@@ -137,6 +191,11 @@ def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, wo
 
 def gdr_chunk_fwd_ckpt(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg_len: int, ckpt,
                        workspace, workspace_bytes: int, stream=None) -> int:
+    specs = _prefill_specs(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST)
+    if specs and int(seg_len) > 0:
+        specs.append(("ckpt", ckpt, desc.B * desc.H * (desc.T // int(seg_len)) * desc.dk * desc.dv, torch.float32))
+    _check_all(specs)
+    _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_chunk_fwd_ckpt(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
                                        _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST), int(seg_len),
                                        _ptr(ckpt), _ptr(workspace), int(workspace_bytes), _stream(stream)))
@@ -148,6 +207,14 @@ def gdr_mc_readout_workspace_size(desc: Desc, n_ckpt: int) -> int:
 
 def gdr_mc_readout(desc: Desc, q, ckpt, n_ckpt: int, seg_len: int, gates, o_in, o_out, workspace,
                    workspace_bytes: int, stream=None) -> int:
+    io, _ = _io(desc)
+    if io is not None and min(desc.B, desc.T, desc.H, desc.dk, desc.dv, int(n_ckpt)) >= 0:
+        n = desc.B * desc.T * desc.H
+        _check_all([("q", q, n * desc.dk, io),
+                    ("ckpt", ckpt, desc.B * desc.H * int(n_ckpt) * desc.dk * desc.dv, torch.float32),
+                    ("gates", gates, n * int(n_ckpt), torch.float32), ("o_in", o_in, n * desc.dv, io),
+                    ("o_out", o_out, n * desc.dv, io)])
+    _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_mc_readout(ctypes.byref(desc), _ptr(q), _ptr(ckpt), int(n_ckpt), int(seg_len),
                                    _ptr(gates), _ptr(o_in), _ptr(o_out), _ptr(workspace), int(workspace_bytes),
                                    _stream(stream)))
@@ -159,6 +226,14 @@ def gdr_osdn_precond_workspace_size(desc: Desc) -> int:
 
 def gdr_osdn_precond(desc: Desc, k, beta, r, eta: float, d0, k_w, dT, qgeo, workspace, workspace_bytes: int,
                      stream=None) -> int:
+    io, gt = _io(desc)
+    if io is not None and min(desc.B, desc.T, desc.H, desc.dk) >= 0:
+        n = desc.B * desc.T * desc.H
+        _check_all([("k", k, n * desc.dk, io), ("k_w", k_w, n * desc.dk, io), ("beta", beta, n, gt),
+                    ("r", r, n, gt), ("d0", d0, desc.B * desc.H * desc.dk, torch.float32),
+                    ("dT", dT, desc.B * desc.H * desc.dk, torch.float32),
+                    ("qgeo", qgeo, desc.B * desc.H, torch.float32)])
+    _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_osdn_precond(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(k_w),
                                      _ptr(dT), _ptr(qgeo), _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
@@ -169,12 +244,28 @@ def gdr_sdm_workspace_size(desc: Desc, n: int, W: int, R: int) -> int:
 
 def gdr_sdm_fwd(desc: Desc, n: int, W: int, R: int, ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace,
                 workspace_bytes: int, stream=None) -> int:
+    io, gt = _io(desc)
+    if io is not None and min(desc.B, desc.T, desc.H, desc.dv, int(n), int(W), int(R)) >= 0:
+        nt = desc.B * desc.T * desc.H
+        _check_all([("ks", ks, nt * 2 * int(n), torch.float32), ("qs", qs, nt * 2 * int(n), torch.float32),
+                    ("v", v, nt * desc.dv, io), ("o", o, nt * desc.dv, io), ("alpha", alpha, nt, gt),
+                    ("beta", beta, nt, gt), ("M", M, desc.B * desc.H * int(n) * int(n) * desc.dv, torch.float32),
+                    ("w_slots", w_slots, nt * int(W), torch.int32), ("r_slots", r_slots, nt * int(R), torch.int32)])
+    _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_sdm_fwd(ctypes.byref(desc), int(n), int(W), int(R), _ptr(ks), _ptr(qs), _ptr(v), _ptr(alpha),
                                 _ptr(beta), _ptr(M), _ptr(o), _ptr(w_slots), _ptr(r_slots), _ptr(workspace),
                                 int(workspace_bytes), _stream(stream)))
 
 
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
+    io, gt = _io(desc)
+    if io is not None and min(desc.B, desc.H, desc.dk, desc.dv) >= 0:
+        n = desc.B * desc.H
+        _check_all([("q", q, n * desc.dk, io), ("k", k, n * desc.dk, io), ("k_w", k_w, n * desc.dk, io),
+                    ("v", v, n * desc.dv, io), ("o", o, n * desc.dv, io),
+                    ("alpha", alpha, n * (desc.dk if desc.alpha_mode == GDR_ALPHA_CHANNEL else 1), gt),
+                    ("beta_k", beta_k, n * (desc.dk if desc.beta_mode in (GDR_BETA_SHARED, GDR_BETA_KV) else 1), gt),
+                    ("beta_v", beta_v, n * desc.dv, gt), ("S", S, n * desc.dk * desc.dv, torch.float32)])
     return int(_lib.gdr_decode_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
                                     _ptr(beta_k), _ptr(beta_v), _ptr(S), _ptr(o), _stream(stream)))
 

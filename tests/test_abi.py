@@ -256,9 +256,97 @@ def test_binding_refuses_host_and_strided_tensors(g):
     import torch
 
     d = _desc(g, B=1, T=4, H=1, dk=8, dv=8, io_dtype=g.GDR_F32)
-    host = torch.zeros((1, 1, 8))
+    host, gate, state = torch.zeros((1, 1, 8)), torch.zeros((1, 1)), torch.zeros((1, 1, 8, 8))
     with pytest.raises(ValueError, match="device tensor"):
+        g.gdr_decode_step(d, host, host, None, host, gate, gate, None, state, host, 0)
+    with pytest.raises(ValueError, match="elements"):
         g.gdr_decode_step(d, host, host, None, host, host, host, None, host, host, 0)
     with pytest.raises(ValueError, match="contiguous"):
         g._ptr(torch.zeros((4, 4)).t())
     assert g._ptr(None) is None
+
+
+# ---- the binding checks every tensor against the descriptor before the call ----
+
+def _prefill_tensors(g, B=1, T=5, H=2, dk=16, dv=16, io=None, gate=None):
+    import torch
+
+    io = io or torch.bfloat16
+    gate = gate or torch.float32
+    return dict(q=torch.zeros(B, T, H, dk, dtype=io), k=torch.zeros(B, T, H, dk, dtype=io),
+                v=torch.zeros(B, T, H, dv, dtype=io), alpha=torch.zeros(B, T, H, dtype=gate),
+                beta_k=torch.zeros(B, T, H, dtype=gate), o=torch.zeros(B, T, H, dv, dtype=io),
+                ST=torch.zeros(B, H, dk, dv, dtype=torch.float32))
+
+
+@pytest.mark.parametrize("bad", ["S0_bf16", "k_other_dk", "k_w_fp32", "beta_k_bf16", "beta_v_shape", "ST_short",
+                                 "o_fp32", "alpha_channel_missing"])
+def test_binding_rejects_mismatched_tensors(g, bad):
+    import torch
+
+    t = _prefill_tensors(g)
+    d = _desc(g, B=1, T=5, H=2, dk=16, dv=16)
+    kw = dict(k_w=None, beta_v=None, S0=None)
+    if bad == "S0_bf16":
+        kw["S0"] = torch.zeros(1, 2, 16, 16, dtype=torch.bfloat16)
+    elif bad == "k_other_dk":
+        t["k"] = torch.zeros(1, 5, 2, 8, dtype=torch.bfloat16)
+    elif bad == "k_w_fp32":
+        kw["k_w"] = torch.zeros(1, 5, 2, 16, dtype=torch.float32)
+    elif bad == "beta_k_bf16":
+        t["beta_k"] = torch.zeros(1, 5, 2, dtype=torch.bfloat16)
+    elif bad == "beta_v_shape":
+        d = _desc(g, B=1, T=5, H=2, dk=16, dv=16, beta_mode=g.GDR_BETA_KV)
+        t["beta_k"] = torch.zeros(1, 5, 2, 16)
+        kw["beta_v"] = torch.zeros(1, 5, 2, 8)
+    elif bad == "ST_short":
+        t["ST"] = torch.zeros(1, 2, 16, 8)
+    elif bad == "o_fp32":
+        t["o"] = torch.zeros(1, 5, 2, 16, dtype=torch.float32)
+    elif bad == "alpha_channel_missing":
+        d = _desc(g, B=1, T=5, H=2, dk=16, dv=16, alpha_mode=g.GDR_ALPHA_CHANNEL)
+    with pytest.raises(ValueError):
+        g.gdr_chunk_fwd(d, t["q"], t["k"], kw["k_w"], t["v"], t["alpha"], t["beta_k"], kw["beta_v"], kw["S0"],
+                        t["o"], t["ST"], None, 0, 0)
+
+
+def test_binding_rejects_host_tensors_of_the_right_shape(g):
+    t = _prefill_tensors(g)
+    d = _desc(g, B=1, T=5, H=2, dk=16, dv=16)
+    with pytest.raises(ValueError, match="device tensor"):
+        g.gdr_chunk_fwd(d, t["q"], t["k"], None, t["v"], t["alpha"], t["beta_k"], None, None, t["o"], t["ST"],
+                        None, 0, 0)
+
+
+def test_binding_rejects_oversized_workspace_claim(g):
+    import torch
+
+    d = _desc(g, B=1, T=5, H=2, dk=16, dv=16)
+    ws = torch.zeros(64, dtype=torch.uint8)
+    with pytest.raises(ValueError, match="workspace"):
+        g.gdr_chunk_fwd(d, None, None, None, None, None, None, None, None, None, None, ws, 65, 0)
+
+
+def test_binding_checks_the_other_entry_points(g):
+    import torch
+
+    bf, f32 = torch.bfloat16, torch.float32
+    dd = _desc(g, B=2, H=3, dk=16, dv=16, gate_dtype=g.GDR_BF16)
+    with pytest.raises(ValueError, match="S"):          # state given in bf16
+        g.gdr_decode_step(dd, torch.zeros(2, 3, 16, dtype=bf), torch.zeros(2, 3, 16, dtype=bf), None,
+                          torch.zeros(2, 3, 16, dtype=bf), torch.zeros(2, 3, dtype=bf), torch.zeros(2, 3, dtype=bf),
+                          None, torch.zeros(2, 3, 16, 16, dtype=bf), torch.zeros(2, 3, 16, dtype=bf))
+    do = _desc(g, B=1, T=4, H=2, dk=16, dv=16)
+    with pytest.raises(ValueError, match="k_w"):        # write key of another size
+        g.gdr_osdn_precond(do, torch.zeros(1, 4, 2, 16, dtype=bf), torch.zeros(1, 4, 2), None, 1.0, None,
+                           torch.zeros(1, 4, 2, 8, dtype=bf), None, None, None, 0, 0)
+    dm = _desc(g, B=1, T=4, H=2, dk=128, dv=128)
+    with pytest.raises(ValueError, match="gates"):      # gates for another number of caches
+        g.gdr_mc_readout(dm, torch.zeros(1, 4, 2, 128, dtype=bf), torch.zeros(1, 2, 3, 128, 128), 3, 64,
+                         torch.zeros(1, 4, 2, 2), None, torch.zeros(1, 4, 2, 128, dtype=bf), None, 0, 0)
+    ds = _desc(g, B=1, T=4, H=2, dk=128, dv=128)
+    with pytest.raises(ValueError, match="w_slots"):    # slot list of the wrong integer type
+        g.gdr_sdm_fwd(ds, 4, 2, 2, torch.zeros(1, 4, 2, 2, 4), torch.zeros(1, 4, 2, 2, 4),
+                      torch.zeros(1, 4, 2, 128, dtype=bf), torch.zeros(1, 4, 2), torch.zeros(1, 4, 2),
+                      torch.zeros(1, 2, 16, 128), torch.zeros(1, 4, 2, 128, dtype=bf),
+                      torch.zeros(1, 4, 2, 2, dtype=torch.int64), None, None, 0, 0)
