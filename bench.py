@@ -239,11 +239,12 @@ def bench_osdn_precond(g, gi, stream, reps, digest=None):
     need = g.gdr_osdn_precond_workspace_size(desc)
     ws = torch.empty(need, dtype=torch.uint8, device=k.device)
     kw = torch.empty_like(k)
+    ctx = g.Context()  # the chunk solve and emission of later blocks overlap the scan on its stream
     dT = torch.empty((w.B, w.H, w.dk), dtype=torch.float32, device=k.device)
     qg = torch.empty((w.B, w.H), dtype=torch.float32, device=k.device)
 
     def call():
-        rc = g.gdr_osdn_precond(desc, k, beta, r, 1.0, None, kw, dT, qg, ws, need, stream)
+        rc = g.gdr_osdn_precond(desc, k, beta, r, 1.0, None, kw, dT, qg, ws, need, ctx, stream)
         if rc != g.GDR_OK:
             raise g.GdrError(rc, "gdr_osdn_precond")
 
@@ -296,9 +297,10 @@ def bench_sdm(g, gi, stream, reps, digest=None):
                   alpha_mode=0, beta_mode=0, flags=0)
     need = g.gdr_sdm_workspace_size(desc, w.n, w.W, w.R)
     ws = torch.empty(need, dtype=torch.uint8, device=v.device)
+    ctx = g.Context()  # the selection of later token blocks overlaps the table pass on its stream
 
     def call():
-        rc = g.gdr_sdm_fwd(desc, w.n, w.W, w.R, ks, qs, v, alpha, beta, M, o, None, None, ws, need, stream)
+        rc = g.gdr_sdm_fwd(desc, w.n, w.W, w.R, ks, qs, v, alpha, beta, M, o, None, None, ws, need, ctx, stream)
         if rc != g.GDR_OK:
             raise g.GdrError(rc, "gdr_sdm_fwd")
 
@@ -332,11 +334,8 @@ def main():
     ap.add_argument("--decode-reps", type=int, default=5)
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-heads", type=int, default=64)
-    ap.add_argument("--generic", action="store_true", help="force the fp32 vector-ALU prefill kernel")
     ap.add_argument("--only-prefill", action="store_true")
     ap.add_argument("--mc-reps", type=int, default=5, help="timed Memory-Caching read-out calls")
-    ap.add_argument("--state-kernel", choices=["cols16", "cols32", "wavecols"], default=None,
-                    help="matrix-core state kernel (default: the library's choice)")
     ap.add_argument("--workload", choices=["gdn", "kda_fg2plus", "osdn_long"], default="gdn",
                     help="prefill workload (default: the B4 H16 T4096 GDN batch the metric is quoted on)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -368,10 +367,7 @@ def main():
     x = gi.make_prefill(w)
     d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
          for k in x}
-    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk,
-                       generic=args.generic, flags={None: 0, "cols16": g.GDR_FLAG_STATE_COLS16,
-                                                    "cols32": g.GDR_FLAG_STATE_COLS32,
-                                                    "wavecols": g.GDR_FLAG_STATE_WAVECOLS}[args.state_kernel])
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk)
     path = g.gdr_chunk_fwd_path(desc)
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device=dev)
     ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)

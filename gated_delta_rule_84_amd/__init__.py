@@ -26,10 +26,6 @@ GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EWORKSPACE, GDR_EHIP = 0, -1, -2, -3, 
 GDR_BF16, GDR_F32 = 0, 1
 GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1
 GDR_BETA_SCALAR, GDR_BETA_SHARED, GDR_BETA_KV = 0, 1, 2
-GDR_FLAG_GENERIC_PATH = 0x1
-GDR_FLAG_STATE_COLS16 = 0x2
-GDR_FLAG_STATE_COLS32 = 0x4
-GDR_FLAG_STATE_WAVECOLS = 0x8
 GDR_FLAG_READ_BEFORE_WRITE = 0x10
 GDR_FLAG_UNDECAYED_PREDICTION = 0x20
 PATH_MFMA, PATH_VALU = 1, 2
@@ -69,17 +65,22 @@ _lib.gdr_mc_readout.argtypes = [_dp, _vp, _vp, ctypes.c_int32, ctypes.c_int32, _
 _lib.gdr_mc_readout.restype = ctypes.c_int
 _lib.gdr_osdn_precond_workspace_size.argtypes = [_dp]
 _lib.gdr_osdn_precond_workspace_size.restype = ctypes.c_size_t
-_lib.gdr_osdn_precond.argtypes = [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]
+_lib.gdr_osdn_precond.argtypes = [_dp, _vp, _vp, _vp, ctypes.c_float, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp,
+                                  _vp]
 _lib.gdr_osdn_precond.restype = ctypes.c_int
 _lib.gdr_sdm_workspace_size.argtypes = [_dp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]
 _lib.gdr_sdm_workspace_size.restype = ctypes.c_size_t
-_lib.gdr_sdm_fwd.argtypes = [_dp] + [ctypes.c_int32] * 3 + [_vp] * 10 + [ctypes.c_size_t, _vp]
+_lib.gdr_sdm_fwd.argtypes = [_dp] + [ctypes.c_int32] * 3 + [_vp] * 10 + [ctypes.c_size_t, _vp, _vp]
 _lib.gdr_sdm_fwd.restype = ctypes.c_int
+_lib.gdr_context_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+_lib.gdr_context_create.restype = ctypes.c_int
+_lib.gdr_context_destroy.argtypes = [_vp]
+_lib.gdr_context_destroy.restype = ctypes.c_int
 
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
             "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond",
-            "gdr_sdm_workspace_size", "gdr_sdm_fwd")
+            "gdr_sdm_workspace_size", "gdr_sdm_fwd", "gdr_context_create", "gdr_context_destroy")
 
 
 class GdrError(RuntimeError):
@@ -164,6 +165,54 @@ def _stream(stream) -> ctypes.c_void_p:
 # the C entry points, one to one
 # ---------------------------------------------------------------------------
 
+def gdr_context_create() -> ctypes.c_void_p:
+    """A caller-owned execution context (a second stream and events) on the current
+    device; raises on failure.  Release it with gdr_context_destroy."""
+    h = ctypes.c_void_p()
+    rc = int(_lib.gdr_context_create(ctypes.byref(h)))
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_context_create")
+    return h
+
+
+def gdr_context_destroy(ctx) -> int:
+    return int(_lib.gdr_context_destroy(ctx))
+
+
+class Context:
+    """Owns one gdr_context; usable as a context manager.  Pass it (or its `handle`)
+    as `ctx` to osdn_precond / sdm_fwd to overlap their parallel passes on the
+    context's second stream."""
+
+    def __init__(self):
+        self.handle = gdr_context_create()
+
+    def close(self):
+        if self.handle is not None:
+            rc = gdr_context_destroy(self.handle)
+            self.handle = None
+            if rc != GDR_OK:
+                raise GdrError(rc, "gdr_context_destroy")
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def _ctx(ctx):
+    if ctx is None:
+        return None
+    return ctx.handle if isinstance(ctx, Context) else ctx
+
+
 def gdr_version() -> int:
     return int(_lib.gdr_version())
 
@@ -225,7 +274,7 @@ def gdr_osdn_precond_workspace_size(desc: Desc) -> int:
 
 
 def gdr_osdn_precond(desc: Desc, k, beta, r, eta: float, d0, k_w, dT, qgeo, workspace, workspace_bytes: int,
-                     stream=None) -> int:
+                     ctx=None, stream=None) -> int:
     io, gt = _io(desc)
     if io is not None and min(desc.B, desc.T, desc.H, desc.dk) >= 0:
         n = desc.B * desc.T * desc.H
@@ -235,7 +284,8 @@ def gdr_osdn_precond(desc: Desc, k, beta, r, eta: float, d0, k_w, dT, qgeo, work
                     ("qgeo", qgeo, desc.B * desc.H, torch.float32)])
     _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_osdn_precond(ctypes.byref(desc), _ptr(k), _ptr(beta), _ptr(r), float(eta), _ptr(d0), _ptr(k_w),
-                                     _ptr(dT), _ptr(qgeo), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+                                     _ptr(dT), _ptr(qgeo), _ptr(workspace), int(workspace_bytes), _ctx(ctx),
+                                     _stream(stream)))
 
 
 def gdr_sdm_workspace_size(desc: Desc, n: int, W: int, R: int) -> int:
@@ -243,7 +293,7 @@ def gdr_sdm_workspace_size(desc: Desc, n: int, W: int, R: int) -> int:
 
 
 def gdr_sdm_fwd(desc: Desc, n: int, W: int, R: int, ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace,
-                workspace_bytes: int, stream=None) -> int:
+                workspace_bytes: int, ctx=None, stream=None) -> int:
     io, gt = _io(desc)
     if io is not None and min(desc.B, desc.T, desc.H, desc.dv, int(n), int(W), int(R)) >= 0:
         nt = desc.B * desc.T * desc.H
@@ -254,7 +304,7 @@ def gdr_sdm_fwd(desc: Desc, n: int, W: int, R: int, ks, qs, v, alpha, beta, M, o
     _check_workspace(workspace, workspace_bytes)
     return int(_lib.gdr_sdm_fwd(ctypes.byref(desc), int(n), int(W), int(R), _ptr(ks), _ptr(qs), _ptr(v), _ptr(alpha),
                                 _ptr(beta), _ptr(M), _ptr(o), _ptr(w_slots), _ptr(r_slots), _ptr(workspace),
-                                int(workspace_bytes), _stream(stream)))
+                                int(workspace_bytes), _ctx(ctx), _stream(stream)))
 
 
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
@@ -282,7 +332,7 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
 
 
-def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, generic=False, flags=0) -> Desc:
+def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, flags=0) -> Desc:
     """Descriptor from tensor shapes: prefill q [B, T, H, dk], decode q [B, H, dk]."""
     if decode:
         B, H, dk = q.shape
@@ -296,14 +346,13 @@ def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, gener
     beta_mode = GDR_BETA_KV if beta_v is not None else (GDR_BETA_SHARED if beta_vec else GDR_BETA_SCALAR)
     return Desc(B=B, T=T, H=H, dk=dk, dv=v.shape[-1], chunk=chunk, io_dtype=_dtype_code(q),
                 gate_dtype=_dtype_code(alpha), alpha_mode=GDR_ALPHA_CHANNEL if alpha_ch else GDR_ALPHA_SCALAR,
-                beta_mode=beta_mode, flags=flags | (GDR_FLAG_GENERIC_PATH if generic else 0))
+                beta_mode=beta_mode, flags=flags)
 
 
 def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=64, want_state=True,
-              out=None, final_state=None, workspace=None, generic=False, flags=0, stream=None):
-    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None).
-    `flags` adds GDR_FLAG_* bits to the descriptor (kernel-selection testing aids)."""
-    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic, flags=flags)
+              out=None, final_state=None, workspace=None, stream=None):
+    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None)."""
+    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk)
     o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     ST = final_state
     if ST is None and want_state:
@@ -319,10 +368,10 @@ def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=6
 
 
 def chunk_fwd_ckpt(q, k, v, alpha, beta_k, seg_len, *, k_w=None, beta_v=None, S0=None, chunk=64,
-                   want_state=True, workspace=None, generic=False, flags=0, stream=None):
+                   want_state=True, workspace=None, stream=None):
     """Prefill that also keeps the state after every complete segment of seg_len tokens.
     Returns (o, ST or None, ckpt [B, H, floor(T / seg_len), dk, dv] fp32)."""
-    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk, generic=generic, flags=flags)
+    desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk)
     o = torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     ST = torch.empty((desc.B, desc.H, desc.dk, desc.dv), dtype=torch.float32, device=q.device) if want_state else None
     n = desc.T // int(seg_len) if seg_len > 0 else 0
@@ -356,7 +405,7 @@ def mc_readout(q, ckpt, seg_len, *, gates=None, o_in=None, out=None, workspace=N
     return o
 
 
-def osdn_precond(k, beta, eta, *, r=None, d0=None, workspace=None, stream=None):
+def osdn_precond(k, beta, eta, *, r=None, d0=None, workspace=None, ctx=None, stream=None):
     """OSDN phase 1.  k [B, T, H, dk] (bf16 or fp32), beta and r [B, T, H].
     Returns (k_w like k, dT [B, H, dk] fp32, qgeo [B, H] fp32)."""
     B, T, H, dk = k.shape
@@ -369,13 +418,13 @@ def osdn_precond(k, beta, eta, *, r=None, d0=None, workspace=None, stream=None):
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = gdr_osdn_precond(desc, k, beta, r, eta, d0, kw, dT, qg, workspace, wbytes, stream)
+    rc = gdr_osdn_precond(desc, k, beta, r, eta, d0, kw, dT, qg, workspace, wbytes, ctx, stream)
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_osdn_precond")
     return kw, dT, qg
 
 
-def sdm_fwd(M, ks, qs, v, alpha, beta, W, R, *, want_slots=False, workspace=None, stream=None):
+def sdm_fwd(M, ks, qs, v, alpha, beta, W, R, *, want_slots=False, workspace=None, ctx=None, stream=None):
     """Sparse Delta Memory over T tokens.  M [B, H, n * n, dv] fp32 is updated in place;
     ks, qs [B, T, H, 2, n] fp32; v [B, T, H, dv].  Returns o (and the selected write /
     read slots when want_slots)."""
@@ -390,7 +439,7 @@ def sdm_fwd(M, ks, qs, v, alpha, beta, W, R, *, want_slots=False, workspace=None
     if workspace is None or workspace.numel() * workspace.element_size() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=v.device)
     rc = gdr_sdm_fwd(desc, n, W, R, ks, qs, v, alpha, beta, M, o, ws_[0], ws_[1], workspace,
-                     workspace.numel() * workspace.element_size(), stream)
+                     workspace.numel() * workspace.element_size(), ctx, stream)
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_sdm_fwd")
     return (o, ws_[0], ws_[1]) if want_slots else o

@@ -1,44 +1,45 @@
 // chunk_mfma.hip -- chunkwise WY / UT-transform prefill on gfx950 bf16 matrix cores.
 //
 // Serves bf16 q / k / k_w / v, dk == dv == 128, chunk 64.  Per chunk of n <= 64
-// tokens with g_t the cumulative log-decay inside the chunk, erase key u, write
-// key w and written value vh (scalar beta: u = k, w = beta k_w, vh = v):
-//     A  = strictly-lower( u_t . (e^{g_t - g_s} (.) w_s) )      block Gram matrix
-//     Tm = (I + A)^{-1}                                          UT transform
-//     P  = lower-incl-diag( q_t . (e^{g_t - g_s} (.) w_s) )      intra-chunk scores
-//     R  = Vh - (e^{g_t} (.) U) S                                residual before the chunk
-//     D  = Tm R                                                  per-token residuals
-//     O  = (e^{g_t} (.) Q) S + P D
-//     S <- Diag(e^{g_C}) S + sum_s (e^{g_C - g_s} (.) w_s) D_s^T
-// (the WY factors of the pages' chunk-parallel form are Tm (e^g (.) U) and Tm Vh;
+// tokens with d(s, t) the decay from token s to token t >= s inside the chunk
+// (gamma_t = d(start, t)), erase key u, write key w and written value vh (scalar
+// beta: u = k, w = beta k_w, vh = v):
+//     A  = strictly-lower( u_t . (d(s, t) (.) w_s) )        block Gram matrix
+//     Tm = (I + A)^{-1}                                     UT transform
+//     P  = lower-incl-diag( q_t . (d(s, t) (.) w_s) )       intra-chunk scores
+//     R  = Vh - (gamma_t (.) U) S                           residual before the chunk
+//     D  = Tm R                                             per-token residuals
+//     O  = (gamma_t (.) Q) S + P D
+//     S <- Diag(gamma_end) S + sum_s (d(s, end) (.) w_s) D_s^T
+// (the WY factors of the pages' chunk-parallel form are Tm (gamma (.) U) and Tm Vh;
 // the write key replaces the key in the Gram matrix and the scores exactly as the
-// OSDN page, section 2.1 states; FG2-GDN page, section 3).  A scalar decay is a
-// per-row / per-column factor applied in fp32 after the product; a decay per key
-// channel is folded into the key-side operands before it.
+// OSDN page, section 2.1 states).  Decays are kept segmented at zero gates (a hard
+// reset): with P the cumulative log decay in which a zero gate adds 0,
+// d(s, t) = [no zero gate in (s, t]] e^{P_t - P_s}, so every factor is <= 1 and no
+// infinity is subtracted from another.  A scalar decay is a per-row / per-column
+// factor applied in fp32 after the product; a decay per key channel is folded into
+// the key-side operands before it.
 //
 // Kernels, two per call:
 //  * prep (scalar alpha and beta) -- one 256-thread block per chunk, fully
 //        parallel: the Gram and score products on MFMA from the raw bf16 keys,
 //        exact-difference decay weights, the UT transform (diagonal blocks by
 //        forward substitution, off-diagonal blocks on fp32 MFMA) and a per-chunk
-//        record: Tm (bf16), P as two bf16 terms, e^{g_t}, beta_s e^{g_C - g_s},
-//        e^{g_C}, g_t, beta_t.
+//        record: Tm (bf16), P as two bf16 terms, gamma_t, beta_s d(s, end),
+//        gamma_end, P_t, beta_t.
 //  * prep (general gates) -- the same for a decay per key channel and / or beta
-//        vectors: it forms U = u (.) e^{g}, Q = q (.) e^{g}, W = w (.) e^{g_C - g}
+//        vectors: it forms U = u (.) gamma, Q = q (.) gamma, W = w (.) d(., end)
 //        as two bf16 terms each (the record carries them), takes the Gram and
-//        score products on the factored decay, and the same UT transform.
+//        score products as matrix-core products of rescaled operands when the
+//        chunk's decays allow it and entry by entry otherwise, and the same UT
+//        transform.
 //  * state -- one workgroup per (batch * head, 32 value columns), walking the
 //        chunks in order: two chain waves carry Y, R, D and the state update for
 //        16 value columns each, two side waves copy operands into LDS and form the
-//        output (wave-specialised kernels, scalar and general-gate variants; a
-//        four-wave kernel that splits every product over the waves is kept as an
-//        alternative for testing).  Every product that touches the state or a
-//        residual uses a two-term bf16 split of the fp32 operand (hi + lo), so the
-//        state path keeps ~16 mantissa bits.
-// For few heads and long sequences (the state kernel then leaves CUs free) the
-// chunks are cut into blocks: the prep of every block runs on a side stream and the
-// state kernel is launched once per block on the caller's stream, after its block's
-// prep, carrying the state through S_T (launch_blocked below).
+//        output (wave-specialised kernels, scalar and general-gate variants).
+//        Every product that touches the state or a residual uses a two-term bf16
+//        split of the fp32 operand (hi + lo), so the state path keeps ~16 mantissa
+//        bits.
 //
 // MFMA operand layouts (v_mfma_f32_16x16x32_bf16, lane l, r = l % 16, q = l / 16):
 //   A (16 x 32): lane holds A[r][8q .. 8q+7];  B (32 x 16): B[8q .. 8q+7][r];
@@ -62,10 +63,10 @@ constexpr int kThreads = 256;
 constexpr int kRecT = 0;        // bf16 [64][64]  Tm
 constexpr int kRecPhi = 8192;   // bf16 [64][64]  P, leading term
 constexpr int kRecPlo = 16384;  // bf16 [64][64]  P, remainder
-constexpr int kRecGam = 24576;  // f32 [64]  e^{g_t}
-constexpr int kRecFac = 24832;  // f32 [64]  beta_s e^{g_C - g_s}, 0 past the chunk end
-constexpr int kRecGC = 25088;   // f32       e^{g_C}
-constexpr int kRecGlog = 25216; // f32 [64]  g_t (cumulative log decay inside the chunk)
+constexpr int kRecGam = 24576;  // f32 [64]  gamma_t = d(start, t)
+constexpr int kRecFac = 24832;  // f32 [64]  beta_s d(s, end), 0 past the chunk end
+constexpr int kRecGC = 25088;   // f32       gamma_end
+constexpr int kRecGlog = 25216; // f32 [64]  P_t (cumulative log decay inside the chunk, zero gates adding 0)
 constexpr int kRecBeta = 25472; // f32 [64]  beta_t, 0 past the chunk end
 constexpr int kRecBytes = 25728;
 
@@ -75,13 +76,13 @@ constexpr int kRecBytes = 25728;
 constexpr int kRcT = 0;          // bf16 [64][64]   Tm
 constexpr int kRcPh = 8192;      // bf16 [64][64]   P, leading term
 constexpr int kRcPl = 16384;     // bf16 [64][64]   P, remainder
-constexpr int kRcUh = 24576;     // bf16 [64][128]  U_t = u_t (.) e^{g_t}              (erase key)
+constexpr int kRcUh = 24576;     // bf16 [64][128]  U_t = u_t (.) gamma_t              (erase key)
 constexpr int kRcUl = 40960;
-constexpr int kRcQh = 57344;     // bf16 [64][128]  Q_t = q_t (.) e^{g_t}
+constexpr int kRcQh = 57344;     // bf16 [64][128]  Q_t = q_t (.) gamma_t
 constexpr int kRcQl = 73728;
-constexpr int kRcWh = 90112;     // bf16 [64][128]  W_t = w_t (.) e^{g_C - g_t}        (write key)
+constexpr int kRcWh = 90112;     // bf16 [64][128]  W_t = w_t (.) d(t, end)            (write key)
 constexpr int kRcWl = 106496;
-constexpr int kRcGC = 122880;    // f32 [128]       e^{g_C} per key channel
+constexpr int kRcGC = 122880;    // f32 [128]       gamma_end per key channel
 constexpr int kRcBytes = 123392;
 
 
@@ -151,6 +152,7 @@ __device__ __forceinline__ void store_p(char *dh, char *dl, const uint16_t (*Ph)
 template <bool GBF16>
 __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, int NT) {
     __shared__ float gl[kC], bl[kC];
+    __shared__ int zl[kC];
     __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part (first: the write keys)
     __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform; first holds the two P terms
     __shared__ __align__(16) float Xs[4][16][16];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
@@ -215,16 +217,27 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
             if (J <= IP) accP[J] = mfma(as_bf16x8(qa[kk]), kb, accP[J]);
         }
     }
-    // cumulative log decay and beta (wave 0)
+    // cumulative log decay and beta (wave 0), segmented at zero gates: P_t sums log alpha
+    // over the chunk's tokens <= t with a zero gate adding 0, and Z_t is the last token
+    // <= t whose gate is 0 (-1 if none).  The decay from token s to token t >= s is
+    // [Z_t <= s] e^{P_t - P_s}: a hard reset makes it exactly 0 and no infinity is ever
+    // subtracted from another.
     if (w == 0) {
-        float la = l < n ? logf(a_raw) : 0.f;
+        const bool zero = l < n && a_raw == 0.f;
+        float la = (l < n && !zero) ? logf(a_raw) : 0.f;
+        int z = zero ? l : -1;
         const float be = l < n ? b_raw : 0.f;
 #pragma unroll
         for (int off = 1; off < 64; off <<= 1) {
             const float y = __shfl_up(la, off);
-            if (l >= off) la += y;
+            const int zy = __shfl_up(z, off);
+            if (l >= off) {
+                la += y;
+                z = max(z, zy);
+            }
         }
         gl[l] = la;
+        zl[l] = z;
         bl[l] = be;
     }
 
@@ -233,10 +246,13 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     // decay / beta weights; Gram to LDS (fp32), scores to LDS as two bf16 terms.
     // Every LDS read is hoisted ahead of the stores so none waits behind them.
     float gG[4], gP[4], gS[4], bS[4];
+    int zG[4], zP[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         gG[i] = gl[16 * IG + 4 * q + i];
         gP[i] = gl[16 * IP + 4 * q + i];
+        zG[i] = zl[16 * IG + 4 * q + i];
+        zP[i] = zl[16 * IP + 4 * q + i];
         gS[i] = gl[16 * i + r];
         bS[i] = bl[16 * i + r];
     }
@@ -250,13 +266,13 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
             if (J <= IG) {
                 const int t = 16 * IG + 4 * q + i;
                 const float v = accG[J][i] * bS[J] * __expf(fminf(gG[i] - gS[J], 0.f));
-                As[t][s] = (s < t && t < n) ? v : 0.f;
+                As[t][s] = (s < t && t < n && zG[i] <= s) ? v : 0.f;
             }
             const int tp = 16 * IP + 4 * q + i;
             float pv = 0.f;
             if (J <= IP) {
                 const float v = accP[J][i] * bS[J] * __expf(fminf(gP[i] - gS[J], 0.f));
-                pv = (s <= tp && tp < n) ? v : 0.f;
+                pv = (s <= tp && tp < n && zP[i] <= s) ? v : 0.f;
             }
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
@@ -276,9 +292,10 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     if (tid < kC) {
         float *gam = reinterpret_cast<float *>(rec + kRecGam);
         float *fac = reinterpret_cast<float *>(rec + kRecFac);
-        gam[tid] = __expf(gl[tid]);
-        fac[tid] = tid < n ? bl[tid] * __expf(gl[n - 1] - gl[tid]) : 0.f;
-        if (tid == 0) *reinterpret_cast<float *>(rec + kRecGC) = __expf(gl[n - 1]);
+        const int zC = zl[n - 1];
+        gam[tid] = zl[tid] < 0 ? __expf(gl[tid]) : 0.f;
+        fac[tid] = (tid < n && zC <= tid) ? bl[tid] * __expf(gl[n - 1] - gl[tid]) : 0.f;
+        if (tid == 0) *reinterpret_cast<float *>(rec + kRecGC) = zC < 0 ? __expf(gl[n - 1]) : 0.f;
         reinterpret_cast<float *>(rec + kRecGlog)[tid] = gl[tid];
         reinterpret_cast<float *>(rec + kRecBeta)[tid] = bl[tid];
     }
@@ -290,29 +307,38 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
 // ---------------------------------------------------------------------------
 // One 256-thread block per chunk for a forget gate per key channel (ACH) and / or
 // beta vectors (BVEC; u = sqrt(beta^k) (.) k, w = sqrt(beta^k) (.) k_w; a scalar beta
-// gives u = k, w = beta k_w).  With g_t the per-channel cumulative log decay inside
-// the chunk, the decay factor e^{g_t - g_s} of the Gram matrix and of the scores
-// splits per channel into a row and a column factor, so both are plain products of
-// rescaled operands:
-//     A = strictly-lower( U What^T ),  P = lower-incl-diag( Q What^T ),
-//     U = u (.) e^{g_t},  Q = q (.) e^{g_t},  What = w (.) e^{-g_t}
-// (FG2-GDN page, section 3: the factored decay of the chunkwise form).  The factor
-// e^{-g_t} bounds the decay one chunk may accumulate per channel (about e^{-80}).
-// The record carries U, Q and W = w (.) e^{g_C - g_t} as two bf16 terms, Tm and P
-// as for the scalar path, and e^{g_C} per channel.
+// gives u = k, w = beta k_w).  Per key channel i the decay from token s to token
+// t >= s inside the chunk is [no zero gate in (s, t]] e^{P_t - P_s}, with P the
+// cumulative log decay in which zero gates add 0 (a zero gate is a hard reset).
+// The record carries U = u (.) gamma_t, Q = q (.) gamma_t and W = w (.) (decay from t
+// to the chunk end) as two bf16 terms each, gamma_t being the decay from the chunk
+// start through t -- every factor <= 1 -- plus Tm, P as for the scalar path, and the
+// decay over the whole chunk per channel.
+// The Gram and score matrices A_ts = sum_i u_ti w_si d_i(s, t) and
+// Pm_ts = sum_i q_ti w_si d_i(s, t) take one of two forms, chosen per chunk:
+//  * factored (no zero gate in the chunk and every channel's decay inside the chunk
+//    within e^{-80}): d_i(s, t) = e^{P_ti} e^{-P_si}, so both matrices are plain
+//    products of U (or Q) and What = w (.) e^{-P} on the matrix cores (three bf16
+//    terms);
+//  * exact (otherwise): every entry is summed over the channels with its own decay
+//    factor on the vector ALU, so no factor can overflow and a zero gate cuts the
+//    chunk exactly.
 template <bool GBF16, bool ACH, bool BVEC>
 __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, int NT) {
-    // the cumulative log decay g[t][i] is dead once the operands are formed; the
-    // Gram and UT arrays take its place
+    // the cumulative log decay P[t][i] is dead once the Gram and score entries are
+    // formed; the Gram and UT arrays take its place
     __shared__ __align__(16) float pool[kC * (kC + 4) + kC * (kC + 8)];
     __shared__ __align__(16) uint16_t Whs[kC][kD + 8], Wls[kC][kD + 8];  // What, two bf16 terms
     __shared__ __align__(16) float Xs[4][16][16];
+    __shared__ uint32_t zbits[2][kD];  // per channel: zero gates among tokens 0..31 | 32..63
     float(*gs)[kD + 4] = reinterpret_cast<float(*)[kD + 4]>(pool);
     float(*As)[kC + 4] = reinterpret_cast<float(*)[kC + 4]>(pool);
     float(*Ts)[kC + 8] = reinterpret_cast<float(*)[kC + 8]>(pool + kC * (kC + 4));
     uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
     uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
-    static_assert(kC * (kD + 4) <= kC * (kC + 4) + kC * (kC + 8), "pool holds g");
+    float(*Wx)[kD] = reinterpret_cast<float(*)[kD]>(&Whs[0][0]);  // exact form: w in fp32
+    static_assert(kC * (kD + 4) <= kC * (kC + 4) + kC * (kC + 8), "pool holds P");
+    static_assert(sizeof(float) * kC * kD <= 2 * sizeof(uint16_t) * kC * (kD + 8), "What space holds w");
 
     const int blk = blockIdx.x;
     const int c = blk % NT, bh = blk / NT;
@@ -326,8 +352,10 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
     const uint16_t *Q = static_cast<const uint16_t *>(p.q);
     char *rec = static_cast<char *>(p.ws) + ((long)bh * NT + c) * kRcBytes;
 
-    // g[t][i]: thread (i, half) scans 32 tokens of channel i; the upper half then adds
-    // the lower half's total.  Tokens past the chunk end decay by 1.
+    // P[t][i]: thread (i, half) scans 32 tokens of channel i; the upper half then adds
+    // the lower half's total.  Tokens past the chunk end decay by 1.  The chunk takes
+    // the factored form unless some channel has a zero gate or leaves [-80, 80].
+    bool unsafe = false;
     {
         const int i = tid & (kD - 1), hf = tid >> 7;
         float a[32];
@@ -335,11 +363,15 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
         for (int j = 0; j < 32; ++j)
             a[j] = ACH ? ld_gate(p.alpha, tok(32 * hf + j) * kD + i, GBF16) : ld_gate(p.alpha, tok(32 * hf + j), GBF16);
         float run = 0.f;
+        uint32_t zb = 0;
 #pragma unroll
         for (int j = 0; j < 32; ++j) {
-            run += 32 * hf + j < n ? logf(a[j]) : 0.f;
+            const bool valid = 32 * hf + j < n, zero = valid && a[j] == 0.f;
+            run += (valid && !zero) ? logf(a[j]) : 0.f;
+            zb |= zero ? (1u << j) : 0u;
             gs[32 * hf + j][i] = run;
         }
+        zbits[hf][i] = zb;
         __syncthreads();
         if (hf == 1) {
             const float off = gs[31][i];
@@ -347,7 +379,24 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
             for (int j = 0; j < 32; ++j) gs[32 + j][i] += off;
         }
         __syncthreads();
-        if (tid < kD) reinterpret_cast<float *>(rec + kRcGC)[tid] = __expf(gs[n - 1][tid]);
+#pragma unroll
+        for (int j = 0; j < 32; ++j) {
+            const float g = gs[32 * hf + j][i];
+            unsafe |= (32 * hf + j < n) && !(g >= -80.f && g <= 80.f);
+        }
+        unsafe |= zb != 0;
+    }
+    const bool exact = __syncthreads_or(unsafe);
+    // zero gate of channel i among tokens lo .. hi (inclusive; empty when lo > hi)
+    auto zero_in = [&](int i, int lo, int hi) -> bool {
+        if (lo > hi) return false;
+        const uint64_t zm = (uint64_t)zbits[0][i] | ((uint64_t)zbits[1][i] << 32);
+        const uint64_t upto = hi >= 63 ? ~0ull : ((1ull << (hi + 1)) - 1);
+        return (zm & upto & ~((1ull << lo) - 1)) != 0;
+    };
+    if (tid < kD) {
+        const bool z = zero_in(tid, 0, n - 1);
+        reinterpret_cast<float *>(rec + kRcGC)[tid] = z ? 0.f : __expf(gs[n - 1][tid]);
     }
 
     // operands: lane (r, q) of wave w forms keys 32 kk + 8 q .. + 7 of token t = 16 w + r
@@ -362,7 +411,7 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
         for (int kk = 0; kk < 4; ++kk) {
             const int k0 = 32 * kk + 8 * q;
             const u32x4 kr = ld16(K + rt + k0), kwr = ld16(KW + rt + k0), qr = ld16(Q + rtp + k0);
-            float u8[8], q8[8], wh8[8], wt8[8];
+            float u8[8], q8[8], wh8[8], wt8[8], wx8[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const uint32_t kb = kr[j >> 1], kwb = kwr[j >> 1], qb = qr[j >> 1];
@@ -377,11 +426,17 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
                 } else {
                     wv *= bsc;
                 }
-                const float g = gs[t][k0 + j], gq = gs[tp][k0 + j], gC = gs[n - 1][k0 + j];
-                u8[j] = t < n ? u * __expf(g) : 0.f;
-                wh8[j] = t < n ? wv * __expf(-g) : 0.f;
-                wt8[j] = t < n ? wv * __expf(gC - g) : 0.f;
-                q8[j] = tp < n ? qv * __expf(gq) : 0.f;
+                const int ch = k0 + j;
+                const float g = gs[t][ch], gq = gs[tp][ch], gC = gs[n - 1][ch];
+                // decay from the chunk start through t, and from t to the chunk end
+                const float head = zero_in(ch, 0, t) ? 0.f : __expf(g);
+                const float headq = zero_in(ch, 0, tp) ? 0.f : __expf(gq);
+                const float tail = zero_in(ch, t + 1, n - 1) ? 0.f : __expf(gC - g);
+                u8[j] = t < n ? u * head : 0.f;
+                wt8[j] = t < n ? wv * tail : 0.f;
+                q8[j] = tp < n ? qv * headq : 0.f;
+                wh8[j] = (t < n && !exact) ? wv * __expf(-g) : 0.f;
+                wx8[j] = t < n ? wv : 0.f;
             }
             bf16x8 h8, l8;
             split8(u8, h8, l8);
@@ -397,56 +452,105 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
             split8(wt8, h8, l8);
             *reinterpret_cast<u32x4 *>(rec + kRcWh + (t * kD + k0) * 2) = __builtin_bit_cast(u32x4, h8);
             *reinterpret_cast<u32x4 *>(rec + kRcWl + (t * kD + k0) * 2) = __builtin_bit_cast(u32x4, l8);
-            split8(wh8, h8, l8);
-            *reinterpret_cast<u32x4 *>(&Whs[t][k0]) = __builtin_bit_cast(u32x4, h8);
-            *reinterpret_cast<u32x4 *>(&Wls[t][k0]) = __builtin_bit_cast(u32x4, l8);
+            if (exact) {
+#pragma unroll
+                for (int j = 0; j < 8; ++j) Wx[t][k0 + j] = wx8[j];
+            } else {
+                split8(wh8, h8, l8);
+                *reinterpret_cast<u32x4 *>(&Whs[t][k0]) = __builtin_bit_cast(u32x4, h8);
+                *reinterpret_cast<u32x4 *>(&Wls[t][k0]) = __builtin_bit_cast(u32x4, l8);
+            }
         }
     }
     __syncthreads();
 
-    // Gram row block IG = w and score row block IP = 3 - w against What (three bf16
-    // products per term pair: hi.hi + hi.lo + lo.hi)
     const int IG = w, IP = 3 - w;
-    f32x4 accG[4], accP[4];
-#pragma unroll
-    for (int J = 0; J < 4; ++J) {
-        accG[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-        accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk)
+    if (!exact) {
+        // Gram row block IG = w and score row block IP = 3 - w against What (three bf16
+        // products per term pair: hi.hi + hi.lo + lo.hi)
+        f32x4 accG[4], accP[4];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
-            const bf16x8 bh8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Whs[16 * J + r][32 * kk + 8 * q]));
-            const bf16x8 bl8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Wls[16 * J + r][32 * kk + 8 * q]));
-            if (J <= IG) {
-                accG[J] = mfma(as_bf16x8(uh[kk]), bh8, accG[J]);
-                accG[J] = mfma(as_bf16x8(uh[kk]), bl8, accG[J]);
-                accG[J] = mfma(as_bf16x8(ul[kk]), bh8, accG[J]);
-            }
-            if (J <= IP) {
-                accP[J] = mfma(as_bf16x8(qh[kk]), bh8, accP[J]);
-                accP[J] = mfma(as_bf16x8(qh[kk]), bl8, accP[J]);
-                accP[J] = mfma(as_bf16x8(ql[kk]), bh8, accP[J]);
-            }
+            accG[J] = f32x4{0.f, 0.f, 0.f, 0.f};
+            accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
-    __syncthreads();  // g is dead: As and Ts take its place
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int J = 0; J < 4; ++J) {
+                const bf16x8 bh8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Whs[16 * J + r][32 * kk + 8 * q]));
+                const bf16x8 bl8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Wls[16 * J + r][32 * kk + 8 * q]));
+                if (J <= IG) {
+                    accG[J] = mfma(as_bf16x8(uh[kk]), bh8, accG[J]);
+                    accG[J] = mfma(as_bf16x8(uh[kk]), bl8, accG[J]);
+                    accG[J] = mfma(as_bf16x8(ul[kk]), bh8, accG[J]);
+                }
+                if (J <= IP) {
+                    accP[J] = mfma(as_bf16x8(qh[kk]), bh8, accP[J]);
+                    accP[J] = mfma(as_bf16x8(qh[kk]), bl8, accP[J]);
+                    accP[J] = mfma(as_bf16x8(ql[kk]), bh8, accP[J]);
+                }
+            }
+        __syncthreads();  // P is dead: As and Ts take its place
 
 #pragma unroll
-    for (int J = 0; J < 4; ++J) {
+        for (int J = 0; J < 4; ++J) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * J + r;
-            if (J <= IG) {
-                const int tg = 16 * IG + 4 * q + i;
-                As[tg][s] = (s < tg && tg < n) ? accG[J][i] : 0.f;
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * J + r;
+                if (J <= IG) {
+                    const int tg = 16 * IG + 4 * q + i;
+                    As[tg][s] = (s < tg && tg < n) ? accG[J][i] : 0.f;
+                }
+                const int tq = 16 * IP + 4 * q + i;
+                const float pv = (J <= IP && s <= tq && tq < n) ? accP[J][i] : 0.f;
+                const __bf16 hi = (__bf16)pv;
+                const __bf16 lo = (__bf16)(pv - (float)hi);
+                Ph[tq][s] = __builtin_bit_cast(uint16_t, hi);
+                Pl[tq][s] = __builtin_bit_cast(uint16_t, lo);
             }
-            const int tq = 16 * IP + 4 * q + i;
-            const float pv = (J <= IP && s <= tq && tq < n) ? accP[J][i] : 0.f;
+        }
+    } else {
+        // thread: row te = tid / 4, columns s = (tid % 4) + 4 j; each entry summed over
+        // the channels with its own decay [no zero in (s, te]] e^{P_te - P_s}
+        const int te = tid >> 2, s0 = tid & 3;
+        float aA[16], aP[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) aA[j] = aP[j] = 0.f;
+        if (te < n) {
+            const long rte = tok(te) * kD;
+            const float bsc = BVEC ? 0.f : ld_gate(p.beta_k, tok(te), GBF16);
+            (void)bsc;
+            for (int i = 0; i < kD; ++i) {
+                const float sbt = BVEC ? sqrtf(ld_gate(p.beta_k, rte + i, GBF16)) : 1.f;
+                const float ut = bf16_to_f32(K[rte + i]) * sbt, qt = bf16_to_f32(Q[rte + i]);
+                const float Pt = gs[te][i];
+                const uint64_t zm = (uint64_t)zbits[0][i] | ((uint64_t)zbits[1][i] << 32);
+                // zero gates of channel i among tokens <= te
+                const uint64_t upto = te >= 63 ? ~0ull : ((1ull << (te + 1)) - 1);
+                const uint64_t zt = zm & upto;
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int s = s0 + 4 * j;
+                    // no zero gate of channel i among tokens s + 1 .. te
+                    const bool open = (zt & ~((2ull << s) - 1)) == 0;
+                    const float d = (s <= te && open) ? __expf(Pt - gs[s][i]) : 0.f;
+                    const float wsd = Wx[s][i] * d;
+                    aA[j] = (s < te) ? fmaf(ut, wsd, aA[j]) : aA[j];
+                    aP[j] = fmaf(qt, wsd, aP[j]);
+                }
+            }
+        }
+        __syncthreads();  // P and w are dead: As and Ts take their place
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+            const int s = s0 + 4 * j;
+            As[te][s] = (s < te && te < n) ? aA[j] : 0.f;
+            const float pv = (s <= te && te < n) ? aP[j] : 0.f;
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
-            Ph[tq][s] = __builtin_bit_cast(uint16_t, hi);
-            Pl[tq][s] = __builtin_bit_cast(uint16_t, lo);
+            Ph[te][s] = __builtin_bit_cast(uint16_t, hi);
+            Pl[te][s] = __builtin_bit_cast(uint16_t, lo);
         }
     }
     __syncthreads();
@@ -456,306 +560,12 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
     store_ut(rec + kRcT, Ts, tid);
 }
 
-// ---------------------------------------------------------------------------
-// state kernel
-// ---------------------------------------------------------------------------
-// Operand orientation: every product takes a token-major input (rows of K, Q,
-// Tm, P, or of the transposed write key) as the A operand and a
-// [value column][k] bf16 array in LDS as the B operand.  A C tile then holds,
-// per lane, 4 consecutive tokens (or key channels) of one value column, which
-// is stored with one 8-byte write per term into exactly the layout the next
-// product reads with 16-byte loads.  The fp32 -> (hi, lo) split is done once,
-// by the lane that produced the value; consumers read ready bf16 fragments.
-template <int BV>
-struct ChunkFrags {
-    u32x4 k[4], q[4];          // A operands: K and Q rows of this wave's 16 tokens
-    u32x4 kw[4];               // rows of a separate write key (same layout as k)
-    u32x4 t[2], ph[2], pl[2];  // rows of Tm and of the two P terms (second half: waves 2, 3)
-    u32x4 v;                   // 16 bytes of this wave's 16 rows of the V tile
-    u32x4 gf;                  // wave 0: 16 bytes of the record's e^{g_t} | fac_t | e^{g_C}
-};
-
-// Per wave and chunk: K and Q rows of its 16 tokens, its rows of Tm and P (the
-// upper half of a triangular row block is never read), its 16 rows of the V tile
-// and, for wave 0, the chunk's decay factors.  Token rows past the end of a short
-// last chunk read the last valid row (their contributions are cancelled where
-// they are used), so every load is unconditional per lane and the whole chunk is
-// in flight while the previous one computes.
-template <int BV>
-__device__ __forceinline__ void load_chunk(const ChunkParams &p, int NT, int bh, int b, int h, int j0, int c,
-                                           int tid, bool sep_kw, ChunkFrags<BV> &f) {
-    constexpr int P8 = BV / 8;  // 16-byte pieces per token row of the V tile
-    const int w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
-    const int t0 = c * kC, n = min(kC, p.T - t0);
-    auto tok = [&](int t) -> long { return ((long)b * p.T + t0 + min(t, n - 1)) * p.H + h; };
-    const uint16_t *K = static_cast<const uint16_t *>(p.k);
-    const uint16_t *Q = static_cast<const uint16_t *>(p.q);
-    const uint16_t *V = static_cast<const uint16_t *>(p.v);
-    const char *rec = static_cast<const char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
-    const long rowk = tok(16 * w + r) * kD + 8 * q;
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-        f.k[kk] = ld16(K + rowk + kk * 32);
-        f.q[kk] = ld16(Q + rowk + kk * 32);
-    }
-    if (sep_kw) {
-        const uint16_t *KW = static_cast<const uint16_t *>(p.kw);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) f.kw[kk] = ld16(KW + rowk + kk * 32);
-    }
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-        if (kk == 1 && w < 2) break;
-        const int off = ((16 * w + r) * kC + kk * 32 + 8 * q) * 2;
-        f.t[kk] = ld16(rec + kRecT + off);
-        f.ph[kk] = ld16(rec + kRecPhi + off);
-        f.pl[kk] = ld16(rec + kRecPlo + off);
-    }
-    const int lv = l % (16 * P8);
-    f.v = ld16(V + tok(16 * w + lv / P8) * kD + j0 + 8 * (lv % P8));
-    if (w == 0) f.gf = ld16(rec + kRecGam + 16 * min(l, 32));
-}
-
-
 // fp32 x = hi + lo, both bf16 round-to-nearest-even, packed four to a u32x2.
 __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
     const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
     hi = u32x2{h0, h1};
     lo = u32x2{pk_bf16(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u)),
                pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u))};
-}
-
-// SEPKW: a separate write key is streamed (compile time, so that with k_w = k the
-// key fragments are used directly and no register copy of a load in flight exists)
-template <int BV, bool SEPKW>
-__global__ void __launch_bounds__(kThreads, BV == 16 ? 2 : 1) gdr_state_kernel(ChunkParams p, int NT, int nbh) {
-    constexpr int NJ = BV / 16;    // value-column tiles
-    constexpr int NVB = kD / BV;
-    constexpr int LZ = kD + 8;     // bf16 row pitch of the state operand arrays
-    constexpr int LT = kC + 8;     // bf16 row pitch of the residual operand arrays
-    constexpr int P8 = BV / 8;
-    // write keys, channel-major; the 8-token column blocks of row ch are XOR-swizzled
-    // by (ch / 8) % 8 so the transposing stores spread over the LDS banks
-    __shared__ __align__(16) uint16_t kwT[2][kD][kC + 8];
-    __shared__ __align__(16) float gfs[2][2 * kC + 4];            // e^{g_t} | fac_t | e^{g_C}
-    __shared__ __align__(16) uint16_t VO[4][16][BV + 8];          // per wave: its V rows, then its O rows
-    __shared__ __align__(16) uint16_t Zh[BV][LZ], Zl[BV][LZ];     // S^T as two bf16 terms
-    __shared__ __align__(16) uint16_t Rh[BV][LT], Rl[BV][LT];     // R^T
-    __shared__ __align__(16) uint16_t Dh[BV][LT], Dl[BV][LT];     // D^T
-    __shared__ __align__(16) uint16_t Eh[BV][LT], El[BV][LT];     // (fac D)^T
-
-    // block -> (head, value block): the NVB blocks of one head share an XCD (its L2)
-    const int x = blockIdx.x;
-    const int xcd = x & 7, rr = x >> 3;
-    const int vb = rr % NVB, grp = rr / NVB;
-    const int bh = grp * 8 + xcd;
-    if (bh >= nbh) return;
-    const int b = bh / p.H, h = bh % p.H, j0 = vb * BV;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, r = l & 15, q = l >> 4;
-    constexpr bool sep_kw = SEPKW;
-
-    // state, C layout: sacc[ct][nt][i] = S[16 (2 w + ct) + 4 q + i][j0 + 16 nt + r]
-    f32x4 sacc[2][NJ];
-#pragma unroll
-    for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int ch = 16 * (2 * w + ct) + 4 * q + i;
-                sacc[ct][nt][i] = p.S0 ? p.S0[((long)bh * kD + ch) * kD + j0 + 16 * nt + r] : 0.f;
-            }
-
-    auto put_z = [&]() __attribute__((always_inline)) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) {
-                u32x2 hi, lo;
-                split4(sacc[ct][nt], hi, lo);
-                *reinterpret_cast<u32x2 *>(&Zh[16 * nt + r][16 * (2 * w + ct) + 4 * q]) = hi;
-                *reinterpret_cast<u32x2 *>(&Zl[16 * nt + r][16 * (2 * w + ct) + 4 * q]) = lo;
-            }
-    };
-    // the transposed write key comes from the key rows the wave already holds
-    auto put_inputs = [&](const ChunkFrags<BV> &f, int buf) __attribute__((always_inline)) {
-        const int s = 16 * w + r;
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const u32x4 src = sep_kw ? f.kw[kk] : f.k[kk];
-            const int col = (((s >> 3) ^ ((4 * kk + q) & 7)) << 3) | (s & 7);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                kwT[buf][32 * kk + 8 * q + 2 * j][col] = (uint16_t)(src[j] & 0xffffu);
-                kwT[buf][32 * kk + 8 * q + 2 * j + 1][col] = (uint16_t)(src[j] >> 16);
-            }
-        }
-        const int lv = l % (16 * P8);
-        *reinterpret_cast<u32x4 *>(&VO[w][lv / P8][8 * (lv % P8)]) = f.v;
-        if (w == 0 && l <= 32) *reinterpret_cast<u32x4 *>(&gfs[buf][4 * l]) = f.gf;
-    };
-
-    uint16_t *O = static_cast<uint16_t *>(p.o);
-    // one chunk: consumes `cur` (loaded one chunk earlier) and fills `nxt`; the loop
-    // below alternates the two buffers so no fragment is ever copied
-    auto chunk_step = [&](const int c, ChunkFrags<BV> &cur, ChunkFrags<BV> &nxt) __attribute__((always_inline)) {
-        const int t0 = c * kC, n = min(kC, p.T - t0);
-        const int buf = c & 1;
-        load_chunk<BV>(p, NT, bh, b, h, j0, min(c + 1, NT - 1), tid, sep_kw, nxt);
-        const f32x4 gam = *reinterpret_cast<const f32x4 *>(&gfs[buf][16 * w + 4 * q]);
-
-        // Y = K S and O0 = Q S for this wave's 16 tokens (S as two bf16 terms)
-        f32x4 accY[NJ], accO[NJ];
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt) {
-            accY[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            accO[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) {
-                const bf16x8 zh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Zh[16 * nt + r][32 * kk + 8 * q]));
-                const bf16x8 zl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Zl[16 * nt + r][32 * kk + 8 * q]));
-                accY[nt] = mfma(as_bf16x8(cur.k[kk]), zh, accY[nt]);
-                accY[nt] = mfma(as_bf16x8(cur.k[kk]), zl, accY[nt]);
-                accO[nt] = mfma(as_bf16x8(cur.q[kk]), zh, accO[nt]);
-                accO[nt] = mfma(as_bf16x8(cur.q[kk]), zl, accO[nt]);
-            }
-        }
-        // R = V - e^{g_t} Y, zero past the end of the chunk
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt) {
-            // V is read unconditionally (a read inside the tail test becomes a branch
-            // with its own LDS round trip per element); rows past the end are zeroed after
-            f32x4 rv;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) rv[i] = bf16_to_f32(VO[w][4 * q + i][16 * nt + r]) - gam[i] * accY[nt][i];
-            if (n < kC) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (16 * w + 4 * q + i >= n) rv[i] = 0.f;
-            }
-            u32x2 hi, lo;
-            split4(rv, hi, lo);
-            *reinterpret_cast<u32x2 *>(&Rh[16 * nt + r][16 * w + 4 * q]) = hi;
-            *reinterpret_cast<u32x2 *>(&Rl[16 * nt + r][16 * w + 4 * q]) = lo;
-        }
-        lds_barrier();
-
-        // D = Tm R (Tm unit lower triangular: waves 0, 1 need only the first 32 tokens)
-        f32x4 accD[NJ];
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt) accD[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk == 1 && w < 2) break;
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) {
-                const bf16x8 rh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Rh[16 * nt + r][32 * kk + 8 * q]));
-                const bf16x8 rl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Rl[16 * nt + r][32 * kk + 8 * q]));
-                accD[nt] = mfma(as_bf16x8(cur.t[kk]), rh, accD[nt]);
-                accD[nt] = mfma(as_bf16x8(cur.t[kk]), rl, accD[nt]);
-            }
-        }
-        const f32x4 fac = *reinterpret_cast<const f32x4 *>(&gfs[buf][kC + 16 * w + 4 * q]);
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt) {
-            u32x2 hi, lo;
-            split4(accD[nt], hi, lo);
-            *reinterpret_cast<u32x2 *>(&Dh[16 * nt + r][16 * w + 4 * q]) = hi;
-            *reinterpret_cast<u32x2 *>(&Dl[16 * nt + r][16 * w + 4 * q]) = lo;
-            split4(accD[nt] * fac, hi, lo);
-            *reinterpret_cast<u32x2 *>(&Eh[16 * nt + r][16 * w + 4 * q]) = hi;
-            *reinterpret_cast<u32x2 *>(&El[16 * nt + r][16 * w + 4 * q]) = lo;
-        }
-        lds_barrier();
-
-        // O = e^{g_t} O0 + P D, staged through this wave's rows of VO, stored 16 bytes per lane
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt) accO[nt] *= gam;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            if (kk == 1 && w < 2) break;
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) {
-                const bf16x8 dh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Dh[16 * nt + r][32 * kk + 8 * q]));
-                const bf16x8 dl = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Dl[16 * nt + r][32 * kk + 8 * q]));
-                accO[nt] = mfma(as_bf16x8(cur.ph[kk]), dh, accO[nt]);
-                accO[nt] = mfma(as_bf16x8(cur.ph[kk]), dl, accO[nt]);
-                accO[nt] = mfma(as_bf16x8(cur.pl[kk]), dh, accO[nt]);
-            }
-        }
-#pragma unroll
-        for (int nt = 0; nt < NJ; ++nt)
-#pragma unroll
-            for (int i = 0; i < 4; i += 2) {
-                const uint32_t o2 = pk_bf16(accO[nt][i], accO[nt][i + 1]);
-                VO[w][4 * q + i][16 * nt + r] = (uint16_t)(o2 & 0xffffu);
-                VO[w][4 * q + i + 1][16 * nt + r] = (uint16_t)(o2 >> 16);
-            }
-        {
-            const int lv = l % (16 * P8);
-            const int t = 16 * w + lv / P8;
-            const u32x4 ov = *reinterpret_cast<const u32x4 *>(&VO[w][lv / P8][8 * (lv % P8)]);
-            if (l < 16 * P8 && t < n)
-                *reinterpret_cast<u32x4 *>(O + (((long)b * p.T + t0 + t) * p.H + h) * kD + j0 + 8 * (lv % P8)) = ov;
-        }
-
-        // S <- e^{g_C} S + K_w^T (fac D): channels 32 w .. 32 w + 31 of this wave
-        const float gC = gfs[buf][2 * kC];
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) sacc[ct][nt] *= gC;
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 ka[2];
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-                const int ch = 16 * (2 * w + ct) + r;
-                const int col = ((4 * kk + q) ^ ((ch >> 3) & 7)) << 3;
-                ka[ct] = as_bf16x8(*reinterpret_cast<const u32x4 *>(&kwT[buf][ch][col]));
-            }
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt) {
-                const bf16x8 eh = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Eh[16 * nt + r][32 * kk + 8 * q]));
-                const bf16x8 el = as_bf16x8(*reinterpret_cast<const u32x4 *>(&El[16 * nt + r][32 * kk + 8 * q]));
-#pragma unroll
-                for (int ct = 0; ct < 2; ++ct) {
-                    sacc[ct][nt] = mfma(ka[ct], eh, sacc[ct][nt]);
-                    sacc[ct][nt] = mfma(ka[ct], el, sacc[ct][nt]);
-                }
-            }
-        }
-        put_z();
-        put_inputs(nxt, (c + 1) & 1);
-        lds_barrier();
-    };
-
-    ChunkFrags<BV> fa, fb;
-    load_chunk<BV>(p, NT, bh, b, h, j0, 0, tid, sep_kw, fa);
-    put_inputs(fa, 0);
-    put_z();
-    __syncthreads();
-    int c = 0;
-    for (; c + 1 < NT; c += 2) {
-        chunk_step(c, fa, fb);
-        chunk_step(c + 1, fb, fa);
-    }
-    if (c < NT) chunk_step(c, fa, fb);
-
-    if (p.ST) {
-#pragma unroll
-        for (int ct = 0; ct < 2; ++ct)
-#pragma unroll
-            for (int nt = 0; nt < NJ; ++nt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int ch = 16 * (2 * w + ct) + 4 * q + i;
-                    p.ST[((long)bh * kD + ch) * kD + j0 + 16 * nt + r] = sacc[ct][nt][i];
-                }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -765,7 +575,7 @@ __global__ void __launch_bounds__(kThreads, BV == 16 ? 2 : 1) gdr_state_kernel(C
 // (batch, head).  Waves 0 and 1 ("chain" waves) own value columns
 // j0 + 16 w .. j0 + 16 w + 15 for all 64 tokens and 128 key channels and carry
 // only the sequential part of a chunk:
-//     Y = K S,  R = V - Diag(e^g) Y,  D = Tm R,  S <- e^{g_C} S + K_w^T (fac D).
+//     Y = K S,  R = V - Diag(gamma) Y,  D = Tm R,  S <- gamma_end S + K_w^T (fac D).
 // The state, R, D and the weighted residuals never leave the wave: each product
 // is a 16-column MFMA whose B operand is built in registers from the C tiles of
 // the product before it.  A C tile holds rows 4q .. 4q+3 of its 16 rows in lane
@@ -782,7 +592,7 @@ __global__ void __launch_bounds__(kThreads, BV == 16 ? 2 : 1) gdr_state_kernel(C
 // start, V and the two P terms into single buffers once the current ones have
 // been read), form O0 = Q S from the state fragments the chain wave leaves in
 // LDS, and after the chain wave has published D, form and store
-// O = Diag(e^g) O0 + P D.  Two barriers per chunk.
+// O = Diag(gamma) O0 + P D.  Two barriers per chunk.
 // LDS rows are kept whole; 16-byte pieces are XOR-swizzled by row so that each
 // read spreads over the LDS banks.
 constexpr int kCW = 32;  // value columns per workgroup
@@ -792,7 +602,7 @@ struct WsBuf {
     uint16_t Q[kC][kD];   // query rows, same layout
     uint16_t KW[kC][kD];  // separate write-key rows, same layout
     uint16_t T[kC][kC];   // Tm rows; piece p of row t stored at p ^ ((t >> 1) & 7)
-    float G[288];         // record tail: e^{g_t} | fac_t | e^{g_C} (+pad) | g_t | beta_t
+    float G[288];         // record tail: gamma_t | fac_t | gamma_end (+pad) | P_t | beta_t
 };
 constexpr int kGFac = 64, kGGC = 128, kGLog = 160, kGBeta = 224;
 static_assert((kRecBytes - kRecGam) == 288 * 4, "gate block of the record");
@@ -981,7 +791,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                         Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sl[kk]), Y[tt]);
                     }
             }
-            // R = V - e^{g_t} Y (rows past the chunk end zeroed)
+            // R = V - gamma_t Y (rows past the chunk end zeroed)
             u32x4 rh[2], rl[2];
             {
                 f32x4 R[4];
@@ -1040,7 +850,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
             }
             lds_barrier();  // B1: D published; V and the P terms of this chunk consumed
 
-            // S <- e^{g_C} S + K_w^T E; A fragments of K_w^T by the transposing read
+            // S <- gamma_end S + K_w^T E; A fragments of K_w^T by the transposing read
             {
                 const float gC = B.G[kGGC];
                 const uint16_t(*KWs)[kD] = SEPKW ? B.KW : B.K;
@@ -1173,11 +983,11 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 // The key-side operands come from the general-gate record with their decay and
 // beta applied (U, Q, W as two bf16 terms each), so the products take three bf16
 // terms (hi.hi + hi.lo + lo.hi):
-//     Y = U S,  R = vh - Y,  D = Tm R,  O = Q S + P D,  S <- Diag(e^{g_C}) S + W^T D.
+//     Y = U S,  R = vh - Y,  D = Tm R,  O = Q S + P D,  S <- Diag(gamma_end) S + W^T D.
 // vh = sqrt(beta) (.) v for a beta vector over the value channels (VSCALE).  The
 // operand tiles do not fit twice in LDS, so everything is single buffered: after
 // the first barrier of chunk c the side waves copy U, Q, Tm, P, V (and beta) of
-// chunk c + 1 (all consumed before it); after the second, W and e^{g_C}, which the
+// chunk c + 1 (all consumed before it); after the second, W and gamma_end, which the
 // chain waves read between the two barriers.
 struct ChanLds {
     uint16_t Uh[kC][kD], Ul[kC][kD];  // rows; piece p of row t stored at piece p ^ (t & 15)
@@ -1187,7 +997,7 @@ struct ChanLds {
     uint16_t Ph[kC][kC], Pl[kC][kC];
     uint16_t V[kC][kCW];
     float Bv[kC][kCW];                // beta over the value channels (fp32 or bf16 bits)
-    float GC[kD];                     // e^{g_C} per key channel
+    float GC[kD];                     // gamma_end per key channel
     u32x4 Sx[2][8][64];
     u32x4 Dx[2][4][64];
 };
@@ -1230,7 +1040,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
 #pragma unroll
         for (int u = 0; u < 8; ++u) dma16(src + 2 * (512 * u + offT[u & 1]), &dst[8 * u][0]);
     };
-    // W and e^{g_C} of chunk c (read by the chain waves between the two barriers)
+    // W and gamma_end of chunk c (read by the chain waves between the two barriers)
     auto issue_w = [&](int c) __attribute__((always_inline)) {
         const char *rc = rec(c);
         if (w == 0) {
@@ -1401,7 +1211,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
             }
             lds_barrier();  // B1: D published; U, Q, Tm, P, V of this chunk consumed; W landed
 
-            // S <- Diag(e^{g_C}) S + W^T D; A fragments of W^T by the transposing read
+            // S <- Diag(gamma_end) S + W^T D; A fragments of W^T by the transposing read
             {
                 const int a = r & 3, m = r >> 2;
 #pragma unroll
@@ -1517,10 +1327,6 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
     }
 }
 
-// State kernel: 1 = the wave-specialised kernel (default), 16 / 32 = the four-wave
-// kernel with that many value columns per workgroup (selected by flags, for testing).
-int state_variant(const ChunkParams &p) { return p.state_cols == 16 || p.state_cols == 32 ? p.state_cols : 1; }
-
 }  // namespace
 
 bool chunk_mfma_supported(const ChunkParams &p) { return p.io_bf16 && p.dk == kD && p.dv == kD && p.C == kC; }
@@ -1533,52 +1339,6 @@ size_t chunk_mfma_workspace(const ChunkParams &p) {
     const long NT = (p.T + kC - 1) / kC;
     return (size_t)p.B * p.H * NT * (general_gates(p) ? kRcBytes : kRecBytes);
 }
-
-namespace {
-constexpr int kPrefillBlocks = 8;   // most chunk blocks of a call (8 measured best: 16 and 4 both slower)
-static_assert(1 + kPrefillBlocks <= kSideEvents, "events of one call");
-SideStream g_prefill_side[kSideMaxDevices];
-
-// Scalar gates, wave-specialised state kernel, chunks cut into nblk blocks: the prep of
-// every block on the side stream, the state kernel block by block on the caller's
-// stream, each launch after its block's prep; the launches after the first start from
-// the state the one before left in ST.
-hipError_t launch_blocked(const ChunkParams &p, int NT, int nblk, const void *ws_fn, unsigned ws_grid,
-                          hipStream_t st) {
-    SideStream *sd = nullptr;
-    std::unique_lock<std::mutex> lock;
-    hipError_t e = side_stream_acquire(g_prefill_side, sd, lock);
-    if (e != hipSuccess) return e;
-    hipEvent_t fork = sd->ev[0], *prepped = sd->ev + 1;
-    const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
-                                   : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
-    const long nbh = (long)p.B * p.H;
-    int nt = NT, nb = (int)nbh;
-    auto bound = [&](int j) { return (int)((long)NT * j / nblk); };
-    if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;  // inputs ready on st
-    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
-    for (int j = 0; j < nblk; ++j) {
-        ChunkParams a = p;
-        a.c0 = bound(j);
-        a.c1 = bound(j + 1);
-        void *args[] = {&a, &nt};
-        if ((e = hipLaunchKernel(prep, dim3((unsigned)(nbh * (a.c1 - a.c0))), dim3(kThreads), args, 0,
-                                 sd->stream)) != hipSuccess)
-            return e;
-        if ((e = hipEventRecord(prepped[j], sd->stream)) != hipSuccess) return e;
-    }
-    for (int j = 0; j < nblk; ++j) {
-        ChunkParams a = p;
-        a.c0 = bound(j);
-        a.c1 = bound(j + 1);
-        if (j > 0) a.S0 = a.ST;  // in place: each workgroup reads and writes only its own columns
-        void *args[] = {&a, &nt, &nb};
-        if ((e = hipStreamWaitEvent(st, prepped[j], 0)) != hipSuccess) return e;
-        if ((e = hipLaunchKernel(ws_fn, dim3(ws_grid), dim3(256), args, 0, st)) != hipSuccess) return e;
-    }
-    return hipSuccess;
-}
-}  // namespace
 
 hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
     const long nbh = (long)p.B * p.H;
@@ -1615,32 +1375,18 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
         return hipLaunchKernel(states[(bvec ? 2 : 0) + (g16 ? 1 : 0)], dim3((unsigned)(groups * 8 * (kD / kCW))),
                                dim3(256), sargs, 0, st);
     }
-    const int bv = state_variant(p);
     const bool sep = p.kw != p.k;
     const void *ws_fn = sep ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
                             : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
-    const unsigned ws_grid = (unsigned)(groups * 8 * (kD / kCW));
-    // Few heads and many chunks: the state kernel holds one CU per workgroup (all of its
-    // LDS) on at most three quarters of the CUs, so the prep of later blocks of chunks
-    // runs beside it on a side stream; the state kernel walks the blocks in order, one
-    // launch per block, carrying the state through ST.
-    const int nblk = (bv == 1 && p.ST && NT >= 256 && ws_grid <= 192) ? min(kPrefillBlocks, NT / 64) : 1;
-    if (nblk > 1) return launch_blocked(arg, NT, nblk, ws_fn, ws_grid, st);
     {
         void *args[] = {&arg, &nt};
         const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
                                        : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
-        const hipError_t e = hipLaunchKernel(prep,
-                                             dim3((unsigned)(nbh * NT)), dim3(kThreads), args, 0, st);
+        const hipError_t e = hipLaunchKernel(prep, dim3((unsigned)(nbh * NT)), dim3(kThreads), args, 0, st);
         if (e != hipSuccess) return e;
     }
     void *args[] = {&arg, &nt, &nb};
-    if (bv == 1) return hipLaunchKernel(ws_fn, dim3(ws_grid), dim3(256), args, 0, st);
-    const void *fn = bv == 32 ? (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<32, true>)
-                                     : reinterpret_cast<const void *>(&gdr_state_kernel<32, false>))
-                              : (sep ? reinterpret_cast<const void *>(&gdr_state_kernel<16, true>)
-                                     : reinterpret_cast<const void *>(&gdr_state_kernel<16, false>));
-    return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / bv))), dim3(kThreads), args, 0, st);
+    return hipLaunchKernel(ws_fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(256), args, 0, st);
 }
 
 }  // namespace gdr

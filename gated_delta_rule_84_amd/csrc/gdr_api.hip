@@ -3,6 +3,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <new>
+
 #include "gdr.h"
 #include "gdr_internal.hpp"
 
@@ -33,13 +35,7 @@ int check_desc(const gdr_desc *d, bool prefill) {
     if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
     if (d->alpha_mode != GDR_ALPHA_SCALAR && d->alpha_mode != GDR_ALPHA_CHANNEL) return GDR_EINVAL;
     if (d->beta_mode < GDR_BETA_SCALAR || d->beta_mode > GDR_BETA_KV) return GDR_EINVAL;
-    if (d->flags & ~(GDR_FLAG_GENERIC_PATH | GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS |
-                     GDR_FLAG_READ_BEFORE_WRITE | GDR_FLAG_UNDECAYED_PREDICTION))
-        return GDR_EINVAL;
-    {
-        const int sel = d->flags & (GDR_FLAG_STATE_COLS16 | GDR_FLAG_STATE_COLS32 | GDR_FLAG_STATE_WAVECOLS);
-        if (sel & (sel - 1)) return GDR_EINVAL;  // at most one state-kernel selector
-    }
+    if (d->flags & ~(GDR_FLAG_READ_BEFORE_WRITE | GDR_FLAG_UNDECAYED_PREDICTION)) return GDR_EINVAL;
     if (d->beta_mode == GDR_BETA_SHARED && d->dk != d->dv) return GDR_EINVAL;
     if (d->dk < 8 || d->dk > 128 || (d->dk & 7) || d->dv < 8 || d->dv > 128 || (d->dv & 7))
         return GDR_EUNSUPPORTED;
@@ -58,16 +54,16 @@ ChunkParams chunk_params(const gdr_desc *d) {
     p.gate_bf16 = d->gate_dtype == GDR_BF16;
     p.alpha_ch = d->alpha_mode == GDR_ALPHA_CHANNEL;
     p.beta_mode = d->beta_mode;
-    p.state_cols = (d->flags & GDR_FLAG_STATE_COLS16)     ? 16
-                   : (d->flags & GDR_FLAG_STATE_COLS32)   ? 32
-                   : (d->flags & GDR_FLAG_STATE_WAVECOLS) ? 1
-                                                          : 0;
     return p;
 }
 
-int select_path(const gdr_desc *d, const ChunkParams &p) {
-    if (!(d->flags & GDR_FLAG_GENERIC_PATH) && chunk_mfma_supported(p)) return 1;
-    return 2;
+int select_path(const gdr_desc *, const ChunkParams &p) { return chunk_mfma_supported(p) ? 1 : 2; }
+
+// A context passed to a call must belong to the current device.
+bool context_ok(const gdr_context *ctx) {
+    if (!ctx) return true;
+    int dev = -1;
+    return hipGetDevice(&dev) == hipSuccess && dev == ctx->device;
 }
 
 int device_lds_limit() {
@@ -84,7 +80,42 @@ using namespace gdr;
 
 extern "C" {
 
-int gdr_version(void) { return (1 << 16) | 0; }
+int gdr_version(void) { return (2 << 16) | 0; }
+
+int gdr_context_create(gdr_context **out) {
+    if (!out) return GDR_EINVAL;
+    *out = nullptr;
+    gdr_context *c = new (std::nothrow) gdr_context;
+    if (!c) return GDR_EHIP;
+    memset(c, 0, sizeof(*c));
+    hipError_t e = hipGetDevice(&c->device);
+    if (e == hipSuccess) e = hipStreamCreateWithFlags(&c->stream, hipStreamNonBlocking);
+    int made = 0;
+    for (; e == hipSuccess && made < kCtxEvents; ++made)
+        e = hipEventCreateWithFlags(&c->ev[made], hipEventDisableTiming);
+    if (e != hipSuccess) {
+        for (int j = 0; j < made; ++j)
+            if (c->ev[j]) (void)hipEventDestroy(c->ev[j]);
+        if (c->stream) (void)hipStreamDestroy(c->stream);
+        delete c;
+        return GDR_EHIP;
+    }
+    *out = c;
+    return GDR_OK;
+}
+
+int gdr_context_destroy(gdr_context *c) {
+    if (!c) return GDR_OK;
+    hipError_t e = hipStreamSynchronize(c->stream);
+    for (int j = 0; j < kCtxEvents; ++j) {
+        const hipError_t f = hipEventDestroy(c->ev[j]);
+        if (e == hipSuccess) e = f;
+    }
+    const hipError_t f = hipStreamDestroy(c->stream);
+    if (e == hipSuccess) e = f;
+    delete c;
+    return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
 
 const char *gdr_status_string(int s) {
     switch (s) {
@@ -159,7 +190,6 @@ int gdr_chunk_fwd_ckpt(const gdr_desc *d, const void *q, const void *k, const vo
             if (overlaps(ST, ns, ins[i], lens[i])) return GDR_EINVAL;
     }
     const int path = select_path(d, p);
-    if (nck > 0 && path == 1 && (p.state_cols == 16 || p.state_cols == 32)) return GDR_EUNSUPPORTED;
     const size_t ws_need = path == 1 ? chunk_mfma_workspace(p) : 0;
     if (ws_need > 0 && (!workspace || workspace_bytes < ws_need || !aligned16(workspace)))
         return GDR_EWORKSPACE;
@@ -252,8 +282,10 @@ size_t gdr_osdn_precond_workspace_size(const gdr_desc *d) {
 }
 
 int gdr_osdn_precond(const gdr_desc *d, const void *k, const void *beta, const void *r, float eta, const float *d0,
-                     void *k_w, float *dT, float *qgeo, void *workspace, size_t workspace_bytes, void *stream) {
+                     void *k_w, float *dT, float *qgeo, void *workspace, size_t workspace_bytes, gdr_context *ctx,
+                     void *stream) {
     if (!d || d->B < 0 || d->T < 0 || d->H < 0) return GDR_EINVAL;
+    if (!context_ok(ctx)) return GDR_EINVAL;
     if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
     if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
     if (d->beta_mode != GDR_BETA_SCALAR) return GDR_EINVAL;
@@ -288,7 +320,7 @@ int gdr_osdn_precond(const gdr_desc *d, const void *k, const void *beta, const v
             if (overlaps(workspace, wneed, ins[j], ilens[j])) return GDR_EINVAL;
     }
     const hipError_t e = launch_osdn_precond(d->B, d->T, d->H, d->dk, d->io_dtype == GDR_BF16, d->gate_dtype == GDR_BF16,
-                                             eta, k, beta, r, d0, k_w, dT, qgeo, workspace,
+                                             eta, k, beta, r, d0, k_w, dT, qgeo, workspace, ctx,
                                              static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
@@ -300,8 +332,9 @@ size_t gdr_sdm_workspace_size(const gdr_desc *d, int32_t n, int32_t W, int32_t R
 
 int gdr_sdm_fwd(const gdr_desc *d, int32_t n, int32_t W, int32_t R, const float *ks, const float *qs, const void *v,
                 const void *alpha, const void *beta, float *M, void *o, int32_t *w_slots, int32_t *r_slots,
-                void *workspace, size_t workspace_bytes, void *stream) {
+                void *workspace, size_t workspace_bytes, gdr_context *ctx, void *stream) {
     if (!d || d->B < 0 || d->T < 0 || d->H < 0) return GDR_EINVAL;
+    if (!context_ok(ctx)) return GDR_EINVAL;
     if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
     if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
     if (n < 1 || W < 1 || R < 1) return GDR_EINVAL;
@@ -332,7 +365,7 @@ int gdr_sdm_fwd(const gdr_desc *d, int32_t n, int32_t W, int32_t R, const float 
         }
     }
     const hipError_t e = launch_sdm(d->B, d->T, d->H, n, W, R, d->io_dtype == GDR_BF16, d->gate_dtype == GDR_BF16,
-                                    ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace,
+                                    ks, qs, v, alpha, beta, M, o, w_slots, r_slots, workspace, ctx,
                                     static_cast<hipStream_t>(stream));
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }

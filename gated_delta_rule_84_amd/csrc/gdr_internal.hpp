@@ -5,41 +5,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include <mutex>
-
-namespace gdr {
-
-// A side stream of one module on one device, with events for forking work off the
-// caller's stream and joining it back.  Created on the module's first call on the
-// device (default priority, non-blocking) and kept until the process ends; the
-// host-side enqueue of a call is serialised by `mu`.  The fork / join through events
-// keeps a call capturable in a HIP graph of the caller's stream.
-constexpr int kSideMaxDevices = 64;
-constexpr int kSideEvents = 66;
-struct SideStream {
-    std::mutex mu;
-    bool ready = false;
-    hipStream_t stream = nullptr;
-    hipEvent_t ev[kSideEvents] = {};
+// A caller-owned execution context (include/gdr.h): a second stream on one device and
+// the events that fork work onto it from the caller's stream and join it back.  The
+// library keeps no copy of it; one context serves one call at a time.
+constexpr int kCtxEvents = 66;
+struct gdr_context {
+    int device;
+    hipStream_t stream;
+    hipEvent_t ev[kCtxEvents];
 };
 
-// The entry of `table` for the current device, created if needed.  The caller holds
-// `side->mu` while it enqueues (locked here on success).
-inline hipError_t side_stream_acquire(SideStream (&table)[kSideMaxDevices], SideStream *&side,
-                                      std::unique_lock<std::mutex> &lock) {
-    int dev = 0;
-    hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return e;
-    if (dev < 0 || dev >= kSideMaxDevices) return hipErrorInvalidDevice;
-    side = &table[dev];
-    lock = std::unique_lock<std::mutex>(side->mu);
-    if (side->ready) return hipSuccess;
-    e = hipStreamCreateWithFlags(&side->stream, hipStreamNonBlocking);
-    for (int j = 0; j < kSideEvents && e == hipSuccess; ++j)
-        e = hipEventCreateWithFlags(&side->ev[j], hipEventDisableTiming);
-    if (e == hipSuccess) side->ready = true;
-    return e;
-}
+namespace gdr {
 
 // Parameters of one prefill call, already validated by the host API.
 struct ChunkParams {
@@ -48,7 +24,6 @@ struct ChunkParams {
     int gate_bf16;  // alpha, beta_k, beta_v are bf16 (else fp32)
     int alpha_ch;   // alpha is per key channel
     int beta_mode;  // 0 scalar, 1 shared vector, 2 separate k / v vectors
-    int state_cols; // matrix-core state kernel: 16 / 32 four-wave width, 1 wave-specialised, 0 default
     const void *q, *k, *kw, *v, *alpha, *beta_k, *beta_v;  // kw never NULL here (defaults to k)
     const float *S0;  // may be NULL (zero state)
     void *o;
@@ -90,10 +65,10 @@ size_t osdn_precond_workspace(int B, int T, int H);
 size_t sdm_workspace(int B, int T, int H, int W, int R);
 hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
                       const float *qs, const void *v, const void *alpha, const void *beta, float *M, void *o,
-                      int32_t *wslots, int32_t *rslots, void *ws, hipStream_t s);
+                      int32_t *wslots, int32_t *rslots, void *ws, const gdr_context *ctx, hipStream_t s);
 hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
                                const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
-                               void *ws, hipStream_t s);
+                               void *ws, const gdr_context *ctx, hipStream_t s);
 hipError_t launch_mc_readout(int B, int T, int H, int N, int seg, const void *q, const float *ckpt,
                              const float *gates, const void *oin, void *oout, void *ws, hipStream_t s);
 

@@ -28,12 +28,12 @@
 //   osdn_qgeo_kernel    q_geo per (batch, head) from the chunk sums, in chunk order.
 // Everything is fp32 (exact products of the stored keys) except the log-ratio
 // sums (fp64).  The chain is the only sequential part: three small matrix-vector
-// products per chunk, on one workgroup per (batch, head).  For a long sequence the
-// chunks are cut into blocks: the chunk solve of every block and the emission of
-// each finished block run on a side stream while the chain works through the
-// blocks in order on the caller's stream (it occupies one CU per sequence, so the
-// parallel passes fill the others); the chain carries d from one block to the next
-// through the next chunk's record.
+// products per chunk, on one workgroup per (batch, head).  For a long sequence and a
+// caller-owned execution context, the chunks are cut into blocks: the chunk solve of
+// every block and the emission of each finished block run on the context's second
+// stream while the chain works through the blocks in order on the caller's stream (it
+// occupies one CU per sequence, so the parallel passes fill the others); the chain
+// carries d from one block to the next through the next chunk's record.
 #include <math.h>
 
 #include "gdr_device.hpp"
@@ -531,13 +531,12 @@ size_t osdn_precond_workspace(int B, int T, int H) {
 
 namespace {
 constexpr int kOsdnBlocks = 32;  // most chunk blocks of a call
-static_assert(2 + 2 * kOsdnBlocks <= kSideEvents, "events of one call");
-SideStream g_osdn_side[kSideMaxDevices];
+static_assert(2 + 2 * kOsdnBlocks <= kCtxEvents, "events of one call");
 }  // namespace
 
 hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gate_bf16, float eta, const void *k,
                                const void *beta, const void *r, const float *d0, void *kw, float *dT, float *qgeo,
-                               void *ws, hipStream_t st) {
+                               void *ws, const gdr_context *ctx, hipStream_t st) {
     const long nbh = (long)B * H;
     if (nbh == 0) return hipSuccess;
     PcParams p;
@@ -570,25 +569,23 @@ hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gat
                                dim3(kPThreads), args, 0, st);
     };
     hipError_t e;
-    const int nblk = p.NT >= 256 ? min(kOsdnBlocks, p.NT / 64) : 1;
+    const int nblk = ctx && p.NT >= 256 ? min(kOsdnBlocks, p.NT / 64) : 1;
     if (nblk == 1) {
         if (p.NT > 0 && (e = launch(chunk_fn, 0, p.NT, st)) != hipSuccess) return e;
         if ((e = launch(chain_fn, 0, p.NT, st)) != hipSuccess) return e;  // with no chunk: dT = d0
         if (p.NT > 0 && (e = launch(emit_fn, 0, p.NT, st)) != hipSuccess) return e;
         return finish();
     }
-    SideStream *sd = nullptr;
-    std::unique_lock<std::mutex> lock;
-    if ((e = side_stream_acquire(g_osdn_side, sd, lock)) != hipSuccess) return e;
-    hipEvent_t fork = sd->ev[0], join = sd->ev[1], *solved = sd->ev + 2, *chained = sd->ev + 2 + kOsdnBlocks;
+    hipStream_t side = ctx->stream;
+    const hipEvent_t fork = ctx->ev[0], join = ctx->ev[1], *solved = ctx->ev + 2, *chained = ctx->ev + 2 + kOsdnBlocks;
     auto bound = [&](int j) { return (int)((long)p.NT * j / nblk); };
     // side: every block's chunk solve; caller's stream: the chain, block by block, each
     // after its block's solve; side again: each block's emission after its chain
     if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;  // inputs ready on st
-    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
     for (int j = 0; j < nblk; ++j) {
-        if ((e = launch(chunk_fn, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
-        if ((e = hipEventRecord(solved[j], sd->stream)) != hipSuccess) return e;
+        if ((e = launch(chunk_fn, bound(j), bound(j + 1), side)) != hipSuccess) return e;
+        if ((e = hipEventRecord(solved[j], side)) != hipSuccess) return e;
     }
     for (int j = 0; j < nblk; ++j) {
         if ((e = hipStreamWaitEvent(st, solved[j], 0)) != hipSuccess) return e;
@@ -596,10 +593,10 @@ hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gat
         if ((e = hipEventRecord(chained[j], st)) != hipSuccess) return e;
     }
     for (int j = 0; j < nblk; ++j) {
-        if ((e = hipStreamWaitEvent(sd->stream, chained[j], 0)) != hipSuccess) return e;
-        if ((e = launch(emit_fn, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
+        if ((e = hipStreamWaitEvent(side, chained[j], 0)) != hipSuccess) return e;
+        if ((e = launch(emit_fn, bound(j), bound(j + 1), side)) != hipSuccess) return e;
     }
-    if ((e = hipEventRecord(join, sd->stream)) != hipSuccess) return e;
+    if ((e = hipEventRecord(join, side)) != hipSuccess) return e;
     if ((e = hipStreamWaitEvent(st, join, 0)) != hipSuccess) return e;
     return finish();
 }

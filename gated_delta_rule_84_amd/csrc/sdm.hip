@@ -617,19 +617,19 @@ size_t sdm_workspace(int B, int T, int H, int W, int R) {
     return (size_t)B * T * H * (wp + rp) * (sizeof(int32_t) + sizeof(float));
 }
 
-// The selection of a block of tokens runs on a side stream while the table pass works
-// through the blocks before it on the caller's stream: the table pass holds one
-// workgroup per CU and is latency bound, so the selection's blocks fill the rest of
-// each CU.  The table pass of block j waits for the selection of block j only.
+// With a caller-owned execution context, the selection of a block of tokens runs on the
+// context's second stream while the table pass works through the blocks before it on
+// the caller's stream: the table pass holds one workgroup per CU and is latency bound,
+// so the selection's blocks fill the rest of each CU.  The table pass of block j waits
+// for the selection of block j only.
 namespace {
 constexpr int kSdmBlocks = 64;    // most token blocks of a call (blocks of >= 128 tokens)
-static_assert(kSdmBlocks + 1 <= kSideEvents, "events of one call");
-SideStream g_sdm_side[kSideMaxDevices];
+static_assert(kSdmBlocks + 1 <= kCtxEvents, "events of one call");
 }  // namespace
 
 hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int gate_bf16, const float *ks,
                       const float *qs, const void *v, const void *alpha, const void *beta, float *M, void *o,
-                      int32_t *wslots, int32_t *rslots, void *ws, hipStream_t st) {
+                      int32_t *wslots, int32_t *rslots, void *ws, const gdr_context *ctx, hipStream_t st) {
     const long ntok = (long)B * T * H;
     if (ntok == 0) return hipSuccess;
     SdmParams p;
@@ -667,22 +667,20 @@ hipError_t launch_sdm(int B, int T, int H, int n, int W, int R, int io_bf16, int
         return hipLaunchKernel(fn, dim3((unsigned)((items + kSelWaves - 1) / kSelWaves)), dim3(64 * kSelWaves), args,
                                0, s);
     };
-    const int nblk = T >= 1024 ? min(kSdmBlocks, T / 128) : 1;
+    const int nblk = ctx && T >= 1024 ? min(kSdmBlocks, T / 128) : 1;
     if (nblk == 1) {
         const hipError_t e = launch(sel, 0, T, st);
         return e != hipSuccess ? e : launch(tab, 0, T, st);
     }
-    SideStream *sd = nullptr;
-    std::unique_lock<std::mutex> lock;
-    hipError_t e = side_stream_acquire(g_sdm_side, sd, lock);
-    if (e != hipSuccess) return e;
-    hipEvent_t fork = sd->ev[0], *done = sd->ev + 1;
+    hipError_t e;
+    hipStream_t side = ctx->stream;
+    const hipEvent_t fork = ctx->ev[0], *done = ctx->ev + 1;
     auto bound = [&](int j) { return (int)((long)T * j / nblk); };
     if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;           // inputs ready on st
-    if ((e = hipStreamWaitEvent(sd->stream, fork, 0)) != hipSuccess) return e;
+    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
     for (int j = 0; j < nblk; ++j) {
-        if ((e = launch(sel, bound(j), bound(j + 1), sd->stream)) != hipSuccess) return e;
-        if ((e = hipEventRecord(done[j], sd->stream)) != hipSuccess) return e;
+        if ((e = launch(sel, bound(j), bound(j + 1), side)) != hipSuccess) return e;
+        if ((e = hipEventRecord(done[j], side)) != hipSuccess) return e;
     }
     for (int j = 0; j < nblk; ++j) {
         if ((e = hipStreamWaitEvent(st, done[j], 0)) != hipSuccess) return e;

@@ -29,16 +29,12 @@
  * [OSDN page, section 1; delta-mem page, section 2.A].
  *
  * Conventions shared by every entry point:
- *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates no device memory, keeps no pointer after a call returns and has
- *     no global mutable state, with one exception: gdr_sdm_fwd, gdr_osdn_precond
- *     and gdr_chunk_fwd (few heads, long sequences, final state requested) each
- *     create, on their first such call on a device, one side stream (default
- *     priority, non-blocking) and a few events, kept until the process ends; the
- *     use of each is serialised by a mutex.  Calls from several host threads are
- *     safe.  Work forked onto a side stream is joined back to `stream` through
- *     events before the call's last launch, so a call captured from `stream` into
- *     a HIP graph takes all of it in.
+ *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     allocates no device memory, keeps no pointer after a call returns and has no
+ *     global mutable state, so calls from several host threads are safe.  The two
+ *     calls that can overlap independent work on a second stream (gdr_osdn_precond,
+ *     gdr_sdm_fwd) take it from a caller-owned gdr_context (below); with a NULL
+ *     context they run everything on `stream`.
  *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
  *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
  *     alignment (so per-step slices of a gate array are accepted).
@@ -84,15 +80,7 @@ typedef enum gdr_alpha_mode { GDR_ALPHA_SCALAR = 0, GDR_ALPHA_CHANNEL = 1 } gdr_
  *   KV:     beta_k [.., H, dk] and beta_v [.., H, dv]     (FG2-GDN+) */
 typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_KV = 2 } gdr_beta_mode;
 
-/* Flags (gdr_desc.flags). */
-#define GDR_FLAG_GENERIC_PATH 0x1  /* prefill: use the fp32 vector-ALU chunk kernel even where
-                                      the bf16 matrix-core kernel applies (testing aid) */
-#define GDR_FLAG_STATE_COLS16 0x2  /* prefill, matrix-core path: run the state recurrence with the
-                                      four-wave kernel, 16 value columns per workgroup (testing aid) */
-#define GDR_FLAG_STATE_COLS32 0x4  /* the same with 32 value columns per workgroup (testing aid) */
-#define GDR_FLAG_STATE_WAVECOLS 0x8 /* the wave-specialised state kernel (the default); at most one
-                                      of the three STATE flags */
-/* Decode only (gdr_chunk_fwd returns GDR_EUNSUPPORTED for them); together they give the
+/* Flags (gdr_desc.flags), decode only (gdr_chunk_fwd returns GDR_EUNSUPPORTED for them); together they give the
  * delta-mem step [delta-mem page, section 2.A update rule, section 2.C read]:
  *   READ_BEFORE_WRITE:      o = S_{t-1}^T q        (the state before the gate and the write)
  *   UNDECAYED_PREDICTION:   S_t = Diag(alpha) S_{t-1} + w (vh - S_{t-1}^T u)^T
@@ -108,10 +96,7 @@ typedef enum gdr_beta_mode { GDR_BETA_SCALAR = 0, GDR_BETA_SHARED = 1, GDR_BETA_
  *   gate_dtype: element type of alpha, beta_k, beta_v
  * The bf16 matrix-core kernels serve io_dtype == GDR_BF16, dk == dv == 128,
  * chunk == 64, for every gate and beta layout (a faster pair for scalar alpha
- * and scalar beta); every other accepted shape runs the fp32 vector-ALU kernel.
- * With alpha_mode == CHANNEL the per-channel cumulative log-decay inside one
- * chunk must stay above about -80 (fp32 exponent range of the factored decay);
- * use a shorter chunk (vector-ALU kernel) for faster-decaying inputs. */
+ * and scalar beta); every other accepted shape runs the fp32 vector-ALU kernel. */
 typedef struct gdr_desc {
     int32_t B, T, H, dk, dv;
     int32_t chunk;
@@ -121,6 +106,26 @@ typedef struct gdr_desc {
     int32_t beta_mode;
     int32_t flags;
 } gdr_desc;
+
+/*
+ * Execution context: a second stream on one device (default priority, non-blocking)
+ * and the events that fork work onto it from the caller's stream and join it back
+ * before the call's last launch.  Created and destroyed by the caller; the library
+ * holds no reference to it between calls.  A call given a context leaves all of its
+ * work ordered on `stream` (and capturable into a HIP graph of `stream`: the fork
+ * and join pull the second stream into the capture).  One context serves one call at
+ * a time: the caller must not pass the same context to two calls that may run
+ * concurrently, nor use it elsewhere while a graph capture that used it is open.
+ *
+ * gdr_context_create: on the current device; *ctx receives the handle.
+ *   GDR_EINVAL for a NULL ctx, GDR_EHIP if the runtime cannot create the stream or
+ *   events (nothing is left allocated then).
+ * gdr_context_destroy: waits for the second stream to drain, then releases it;
+ *   NULL is accepted and does nothing.
+ */
+typedef struct gdr_context gdr_context;
+int gdr_context_create(gdr_context **ctx);
+int gdr_context_destroy(gdr_context *ctx);
 
 /* Bytes of device workspace gdr_chunk_fwd needs for `desc` (0 if none).
  * Returns 0 for a descriptor gdr_chunk_fwd would reject. */
@@ -176,9 +181,7 @@ int gdr_decode_step(const gdr_desc *desc, const void *q, const void *k, const vo
  *   ckpt      [B, H, N, dk, dv] fp32, N = floor(T / seg_len): slot s holds the state
  *             after token (s + 1) * seg_len - 1.  May be NULL when N == 0; must not
  *             overlap any input, o or ST.
- * Everything else is exactly gdr_chunk_fwd (same outputs, same workspace size).  The
- * four-wave state kernels selected by GDR_FLAG_STATE_COLS16 / 32 do not keep segment
- * states: with those flags the call returns GDR_EUNSUPPORTED.
+ * Everything else is exactly gdr_chunk_fwd (same outputs, same workspace size).
  */
 int gdr_chunk_fwd_ckpt(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
                        const void *v, const void *alpha, const void *beta_k, const void *beta_v,
@@ -229,19 +232,21 @@ int gdr_mc_readout(const gdr_desc *desc, const void *q, const float *ckpt, int32
  *   k      [B, T, H, dk] io_dtype (required); k_w [B, T, H, dk] io_dtype output
  *   beta   [B, T, H] gate_dtype (required; desc->beta_mode must be GDR_BETA_SCALAR)
  *   r      [B, T, H] gate_dtype retention in [0, 1], or NULL for 1 (values below
- *          1e-30 act as 0)
+ *          1e-30 act as 1e-30, which for d's update is indistinguishable from 0)
  *   d0     [B, H, dk] fp32 or NULL;  dT [B, H, dk] fp32 final preconditioner or NULL
  *   qgeo   [B, H] fp32 or NULL (1 when T == 0)
  *   workspace at least gdr_osdn_precond_workspace_size() bytes
+ *   ctx    an execution context of the current device, or NULL
  * dk: multiple of 8 in [8, 128].  desc->dv, chunk and alpha_mode are not used.
- * From T >= 16,384 (256 chunks of 64) the chunk solve and the emission of the
- * write keys run on the library's side stream beside the sequential scan, block
- * by block (see the conventions above); the results are the same bit for bit.
+ * With a context and T >= 16,384 (256 chunks of 64) the chunk solve and the
+ * emission of the write keys run on the context's second stream beside the
+ * sequential scan, block by block; the results are the same bit for bit.  A
+ * context of another device gives GDR_EINVAL.
  */
 size_t gdr_osdn_precond_workspace_size(const gdr_desc *desc);
 int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, const void *r, float eta,
                      const float *d0, void *k_w, float *dT, float *qgeo, void *workspace,
-                     size_t workspace_bytes, void *stream);
+                     size_t workspace_bytes, gdr_context *ctx, void *stream);
 
 /*
  * Sparse Delta Memory [Resumo Técnico: Sparse Delta Memory (SDM), Mecanismo Central
@@ -264,16 +269,17 @@ int gdr_osdn_precond(const gdr_desc *desc, const void *k, const void *beta, cons
  *   w_slots, r_slots [B, T, H, W] / [B, T, H, R] int32 outputs (selected slots, best
  *             first) or NULL
  *   workspace at least gdr_sdm_workspace_size() bytes
+ *   ctx       an execution context of the current device, or NULL
  * Supported: dv == 128, 1 <= n <= 1024, 1 <= W, R <= min(128, n * n) (else
  * GDR_EUNSUPPORTED).  desc->dk, chunk, alpha_mode and beta_mode are not used.
- * With T >= 1024 the selection of later token blocks runs on a side stream of the
- * current device, forked from and joined back into `stream` through events (the call
- * stays in stream order and capturable); `stream` must belong to the current device.
+ * With a context and T >= 1024 the selection of later token blocks runs on the
+ * context's second stream beside the table pass (the results are the same bit for
+ * bit); a context of another device gives GDR_EINVAL.
  */
 size_t gdr_sdm_workspace_size(const gdr_desc *desc, int32_t n, int32_t W, int32_t R);
 int gdr_sdm_fwd(const gdr_desc *desc, int32_t n, int32_t W, int32_t R, const float *ks, const float *qs,
                 const void *v, const void *alpha, const void *beta, float *M, void *o, int32_t *w_slots,
-                int32_t *r_slots, void *workspace, size_t workspace_bytes, void *stream);
+                int32_t *r_slots, void *workspace, size_t workspace_bytes, gdr_context *ctx, void *stream);
 
 /* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
  * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */

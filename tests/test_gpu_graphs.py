@@ -44,8 +44,8 @@ PREFILL_CASES = {
     "kda_fg2plus_general_gates": dict(base=gi.KDA_FG2PLUS_PREFILL, B=1, T=200, H=2, seed=121),
     "osdn_write_key_S0": dict(base=gi.OSDN_LONG_PREFILL, B=1, T=257, H=2, seed=122),
     "valu_f32_d64": dict(base=gi.GDN_PREFILL, B=1, T=130, H=2, dk=64, dv=64, io=gi.F32, seed=123),
-    # few heads, 258 chunks: the prep of later chunk blocks forked onto the side stream
-    "osdn_blocked_T16500": dict(base=gi.OSDN_LONG_PREFILL, B=1, T=16500, H=2, seed=127),
+    # few heads, 258 chunks walked in order
+    "osdn_long_T16500": dict(base=gi.OSDN_LONG_PREFILL, B=1, T=16500, H=2, seed=127),
 }
 
 
@@ -75,18 +75,21 @@ def test_checkpointed_prefill_graph_replays_equal_eager():
     _replay_and_compare(torch, graph, res, lambda: g.chunk_fwd_ckpt(*args), "ckpt")
 
 
-# T = 16,500: the chunks are cut into blocks, with the chunk solve and the emission
-# forked onto the library's side stream and joined back through events
-@pytest.mark.parametrize("T", [700, 16500])
-def test_osdn_precond_graph_replays_equal_eager(T):
+# T = 16,500 with an execution context: the chunks are cut into blocks, with the chunk
+# solve and the emission forked onto the context's second stream and joined back
+# through events
+@pytest.mark.parametrize("T,use_ctx", [(700, False), (16500, False), (16500, True)])
+def test_osdn_precond_graph_replays_equal_eager(T, use_ctx):
     torch, g = gpu()
     w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=T, H=3, seed=125)
     x = gi.make_prefill(w)
     k = gi.to_torch(x["k"], w.io)
     beta = gi.to_torch(x["beta_k"], w.gate)
     r = gi.to_torch(gi.make_retention(w), w.gate)
-    graph, res = _capture(torch, lambda: g.osdn_precond(k, beta, 0.05, r=r))
-    _replay_and_compare(torch, graph, res, lambda: g.osdn_precond(k, beta, 0.05, r=r), f"osdn_precond T={T}")
+    ctx = g.Context() if use_ctx else None
+    graph, res = _capture(torch, lambda: g.osdn_precond(k, beta, 0.05, r=r, ctx=ctx))
+    _replay_and_compare(torch, graph, res, lambda: g.osdn_precond(k, beta, 0.05, r=r, ctx=ctx),
+                        f"osdn_precond T={T} context={use_ctx}")
 
 
 def test_mc_readout_graph_replays_equal_eager():

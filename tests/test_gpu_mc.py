@@ -18,10 +18,10 @@ from tests.gpu_util import TOL, gpu, log, to_np, upload
 pytestmark = pytest.mark.gpu
 
 
-def _ckpt_run(w, x, seg, flags=0, generic=False):
+def _ckpt_run(w, x, seg):
     torch, g = gpu()
     d = upload(x, w)
-    kw = dict(k_w=d["k_w"], beta_v=d["beta_v"], S0=d["S0"], chunk=w.chunk, generic=generic, flags=flags)
+    kw = dict(k_w=d["k_w"], beta_v=d["beta_v"], S0=d["S0"], chunk=w.chunk)
     o, ST, ck = g.chunk_fwd_ckpt(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], seg, **kw)
     o2, ST2 = g.chunk_fwd(d["q"], d["k"], d["v"], d["alpha"], d["beta_k"], **kw)
     torch.cuda.synchronize()
@@ -53,21 +53,6 @@ def test_segment_states(name, w, seg):
     per = [oracle.rel_l2(ckg[:, :, s], ck_ref[:, :, s]) for s in range(ck_ref.shape[2])]
     log(f"          rel-L2 per segment state {[f'{e:.2e}' for e in per]}")
     assert max(per) <= TOL[w.io]
-
-
-def test_segment_states_need_supported_kernel():
-    """The four-wave state kernels keep no segment states: the call is refused."""
-    torch, g = gpu()
-    w = gi.GDN_PREFILL.scaled(B=1, T=256, H=2, seed=66)
-    x = gi.make_prefill(w)
-    d = upload(x, w)
-    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None, chunk=64, flags=g.GDR_FLAG_STATE_COLS16)
-    o = torch.empty_like(d["v"])
-    ck = torch.empty((1, 2, 2, 128, 128), dtype=torch.float32, device="cuda")
-    ws = torch.empty(g.gdr_chunk_fwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
-    rc = g.gdr_chunk_fwd_ckpt(desc, d["q"], d["k"], None, d["v"], d["alpha"], d["beta_k"], None, None, o, None,
-                              128, ck, ws, ws.numel())
-    assert rc == g.GDR_EUNSUPPORTED
 
 
 def _readout_gpu(w, x, in_place=False):

@@ -12,7 +12,7 @@ from tests.gpu_util import TOL, gpu, log, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _run(w, eta, *, apf, d0_std=0.0, zero_keys=()):
+def _run(w, eta, *, apf, d0_std=0.0, zero_keys=(), ctx=None, with_plain=False):
     torch, g = gpu()
     x = gi.make_prefill(w)
     k = x["k"].copy()
@@ -23,10 +23,17 @@ def _run(w, eta, *, apf, d0_std=0.0, zero_keys=()):
     d0 = None
     if d0_std > 0:
         d0 = (1.0 + np.random.default_rng(w.seed).normal(0, d0_std, (w.B, w.H, w.dk))).astype(np.float32)
-    kw, dT, qg = g.osdn_precond(gi.to_torch(k, w.io), gi.to_torch(beta, w.gate), eta,
-                                r=None if r is None else gi.to_torch(r, w.gate),
-                                d0=None if d0 is None else gi.to_torch(d0, gi.F32))
+    args = (gi.to_torch(k, w.io), gi.to_torch(beta, w.gate), eta)
+    kwargs = dict(r=None if r is None else gi.to_torch(r, w.gate), d0=None if d0 is None else gi.to_torch(d0, gi.F32))
+    kw, dT, qg = g.osdn_precond(*args, **kwargs, ctx=ctx)
     torch.cuda.synchronize()
+    if with_plain:
+        # the same call without a context (every pass on the caller's stream): bit for bit equal
+        plain = g.osdn_precond(*args, **kwargs)
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip((kw, dT, qg), plain))
+        log(f"[osdn] blocked on the context's second stream equal to the single-stream call: {same}")
+        assert same
     ref = oracle.osdn_precond(gi.as_f64(k, w.io), gi.as_f64(beta, w.gate), eta,
                               r=None if r is None else gi.as_f64(r, w.gate), d0=d0)
     return (to_np(kw), to_np(dT), to_np(qg)), ref
@@ -39,8 +46,9 @@ CASES = [
     ("osdn_apf_strong_eta", BASE.scaled(T=640, seed=93), 4.0, True, 0.0),
     ("f32_io_dk24", BASE.scaled(T=300, dk=24, dv=24, io=gi.F32, seed=94), 1.0, True, 0.2),
     ("bf16_dk8_bf16_gates", BASE.scaled(T=200, dk=8, dv=8, gate=gi.BF16, seed=95), 0.5, True, 0.0),
-    # 256 chunks and more are cut into blocks that the chain walks in order while the
-    # parallel passes of other blocks run beside it (here 4 blocks, the last ragged)
+    # with an execution context, 256 chunks and more are cut into blocks that the chain
+    # walks in order while the parallel passes of other blocks run beside it on the
+    # context's second stream (here 4 blocks, the last ragged)
     ("chunk_blocks_ragged", BASE.scaled(B=1, T=16500, H=2, seed=97), 1.0, True, 0.3),
     ("chunk_blocks_f32_dk24", BASE.scaled(B=2, T=16384, H=1, dk=24, dv=24, io=gi.F32, seed=98), 1.0, False, 0.0),
     ("chunk_blocks_bf16_gates", BASE.scaled(B=1, T=20000, H=1, gate=gi.BF16, seed=99), 0.7, True, 0.2),
@@ -49,7 +57,10 @@ CASES = [
 
 @pytest.mark.parametrize("name,w,eta,apf,d0_std", CASES, ids=[c[0] for c in CASES])
 def test_precond_parity(name, w, eta, apf, d0_std):
-    (kw, dT, qg), (kw_r, dT_r, qg_r) = _run(w, eta, apf=apf, d0_std=d0_std)
+    torch, g = gpu()
+    blocks = name.startswith("chunk_blocks")
+    ctx = g.Context() if blocks else None
+    (kw, dT, qg), (kw_r, dT_r, qg_r) = _run(w, eta, apf=apf, d0_std=d0_std, ctx=ctx, with_plain=blocks)
     ek, ed = oracle.rel_l2(kw, kw_r), oracle.rel_l2(dT, dT_r)
     eq = float(np.max(np.abs(qg - qg_r) / np.abs(qg_r)))
     log(f"[osdn] {name}: rel-L2 kw={ek:.3e} dT={ed:.3e} qgeo max rel={eq:.3e} (qgeo {qg_r.mean():.3f})")

@@ -29,13 +29,17 @@ CASES = [
     ("gdn_T_multiple_of_C", SMALL.scaled(T=128, seed=21)),
     ("bf16_gates", SMALL.scaled(gate=gi.BF16, T=100, seed=22)),
     ("f32_io_d64", SMALL.scaled(io=gi.F32, dk=64, dv=64, T=150, seed=23)),
+    # bf16 shapes the matrix-core kernels do not take run the vector-ALU kernel
+    ("valu_kda_fg2plus_C32", gi.KDA_FG2PLUS_PREFILL.scaled(B=2, T=150, H=2, chunk=32, seed=24)),
+    ("valu_osdn_kw_S0_C32", gi.OSDN_LONG_PREFILL.scaled(B=2, T=130, H=2, chunk=32, seed=25)),
+    ("valu_fg2_shared_d64", gi.KDA_FG2PLUS_PREFILL.scaled(B=1, T=100, H=2, dk=64, dv=64,
+                                                          beta_mode=gi.BETA_SHARED, seed=26)),
 ]
 
 
 @pytest.mark.parametrize("name,w", CASES, ids=[c[0] for c in CASES])
-@pytest.mark.parametrize("generic", [False, True], ids=["auto", "generic"])
-def test_prefill_parity_small(name, w, generic):
-    r = run_prefill(w, gi.make_prefill(w), generic=generic)
+def test_prefill_parity_small(name, w):
+    r = run_prefill(w, gi.make_prefill(w))
     assert r["finite"]
     assert r["o"] <= TOL[w.io], r
     assert r["S"] <= TOL[w.io], r
@@ -57,36 +61,34 @@ def test_full_size_prefill(w):
     assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
 
 
-# With few heads and 256 chunks or more (and the final state requested), the prep of
-# later blocks of chunks runs beside the state recurrence, which is launched once per
-# block and carries the state through ST.  Against the oracle, and bit for bit against
-# the single-launch schedule (taken when no final state is requested).
-BLOCKED = [
+# Long sequences with few heads (hundreds of chunks walked in order): against the
+# oracle, and the read-out bit for bit equal whether or not the final state is asked for.
+LONG = [
     ("gdn_T16500_ragged", gi.GDN_PREFILL.scaled(B=1, T=16500, H=2, seed=41)),
     ("osdn_kw_S0_T16384", gi.OSDN_LONG_PREFILL.scaled(B=2, T=16384, H=1, seed=42)),
     ("gdn_bf16_gates_T16400", gi.GDN_PREFILL.scaled(B=1, T=16400, H=1, gate=gi.BF16, seed=44)),
 ]
 
 
-@pytest.mark.parametrize("name,w", BLOCKED, ids=[c[0] for c in BLOCKED])
-def test_blocked_long_sequence(name, w):
+@pytest.mark.parametrize("name,w", LONG, ids=[c[0] for c in LONG])
+def test_long_sequence(name, w):
     x = gi.make_prefill(w)
     r = run_prefill(w, x)
     assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
     torch, g = gpu()
     d = upload(x, w)
     args = (d["q"], d["k"], d["v"], d["alpha"], d["beta_k"])
-    o_blk, _ = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"])
+    o_st, _ = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"])
     o_one, none = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"], want_state=False)
     torch.cuda.synchronize()
     assert none is None
-    log(f"[prefill blocked] {name}: o equal to the single-launch schedule: {torch.equal(o_blk, o_one)}")
-    assert torch.equal(o_blk, o_one)
+    log(f"[prefill long] {name}: o equal with and without the final state: {torch.equal(o_st, o_one)}")
+    assert torch.equal(o_st, o_one)
 
 
-def test_blocked_in_place_and_checkpoints():
-    """The blocked schedule with S0 and S_T in one buffer (in-place resume), and with
-    segment states kept: both bit for bit against the single-launch schedule."""
+def test_long_in_place_and_checkpoints():
+    """A long sequence with S0 and S_T in one buffer (in-place resume), and with segment
+    states kept: both bit for bit against the plain call."""
     torch, g = gpu()
     w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=16500, H=2, seed=43)
     d = upload(gi.make_prefill(w), w)
@@ -102,7 +104,7 @@ def test_blocked_in_place_and_checkpoints():
     torch.cuda.synchronize()
     assert none is None and ck.shape[2] == 4
     same_ck = torch.equal(o_c, o_ref) and torch.equal(S_c, S_ref) and torch.equal(o_c1, o_ref) and torch.equal(ck, ck1)
-    log(f"[prefill blocked] in place equal {same_io}; checkpoints equal {same_ck}")
+    log(f"[prefill long] in place equal {same_io}; checkpoints equal {same_ck}")
     assert same_io and same_ck
 
 

@@ -24,10 +24,11 @@ def _upload(w, x):
                 M=gi.to_torch(x["M0"], gi.F32))
 
 
-def _run(w, x):
+def _run(w, x, ctx=None):
     torch, g = gpu()
     d = _upload(w, x)
-    o, wsl, rsl = g.sdm_fwd(d["M"], d["ks"], d["qs"], d["v"], d["alpha"], d["beta"], w.W, w.R, want_slots=True)
+    o, wsl, rsl = g.sdm_fwd(d["M"], d["ks"], d["qs"], d["v"], d["alpha"], d["beta"], w.W, w.R, want_slots=True,
+                            ctx=ctx)
     torch.cuda.synchronize()
     return o, d["M"], wsl, rsl
 
@@ -51,7 +52,8 @@ CASES = [
     ("headline_widths_n256", BASE.scaled(B=1, H=2, T=20, n=256, W=128, R=128, seed=97)),
     ("n1024_np16", BASE.scaled(B=1, H=1, T=6, n=1024, W=128, R=100, seed=98)),
     ("widths_over_64", BASE.scaled(B=1, H=2, T=10, n=128, W=65, R=127, seed=99)),
-    # T >= 1024: selection and table pass in eight token blocks on two streams
+    # T >= 1024 with an execution context: selection and table pass in eight token
+    # blocks on two streams
     ("token_blocks_T1100", BASE.scaled(B=2, H=2, T=1100, n=16, W=6, R=5, seed=100)),
 ]
 
@@ -60,7 +62,14 @@ CASES = [
 def test_sdm_parity(name, w):
     x = gi.make_sparse_memory(w)
     log(f"[sdm] {name}: B={w.B} T={w.T} H={w.H} n={w.n} W={w.W} R={w.R} io={w.io} gate={w.gate}")
-    o, M, wsl, rsl = _run(w, x)
+    torch, g = gpu()
+    blocks = name.startswith("token_blocks")
+    o, M, wsl, rsl = _run(w, x, ctx=g.Context() if blocks else None)
+    if blocks:
+        o1, M1, wsl1, rsl1 = _run(w, x)
+        same = torch.equal(o, o1) and torch.equal(M, M1) and torch.equal(wsl, wsl1) and torch.equal(rsl, rsl1)
+        log(f"          two streams equal to one stream: {same}")
+        assert same
     o_ref, M_ref, wsl_ref, rsl_ref = _ref(w, x)
     assert np.array_equal(wsl.cpu().numpy(), wsl_ref), "write slots differ"
     assert np.array_equal(rsl.cpu().numpy(), rsl_ref), "read slots differ"

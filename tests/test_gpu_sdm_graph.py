@@ -1,6 +1,6 @@
-"""Sparse Delta Memory inside a captured HIP graph: a call of T >= 1024 forks its
-selection onto the library's side stream and joins back through events, which a
-capture of the caller's stream takes in.  Each replay (with eager work between the
+"""Sparse Delta Memory inside a captured HIP graph: a call of T >= 1024 given an
+execution context forks its selection onto the context's second stream and joins
+back through events, which a capture of the caller's stream takes in.  Each replay (with eager work between the
 replays) must equal, bit for bit, the same call run eagerly on a copy of the table."""
 import numpy as np
 import pytest
@@ -28,13 +28,14 @@ def test_sdm_graph_replays_equal_eager_calls():
     o_graph = torch.empty_like(v)
     o_eager = torch.empty_like(v)
 
+    ctx = g.Context()
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.stream(side):
         with torch.cuda.graph(graph, stream=side):
             rc = g.gdr_sdm_fwd(desc, w.n, w.W, w.R, ks, qs, v, a, b, M_graph, o_graph, None, None, ws_graph, need,
-                               side)
+                               ctx=ctx, stream=side)
     assert rc == g.GDR_OK
     torch.cuda.synchronize()
     for rep in range(3):

@@ -1,9 +1,9 @@
-"""Calls from several host threads at once.  The entry points that fork work onto
-the library's side stream (long OSDN phase 1, long Sparse Delta Memory, long
-few-head prefill) share one side stream and one set of events per device, with
-the enqueue of a call serialised by a mutex.  Two threads each issue their own
-call on their own stream, at the same time and several times over; every result
-must equal, bit for bit, the same call made alone."""
+"""Calls from several host threads at once.  The library holds no shared state: the
+calls that overlap work on a second stream (long OSDN phase 1, long Sparse Delta
+Memory) take it from a caller-owned execution context, one per thread here, and the
+prefill forks nothing.  Threads each issue their own call on their own stream, at
+the same time and several times over; every result must equal, bit for bit, the
+same call made alone."""
 import threading
 
 import pytest
@@ -55,23 +55,26 @@ def test_concurrent_side_stream_calls_equal_solo_calls():
     v, a, b = gi.to_torch(xs["v"], ws.io), gi.to_torch(xs["alpha"], ws.gate), gi.to_torch(xs["beta"], ws.gate)
     M0 = gi.to_torch(xs["M0"], gi.F32)
 
-    def osdn(stream):
-        return g.osdn_precond(k, beta, 0.5, r=r, stream=stream)
+    def osdn(stream, ctx=None):
+        return g.osdn_precond(k, beta, 0.5, r=r, ctx=ctx, stream=stream)
 
-    def prefill(stream):
+    def prefill(stream, ctx=None):
         return g.chunk_fwd(dp["q"], dp["k"], dp["v"], dp["alpha"], dp["beta_k"], k_w=dp["k_w"], S0=dp["S0"],
                            stream=stream)
 
-    def sdm(stream):
+    def sdm(stream, ctx=None):
         M = M0.clone()  # on the calling thread's stream
-        o = g.sdm_fwd(M, ks, qs, v, a, b, ws.W, ws.R, stream=stream)
+        o = g.sdm_fwd(M, ks, qs, v, a, b, ws.W, ws.R, ctx=ctx, stream=stream)
         return (o, M)
 
     solo = [osdn(None), prefill(None), sdm(None)]
     torch.cuda.synchronize()
     for name, pair in (("osdn + prefill", [osdn, prefill]), ("osdn + osdn", [osdn, osdn]),
                        ("sdm + prefill", [sdm, prefill]), ("all three", [osdn, prefill, sdm])):
-        outs = _run_threads(torch, pair)
+        ctxs = [g.Context() for _ in pair]
+        outs = _run_threads(torch, [lambda st, f=f, c=c: f(st, c) for f, c in zip(pair, ctxs)])
+        for c in ctxs:
+            c.close()
         ref = {osdn: solo[0], prefill: solo[1], sdm: solo[2]}
         same = [all(torch.equal(x, y) for x, y in zip(out, ref[f])) for f, out in zip(pair, outs)]
         log(f"[threads] {name}: equal to the solo calls {same}")
