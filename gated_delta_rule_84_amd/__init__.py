@@ -22,7 +22,8 @@ import torch  # loads the HIP runtime the library binds to
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgdr.so")
 
-GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EWORKSPACE, GDR_EHIP = 0, -1, -2, -3, -4
+GDR_OK, GDR_EINVAL, GDR_EUNSUPPORTED, GDR_EWORKSPACE, GDR_EHIP, GDR_ETOOLARGE = 0, -1, -2, -3, -4, -5
+GDR_NOALLOC_SCRATCH_BYTES = 128 << 20
 GDR_BF16, GDR_F32 = 0, 1
 GDR_ALPHA_SCALAR, GDR_ALPHA_CHANNEL = 0, 1
 GDR_BETA_SCALAR, GDR_BETA_SHARED, GDR_BETA_KV = 0, 1, 2
@@ -48,6 +49,8 @@ _lib.gdr_chunk_fwd_workspace_size.argtypes = [_dp]
 _lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_size_t
 _lib.gdr_chunk_fwd.argtypes = [_dp] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
 _lib.gdr_chunk_fwd.restype = ctypes.c_int
+_lib.gdr_chunk_fwd_noalloc.argtypes = [_dp] + [_vp] * 10 + [_vp]
+_lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
 _lib.gdr_decode_step.argtypes = [_dp] + [_vp] * 9 + [_vp]
 _lib.gdr_decode_step.restype = ctypes.c_int
 _lib.gdr_chunk_fwd_path.argtypes = [_dp]
@@ -80,7 +83,8 @@ _lib.gdr_context_destroy.restype = ctypes.c_int
 EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", "gdr_chunk_fwd_path",
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
             "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond",
-            "gdr_sdm_workspace_size", "gdr_sdm_fwd", "gdr_context_create", "gdr_context_destroy")
+            "gdr_sdm_workspace_size", "gdr_sdm_fwd", "gdr_context_create", "gdr_context_destroy",
+            "gdr_chunk_fwd_noalloc")
 
 
 class GdrError(RuntimeError):
@@ -236,6 +240,12 @@ def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, wo
     return int(_lib.gdr_chunk_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
                                   _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST),
                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def gdr_chunk_fwd_noalloc(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, stream=None) -> int:
+    _check_all(_prefill_specs(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST))
+    return int(_lib.gdr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
+                                          _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST), _stream(stream)))
 
 
 def gdr_chunk_fwd_ckpt(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg_len: int, ckpt,

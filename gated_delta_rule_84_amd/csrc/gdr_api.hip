@@ -3,6 +3,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
 #include <new>
 
 #include "gdr.h"
@@ -66,6 +67,31 @@ bool context_ok(const gdr_context *ctx) {
     return hipGetDevice(&dev) == hipSuccess && dev == ctx->device;
 }
 
+// Scratch of gdr_chunk_fwd_noalloc: one static array per device.  In host code its
+// name is a host-side stand-in, so kernels and copies get the device address looked up
+// once per device (kept in noalloc_ptr, guarded by noalloc_mu).
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex noalloc_mu;
+void *noalloc_ptr[kMaxDevices] = {};
+
+hipError_t noalloc_scratch(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(noalloc_mu);
+    if (!noalloc_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!ptr) return hipErrorInvalidSymbol;
+        noalloc_ptr[dev] = ptr;
+    }
+    *out = noalloc_ptr[dev];
+    return hipSuccess;
+}
+
 int device_lds_limit() {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) != hipSuccess) return -1;
@@ -127,6 +153,8 @@ const char *gdr_status_string(int s) {
     case GDR_EWORKSPACE: return "GDR_EWORKSPACE: workspace missing or smaller than "
                                 "gdr_chunk_fwd_workspace_size()";
     case GDR_EHIP: return "GDR_EHIP: the HIP runtime reported an error";
+    case GDR_ETOOLARGE: return "GDR_ETOOLARGE: the call needs more scratch than the static scratch array of "
+                               "gdr_chunk_fwd_noalloc holds (GDR_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown gdr status";
     }
 }
@@ -231,6 +259,23 @@ int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k
     const int32_t seg = d && d->chunk > 0 ? (0x7fffffff / d->chunk) * d->chunk : 1;
     return gdr_chunk_fwd_ckpt(d, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg, nullptr, workspace,
                               workspace_bytes, stream);
+}
+
+int gdr_chunk_fwd_noalloc(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                          const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                          void *o, float *ST, void *stream) {
+    // everything that needs no device is checked first, the size against the array included
+    const int rc = check_desc(d, true);
+    if (rc) return rc;
+    const size_t need = gdr_chunk_fwd_workspace_size(d);
+    if (need > GDR_NOALLOC_SCRATCH_BYTES) return GDR_ETOOLARGE;
+    void *ws = nullptr;
+    if (need > 0) {
+        const hipError_t e = noalloc_scratch(&ws);
+        if (e != hipSuccess) return GDR_EHIP;
+    }
+    return gdr_chunk_fwd(d, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, ws, need > 0 ? GDR_NOALLOC_SCRATCH_BYTES : 0,
+                         stream);
 }
 
 size_t gdr_mc_readout_workspace_size(const gdr_desc *d, int32_t n_ckpt) {

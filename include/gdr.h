@@ -31,7 +31,9 @@
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller.  The library
  *     allocates no device memory, keeps no pointer after a call returns and has no
- *     global mutable state, so calls from several host threads are safe.  The two
+ *     global mutable state beyond the per-device address of gdr_chunk_fwd_noalloc's
+ *     static scratch array (looked up once, under a lock), so calls from several
+ *     host threads are safe (gdr_chunk_fwd_noalloc: see its own rule).  The two
  *     calls that can overlap independent work on a second stream (gdr_osdn_precond,
  *     gdr_sdm_fwd) take it from a caller-owned gdr_context (below); with a NULL
  *     context they run everything on `stream`.
@@ -61,7 +63,9 @@ typedef enum gdr_status {
                               aliasing output, beta layout inconsistent with beta_mode */
     GDR_EUNSUPPORTED = -2, /* shape outside what the kernels implement (see below) */
     GDR_EWORKSPACE = -3,   /* workspace missing or smaller than gdr_chunk_fwd_workspace_size */
-    GDR_EHIP = -4          /* the HIP runtime reported an error at launch */
+    GDR_EHIP = -4,         /* the HIP runtime reported an error at launch */
+    GDR_ETOOLARGE = -5     /* gdr_chunk_fwd_noalloc: the call needs more scratch than the
+                              library's static scratch array holds */
 } gdr_status;
 
 /* Element types. */
@@ -155,6 +159,30 @@ int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void
                   const void *v, const void *alpha, const void *beta_k, const void *beta_v,
                   const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * Prefill with no workspace argument and no allocation, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid hipMalloc.  Same arguments, results and kernels as
+ * gdr_chunk_fwd, except that the scratch gdr_chunk_fwd takes as `workspace` is a
+ * static device array inside the library, GDR_NOALLOC_SCRATCH_BYTES (128 MiB) per
+ * device, held by every device the library runs on until the process ends.
+ *
+ *   - A call whose gdr_chunk_fwd_workspace_size(desc) exceeds the array returns
+ *     GDR_ETOOLARGE before anything is enqueued (the scalar-gate matrix-core path
+ *     takes up to 5,216 chunks of 64 tokens over all (b, h), e.g. B=4, H=16, T=4096;
+ *     the general-gate path up to 1,087).
+ *   - The first call on a device looks the array's address up (a runtime symbol
+ *     query, no allocation) and keeps it for that device.
+ *   - Every call on one device shares that device's array and nothing in it needs
+ *     clearing (each call writes what it reads).  Calls that may overlap on one device
+ *     (concurrent streams, or host threads issuing at the same time) race on it and
+ *     must be serialised by the caller.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int gdr_chunk_fwd_noalloc(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
+                          const void *v, const void *alpha, const void *beta_k, const void *beta_v,
+                          const float *S0, void *o, float *ST, void *stream);
 
 /*
  * Decode: one token for every (b, h), applied in place to a resident state

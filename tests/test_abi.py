@@ -354,3 +354,18 @@ def test_context_create_and_destroy_arguments(g):
     """gdr_context_create refuses a NULL out-pointer; destroying NULL is a no-op."""
     assert g._lib.gdr_context_create(None) == g.GDR_EINVAL
     assert g.gdr_context_destroy(None) == g.GDR_OK
+
+
+def test_noalloc_rejects_calls_beyond_its_scratch(g):
+    """gdr_chunk_fwd_noalloc refuses, before touching any device, a call whose record
+    would not fit its static scratch (GDR_ETOOLARGE); a descriptor error comes first."""
+    q, k, v, a, b, o, st = _ptrs(n=7, step=0x40000000)
+    big = _desc(g, B=4, H=16, T=8192)            # 8,192 chunks x 25,728 B > 128 MiB
+    assert g.gdr_chunk_fwd_workspace_size(big) > g.GDR_NOALLOC_SCRATCH_BYTES
+    assert g.gdr_chunk_fwd_noalloc(big, q, k, None, v, a, b, None, None, o, st, 0) == g.GDR_ETOOLARGE
+    chan = _desc(g, B=1, H=1, T=64 * 1088, alpha_mode=g.GDR_ALPHA_CHANNEL)
+    assert g.gdr_chunk_fwd_noalloc(chan, q, k, None, v, a, b, None, None, o, st, 0) == g.GDR_ETOOLARGE
+    assert g.gdr_chunk_fwd_noalloc(_desc(g, dk=12), q, k, None, v, a, b, None, None, o, st, 0) == g.GDR_EUNSUPPORTED
+    fits = _desc(g, B=4, H=16, T=4096)           # the headline batch: 105 MB of records
+    assert g.gdr_chunk_fwd_workspace_size(fits) <= g.GDR_NOALLOC_SCRATCH_BYTES
+    assert "scratch" in g.gdr_status_string(g.GDR_ETOOLARGE)
