@@ -923,7 +923,12 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     pl[f] = cat(ld8(&sm.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Pl[t][8 * (p2 ^ sw) + hf]));
                 }
             }
-            lds_barrier();  // B1: D published; V and the P terms of this chunk consumed
+            // B1: D published; V and the P terms of this chunk consumed.  The side wave's
+            // own LDS reads are complete (lgkmcnt) and the asm is a compiler memory barrier,
+            // but unlike lds_barrier() there is no release fence: that would also wait for
+            // the next chunk's copies issued above (they write LDS), holding every wave at
+            // B1 until they land; they only need to have landed by B2.
+            asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
             if (c + 1 < p.c1) issue_late(c + 1);
 
             // O += P D, then stored per lane (4 tokens of one value column per tile)
