@@ -24,6 +24,8 @@ Layouts (row-major):
            S: [B, H, dk, dv] fp32
   sparse memory  ks, qs: [B, T, H, 2, n] fp32 half scores, v: [B, T, H, dv],
            alpha, beta: [B, T, H], M0: [B, H, n * n, dv] fp32
+  delta-mem pass  q, k, v: [B, T, H, r], lam, beta: [B, T, H], seg_end: [B, T] uint8
+           or None, M0: [B, H, r, r] fp32 (row a predicts value component a)
   cache read-out  q: [B, T, H, dk] bf16, ckpt: [B, H, N, dk, dv] fp32,
            gates: [B, T, H, N] fp32 or None, o_in: [B, T, H, dv] bf16 or None
 """
@@ -225,6 +227,30 @@ class SparseMemory:
         return dataclasses.replace(self, **kw)
 
 
+@dataclasses.dataclass(frozen=True)
+class DmemSeq:
+    """A delta-mem context pass: per (b, h) an r x r memory written over T tokens, one
+    write per token (TSW) or per segment (SSW, segments of a length mix), with J
+    sub-states per group of heads whose reads are aggregated (MSW; H = G J)."""
+
+    name: str
+    B: int
+    T: int
+    H: int
+    J: int
+    r: int
+    seg_mean: float = 0.0       # mean segment length (lengths 1 + geometric); 0: every token is one (TSW)
+    io: str = BF16              # q, k, v, out
+    gate: str = BF16            # lambda, beta
+    lam_mu: float = -4.0        # lambda = sigmoid(-N(mu, sd)), as the decode workloads
+    lam_sd: float = 1.0
+    m_std: float = 0.02         # M0 ~ N(0, m_std) fp32
+    seed: int = 0
+
+    def scaled(self, **kw) -> "DmemSeq":
+        return dataclasses.replace(self, **kw)
+
+
 # Sparse Delta Memory at the headline batch's shape: 65,536 slots of 128 values per
 # (b, h) (2 GiB of tables), W = R = 128 (the dense query width)
 SDM_B4H16 = SparseMemory("sdm_bf16_B4H16T4096N65536dv128W128R128", B=4, T=4096, H=16, n=256, dv=128, W=128,
@@ -233,6 +259,11 @@ SDM_B4H16 = SparseMemory("sdm_bf16_B4H16T4096N65536dv128W128R128", B=4, T=4096, 
 # read-out of the long-context batch's segment caches: 16 segments of 4096 tokens
 MC_LONG_GRM = CacheReadout("mc_grm_bf16_B1H32T65536d128seg4096", B=1, T=65536, H=32, dk=128, dv=128,
                            seg=4096, gate_kind="dense", seed=8407)
+
+# delta-mem context passes at the small-state decode batch's shape (8192 memories of 8 x 8):
+# segment writes over messages of ~16 tokens, and four sub-states per group of heads
+DMEM_SSW = DmemSeq("deltamem_ssw_bf16_B8192T256H1r8", B=8192, T=256, H=1, J=1, r=8, seg_mean=16.0, seed=8409)
+DMEM_MSW = DmemSeq("deltamem_msw_bf16_B2048T256H4J4r8", B=2048, T=256, H=4, J=4, r=8, seed=8410)
 
 PREFILL_WORKLOADS = [TINY_GDN_F32, GDN_PREFILL, KDA_FG2PLUS_PREFILL, OSDN_LONG_PREFILL]
 DECODE_WORKLOADS = [DECODE_B512, DECODE_DMEM_R8]
@@ -324,6 +355,42 @@ def make_cache_readout(w: CacheReadout) -> dict:
         raise ValueError(w.gate_kind)
     o_in = store(rng.standard_normal((B, T, H, dv)), BF16) if w.with_o_in else None
     return dict(q=q, ckpt=ckpt, gates=gates, o_in=o_in)
+
+
+def make_dmem_seq(w: DmemSeq) -> dict:
+    """Draw a delta-mem context pass.  Draw order: q, k, v, lambda, beta, segment
+    lengths, M0.  seg_end [B, T] uint8 marks each segment's last token (None for TSW);
+    every row's last token closes its last segment."""
+    rng = np.random.default_rng(w.seed)
+    B, T, H, r = w.B, w.T, w.H, w.r
+    q = store(_l2_normalise(rng.standard_normal((B, T, H, r))), w.io)
+    k = store(_l2_normalise(rng.standard_normal((B, T, H, r))), w.io)
+    v = store(rng.standard_normal((B, T, H, r)), w.io)
+    lam = store(_sigmoid(-rng.normal(w.lam_mu, w.lam_sd, (B, T, H))), w.gate)
+    beta = store(_sigmoid(rng.standard_normal((B, T, H))), w.gate)
+    seg_end = None
+    if w.seg_mean > 0.0:
+        # lengths 1 + Geometric(1 / seg_mean) (mean seg_mean), enough of them to cover T
+        n = int(2 * T / w.seg_mean) + 16
+        lens = rng.geometric(1.0 / w.seg_mean, (B, n))
+        ends = np.cumsum(lens, axis=1) - 1
+        seg_end = np.zeros((B, T), dtype=np.uint8)
+        rows = np.repeat(np.arange(B), n)
+        e = ends.reshape(-1)
+        keep = e < T
+        seg_end[rows[keep], e[keep]] = 1
+        seg_end[:, T - 1] = 1
+    M0 = rng.normal(0.0, w.m_std, (B, H, r, r)).astype(np.float32)
+    return dict(q=q, k=k, v=v, lam=lam, beta=beta, seg_end=seg_end, M0=M0)
+
+
+def dmem_seq_f64(w: DmemSeq, x: dict) -> dict:
+    out = {key: as_f64(x[key], w.io) for key in ("q", "k", "v")}
+    out["lam"] = as_f64(x["lam"], w.gate)
+    out["beta"] = as_f64(x["beta"], w.gate)
+    out["M0"] = as_f64(x["M0"], F32)
+    out["seg_end"] = x["seg_end"]
+    return out
 
 
 def make_retention(w: Prefill, mu: float = 4.0, sd: float = 1.0) -> np.ndarray:

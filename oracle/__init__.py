@@ -15,6 +15,9 @@ Contents:
     (write keys, final preconditioner, geometric-mean loss ratio q_geo).
   * ``sdm``: Sparse Delta Memory -- product-key slot selection (all slot scores
     ranked directly), per-slot gated delta writes and the weighted sparse read.
+  * ``dmem``: delta-mem write granularities -- one write per token (TSW) or per
+    segment with the segment's mean key and value (SSW), and J sub-states per group
+    of heads with summed reads (MSW), reads taken before the write, plain fp64.
   * ``memcache``: Memory Caching -- the state after every segment (the sequential
     run, one segment at a time) and the residual / gated read-out over those
     cached states, plain fp64.
