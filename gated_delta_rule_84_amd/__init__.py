@@ -75,6 +75,8 @@ _lib.gdr_sdm_workspace_size.argtypes = [_dp, ctypes.c_int32, ctypes.c_int32, cty
 _lib.gdr_sdm_workspace_size.restype = ctypes.c_size_t
 _lib.gdr_sdm_fwd.argtypes = [_dp] + [ctypes.c_int32] * 3 + [_vp] * 10 + [ctypes.c_size_t, _vp, _vp]
 _lib.gdr_sdm_fwd.restype = ctypes.c_int
+_lib.gdr_dmem_fwd.argtypes = [_dp, ctypes.c_int32] + [_vp] * 8 + [_vp]
+_lib.gdr_dmem_fwd.restype = ctypes.c_int
 _lib.gdr_context_create.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
 _lib.gdr_context_create.restype = ctypes.c_int
 _lib.gdr_context_destroy.argtypes = [_vp]
@@ -84,7 +86,7 @@ EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", 
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
             "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond",
             "gdr_sdm_workspace_size", "gdr_sdm_fwd", "gdr_context_create", "gdr_context_destroy",
-            "gdr_chunk_fwd_noalloc")
+            "gdr_chunk_fwd_noalloc", "gdr_dmem_fwd")
 
 
 class GdrError(RuntimeError):
@@ -317,6 +319,18 @@ def gdr_sdm_fwd(desc: Desc, n: int, W: int, R: int, ks, qs, v, alpha, beta, M, o
                                 int(workspace_bytes), _ctx(ctx), _stream(stream)))
 
 
+def gdr_dmem_fwd(desc: Desc, J: int, q, k, v, lam, beta, seg_end, M, out, stream=None) -> int:
+    io, gt = _io(desc)
+    if io is not None and min(desc.B, desc.T, desc.H, desc.dk) >= 0 and int(J) >= 1 and desc.H % int(J) == 0:
+        nt = desc.B * desc.T * desc.H
+        _check_all([("q", q, nt * desc.dk, io), ("k", k, nt * desc.dk, io), ("v", v, nt * desc.dk, io),
+                    ("lam", lam, nt, gt), ("beta", beta, nt, gt), ("seg_end", seg_end, desc.B * desc.T, torch.uint8),
+                    ("M", M, desc.B * desc.H * desc.dk * desc.dk, torch.float32),
+                    ("out", out, nt // int(J) * desc.dk, io)])
+    return int(_lib.gdr_dmem_fwd(ctypes.byref(desc), int(J), _ptr(q), _ptr(k), _ptr(v), _ptr(lam), _ptr(beta),
+                                 _ptr(seg_end), _ptr(M), _ptr(out), _stream(stream)))
+
+
 def gdr_decode_step(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S, o, stream=None) -> int:
     io, gt = _io(desc)
     if io is not None and min(desc.B, desc.H, desc.dk, desc.dv) >= 0:
@@ -453,6 +467,20 @@ def sdm_fwd(M, ks, qs, v, alpha, beta, W, R, *, want_slots=False, workspace=None
     if rc != GDR_OK:
         raise GdrError(rc, "gdr_sdm_fwd")
     return (o, ws_[0], ws_[1]) if want_slots else o
+
+
+def dmem_fwd(M, q, k, v, lam, beta, *, seg_end=None, J=1, out=None, stream=None):
+    """delta-mem context pass: M [B, H, r, r] fp32 is updated in place; q, k, v
+    [B, T, H, r]; lam, beta [B, T, H]; seg_end [B, T] uint8 or None (one write per
+    token).  Returns the reads [B, T, H // J, r] (J sub-states per group, reads summed)."""
+    B, T, H, r = q.shape
+    desc = Desc(B=B, T=T, H=H, dk=r, dv=r, chunk=64, io_dtype=_dtype_code(q), gate_dtype=_dtype_code(lam),
+                alpha_mode=0, beta_mode=0, flags=0)
+    o = out if out is not None else torch.empty((B, T, H // J, r), dtype=q.dtype, device=q.device)
+    rc = gdr_dmem_fwd(desc, J, q, k, v, lam, beta, seg_end, M, o, stream)
+    if rc != GDR_OK:
+        raise GdrError(rc, "gdr_dmem_fwd")
+    return o
 
 
 def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, out=None, flags=0, stream=None):

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libgdr.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["gdr_api.hip", "decode.hip", "chunk_valu.hip", "chunk_mfma.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip"]
+SOURCES = ["gdr_api.hip", "decode.hip", "chunk_valu.hip", "chunk_mfma.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip", "dmem.hip"]
 ARCH = "gfx950"
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -415,6 +415,52 @@ int gdr_sdm_fwd(const gdr_desc *d, int32_t n, int32_t W, int32_t R, const float 
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
 }
 
+int gdr_dmem_fwd(const gdr_desc *d, int32_t J, const void *q, const void *k, const void *v, const void *lam,
+                 const void *beta, const uint8_t *seg_end, float *M, void *out, void *stream) {
+    if (!d || d->B < 0 || d->T < 0 || d->H < 0 || d->dk < 1 || d->dk != d->dv) return GDR_EINVAL;
+    if (d->io_dtype != GDR_BF16 && d->io_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->gate_dtype != GDR_BF16 && d->gate_dtype != GDR_F32) return GDR_EINVAL;
+    if (d->alpha_mode != GDR_ALPHA_SCALAR || d->beta_mode != GDR_BETA_SCALAR || d->flags != 0) return GDR_EINVAL;
+    if (J < 1) return GDR_EINVAL;
+    const int r = d->dk;
+    if ((r != 8 && r != 16) || (J != 1 && J != 2 && J != 4 && J != 8) || J > 64 / r) return GDR_EUNSUPPORTED;
+    if (d->H % J) return GDR_EINVAL;
+    const long long nbh = (long long)d->B * d->H, ntok = nbh * d->T;
+    if (nbh > 0x7fffffffLL || ntok * r > 0x7fffffffffffLL) return GDR_EUNSUPPORTED;
+    if (ntok == 0) return GDR_OK;
+    if (!q || !k || !v || !lam || !beta || !M || !out) return GDR_EINVAL;
+    const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;
+    if (!aligned16(q) || !aligned16(k) || !aligned_to(v, es) || !aligned_to(out, es) || !aligned_to(M, 4))
+        return GDR_EINVAL;
+    if (!aligned_to(lam, gs) || !aligned_to(beta, gs)) return GDR_EINVAL;
+    {
+        const size_t nrow = (size_t)ntok * r * es, ng = (size_t)ntok * gs;
+        const void *ins[] = {q, k, v, lam, beta, seg_end};
+        const size_t il[] = {nrow, nrow, nrow, ng, ng, (size_t)d->B * d->T};
+        const size_t nm = (size_t)nbh * r * r * sizeof(float), no = (size_t)ntok / J * r * es;
+        for (int i = 0; i < 6; ++i)
+            if (overlaps(M, nm, ins[i], il[i]) || overlaps(out, no, ins[i], il[i])) return GDR_EINVAL;
+        if (overlaps(M, nm, out, no)) return GDR_EINVAL;
+    }
+    DmemParams p{};
+    p.B = d->B;
+    p.T = d->T;
+    p.H = d->H;
+    p.R = r;
+    p.J = J;
+    p.io_bf16 = d->io_dtype == GDR_BF16;
+    p.gate_bf16 = d->gate_dtype == GDR_BF16;
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.lam = lam;
+    p.beta = beta;
+    p.seg = seg_end;
+    p.M = M;
+    p.out = out;
+    return launch_dmem(p, static_cast<hipStream_t>(stream)) == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
 int gdr_decode_step(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
                     const void *alpha, const void *beta_k, const void *beta_v, float *S, void *o,
                     void *stream) {

@@ -53,8 +53,19 @@ struct DecodeParams {
     void *o;
 };
 
+// Parameters of one delta-mem context pass (R x R memories, J sub-states per group).
+struct DmemParams {
+    int B, T, H, R, J;
+    int io_bf16, gate_bf16;
+    const void *q, *k, *v, *lam, *beta;
+    const uint8_t *seg;  // NULL: every token closes its segment
+    float *M;
+    void *out;
+};
+
 // Launchers (defined next to their kernels).  They only enqueue work.
 hipError_t launch_decode(const DecodeParams &p, hipStream_t s);
+hipError_t launch_dmem(const DmemParams &p, hipStream_t s);
 hipError_t launch_chunk_valu(const ChunkParams &p, hipStream_t s);
 size_t chunk_mfma_workspace(const ChunkParams &p);
 bool chunk_mfma_supported(const ChunkParams &p);

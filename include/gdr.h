@@ -309,6 +309,38 @@ int gdr_sdm_fwd(const gdr_desc *desc, int32_t n, int32_t W, int32_t R, const flo
                 const void *v, const void *alpha, const void *beta, float *M, void *o, int32_t *w_slots,
                 int32_t *r_slots, void *workspace, size_t workspace_bytes, gdr_context *ctx, void *stream);
 
+/*
+ * delta-mem context pass [delta-mem: Efficient Online Memory for Large Language
+ * Models, section 2.A (update rule), 2.C (read before the write), 2.D (write
+ * granularities)].  Per (b, h) an r x r fp32 memory M, row a predicting value
+ * component a as M k.  Tokens are grouped into segments; every token t of a segment
+ * reads the memory as it was before the segment's write, and the segment is then
+ * written once:
+ *     read   r_t = M q_t
+ *     write  M <- lam M + beta (vbar - M kbar) kbar^T
+ * with kbar, vbar the means of the segment's keys and values and lam, beta the gates
+ * stored at the segment's last token (the gates of its other tokens are not read).
+ *   - token-state write (TSW): seg_end NULL, every token is its own segment (the
+ *     page's per-token step with the read before the write);
+ *   - sequence-state write (SSW): seg_end[b, t] != 0 marks the last token of a
+ *     segment (a message); the last token of the sequence always closes one;
+ *   - multi-state write (MSW): J sub-states per group of heads, heads h = g J + j
+ *     (j < J) of one group each written as above from their own q, k, v and gates;
+ *     the group's read is the sum of its J sub-state reads.
+ *
+ *   q, k, v   [B, T, H, r] io_dtype (16-byte aligned)
+ *   lam, beta [B, T, H] gate_dtype
+ *   seg_end   [B, T] uint8 or NULL
+ *   M         [B, H, r, r] fp32, the memory before the pass on entry, after it on return
+ *   out       [B, T, H / J, r] io_dtype (bf16 rounded to nearest even)
+ * desc: B, T, H >= 0; dk == dv == r; alpha_mode, beta_mode scalar; flags 0; chunk
+ * not used.  Supported: r = 8 (J = 1, 2, 4, 8) or r = 16 (J = 1, 2, 4), H a multiple
+ * of J (else GDR_EUNSUPPORTED / GDR_EINVAL).  Outputs must not overlap the inputs.
+ * Runs on `stream`; returns once the work is enqueued.
+ */
+int gdr_dmem_fwd(const gdr_desc *desc, int32_t J, const void *q, const void *k, const void *v, const void *lam,
+                 const void *beta, const uint8_t *seg_end, float *M, void *out, void *stream);
+
 /* Which prefill kernel `desc` selects: 1 = bf16 matrix-core kernel,
  * 2 = fp32 vector-ALU kernel, or a negative gdr_status if desc is rejected. */
 int gdr_chunk_fwd_path(const gdr_desc *desc);

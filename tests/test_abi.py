@@ -325,6 +325,27 @@ def test_binding_rejects_oversized_workspace_claim(g):
         g.gdr_chunk_fwd(d, None, None, None, None, None, None, None, None, None, None, ws, 65, 0)
 
 
+def test_dmem_validation(g):
+    d = _desc(g, T=40, H=4, dk=8, dv=8)
+    q, k, v, lam, beta, seg, M, out = _ptrs(n=8, step=0x10000000)
+    call = lambda desc, J=1, **kw_: g.gdr_dmem_fwd(
+        desc, J, kw_.get("q", q), k, v, lam, beta, kw_.get("seg", seg), kw_.get("M", M), kw_.get("out", out), 0)
+    assert call(_desc(g, T=40, H=4, dk=4, dv=4)) == g.GDR_EUNSUPPORTED   # r = 8 or 16
+    assert call(_desc(g, T=40, H=4, dk=16, dv=16), J=8) == g.GDR_EUNSUPPORTED  # 16-wide: at most 4 sub-states
+    assert call(d, J=3) == g.GDR_EUNSUPPORTED
+    assert call(_desc(g, T=40, H=6, dk=8, dv=8), J=4) == g.GDR_EINVAL   # H a multiple of J
+    assert call(_desc(g, T=40, H=4, dk=8, dv=16)) == g.GDR_EINVAL       # square memory
+    assert call(d, J=0) == g.GDR_EINVAL
+    assert call(_desc(g, T=40, H=4, dk=8, dv=8, alpha_mode=1)) == g.GDR_EINVAL
+    assert call(_desc(g, T=40, H=4, dk=8, dv=8, flags=0x10)) == g.GDR_EINVAL
+    assert call(d, q=None) == g.GDR_EINVAL
+    assert call(d, q=FakePtr(q.addr + 8)) == g.GDR_EINVAL               # rows are read 16 bytes at a time
+    assert call(d, out=FakePtr(k.addr + 64)) == g.GDR_EINVAL            # output overlaps k
+    assert call(d, M=FakePtr(out.addr)) == g.GDR_EINVAL                 # memory overlaps the output
+    assert call(_desc(g, T=0, H=4, dk=8, dv=8)) == g.GDR_OK             # nothing to do
+    assert call(_desc(g, B=0, H=4, dk=8, dv=8), q=None) == g.GDR_OK
+
+
 def test_binding_checks_the_other_entry_points(g):
     import torch
 
@@ -342,6 +363,15 @@ def test_binding_checks_the_other_entry_points(g):
     with pytest.raises(ValueError, match="gates"):      # gates for another number of caches
         g.gdr_mc_readout(dm, torch.zeros(1, 4, 2, 128, dtype=bf), torch.zeros(1, 2, 3, 128, 128), 3, 64,
                          torch.zeros(1, 4, 2, 2), None, torch.zeros(1, 4, 2, 128, dtype=bf), None, 0, 0)
+    dd = _desc(g, B=1, T=4, H=4, dk=8, dv=8, gate_dtype=g.GDR_BF16)
+    with pytest.raises(ValueError, match="out"):        # reads of every head where groups of 2 were asked for
+        g.gdr_dmem_fwd(dd, 2, torch.zeros(1, 4, 4, 8, dtype=bf), torch.zeros(1, 4, 4, 8, dtype=bf),
+                       torch.zeros(1, 4, 4, 8, dtype=bf), torch.zeros(1, 4, 4, dtype=bf), torch.zeros(1, 4, 4, dtype=bf),
+                       None, torch.zeros(1, 4, 8, 8), torch.zeros(1, 4, 4, 8, dtype=bf))
+    with pytest.raises(ValueError, match="seg_end"):    # segment marks as booleans
+        g.gdr_dmem_fwd(dd, 1, torch.zeros(1, 4, 4, 8, dtype=bf), torch.zeros(1, 4, 4, 8, dtype=bf),
+                       torch.zeros(1, 4, 4, 8, dtype=bf), torch.zeros(1, 4, 4, dtype=bf), torch.zeros(1, 4, 4, dtype=bf),
+                       torch.zeros(1, 4, dtype=torch.bool), torch.zeros(1, 4, 8, 8), torch.zeros(1, 4, 4, 8, dtype=bf))
     ds = _desc(g, B=1, T=4, H=2, dk=128, dv=128)
     with pytest.raises(ValueError, match="w_slots"):    # slot list of the wrong integer type
         g.gdr_sdm_fwd(ds, 4, 2, 2, torch.zeros(1, 4, 2, 2, 4), torch.zeros(1, 4, 2, 2, 4),
