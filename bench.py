@@ -3,14 +3,17 @@
 
 One step = one gdr_chunk_fwd over the batch B=4, H=16, T=4096, dk=dv=128,
 chunk 64 (bf16 q/k/v, fp32 scalar gates, zero initial state, o and the final
-state written), inputs resident in HBM.  The decode step (B=512, H=16,
-d=128, 256 steps replayed as one HIP graph, and the r=8 small-state case) is
-timed in the same run and reported under "decode", and the Memory-Caching
-read-out of the long-context batch's 16 segment states (B=1, H=32, T=65536,
-gated) under "mc_readout", and the OSDN phase-1 preconditioner scan of the
-long-context batch's keys (with retention gates) under "osdn_precond".
+state written), inputs resident in HBM.  The same run times every other
+configuration the library is specified on, each with its own roofline, under
+"configs": the tiny fp32 GDN batch, the KDA / FG2-GDN+ batch (channel decay,
+key and value beta vectors), the long-context OSDN batch (B=1, H=32, T=65536,
+write key, nonzero S0), and the decode step (B=512, H=16, d=128, 256 steps
+replayed as one HIP graph, and the r=8 delta-mem case).  Also reported: the
+delta-mem context pass (segment and multi-state writes), the Memory-Caching
+read-out, OSDN phase 1 and Sparse Delta Memory.
 
-Prints ONE JSON line.  `value` is prefill tokens/s (B*T per step).
+Prints ONE JSON line.  `value` is prefill tokens/s (B*T per step) of the headline
+batch.
 """
 from __future__ import annotations
 
@@ -27,8 +30,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFLOPS = 2516.6  # MI355X dense bf16 matrix peak
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip", "sdm.hip", "gdr_ut.hpp",
-                  "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
+KERNEL_SOURCES = ["gdr_api.hip", "chunk_mfma.hip", "chunk_valu.hip", "decode.hip", "mc_readout.hip", "osdn_precond.hip",
+                  "sdm.hip", "dmem.hip", "gdr_ut.hpp", "gdr_device.hpp", "gdr_internal.hpp", "gdr_mfma.hpp"]
 
 
 def prefill_flops_per_token_head(C, dk, dv):
@@ -222,7 +225,7 @@ def bench_mc_readout(g, gi, stream, reps, digest=None):
                          "frac": tf / BF16_MFMA_PEAK_TFLOPS, "traffic": load_traffic(w.name, digest)}}
 
 
-def bench_osdn_precond(g, gi, stream, reps, digest=None):
+def bench_osdn_precond(g, gi, stream, reps, digest=None, x=None):
     """OSDN phase 1 over the long-context batch's keys (B=1, H=32, T=65536, retention
     gates), inputs resident; events on the launch stream around each call (chunk
     solve + scan).  Algorithmic bytes: k read and k_w written (bf16), beta and r
@@ -230,7 +233,8 @@ def bench_osdn_precond(g, gi, stream, reps, digest=None):
     import torch
 
     w = gi.OSDN_LONG_PREFILL
-    x = gi.make_prefill(w)
+    if x is None:
+        x = gi.make_prefill(w)
     k = gi.to_torch(x["k"], w.io)
     beta = gi.to_torch(x["beta_k"], w.gate)
     r = gi.to_torch(gi.make_retention(w), w.gate)
@@ -323,6 +327,137 @@ def bench_sdm(g, gi, stream, reps, digest=None):
                          "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(w.name, digest)}}
 
 
+def progress(msg):
+    """A progress line on stderr (stdout carries only the JSON line)."""
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def time_prefill(g, gi, w, x, steps, warmup, stream, digest, cold=False):
+    """`steps` gdr_chunk_fwd calls back to back between one pair of HIP events on the
+    launch stream after `warmup` untimed calls (an event pair around every call would
+    add its own few microseconds per call); with `cold`, also the median of 5 calls
+    after flushing L2 and the Infinity Cache.  Returns times and the roofline."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
+         for k in x}
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk)
+    path = g.gdr_chunk_fwd_path(desc)
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device=dev)
+    ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    wsz = g.gdr_chunk_fwd_workspace_size(desc)
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        rc = g.gdr_chunk_fwd(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"], d["beta_v"],
+                             d["S0"], o, ST, ws, wsz, stream)
+        if rc != g.GDR_OK:
+            raise g.GdrError(rc, "gdr_chunk_fwd")
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_event = e0.elapsed_time(e1) / steps
+    res = {}
+    if cold:
+        flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
+        times = []
+        for _ in range(5):
+            flush.fill_(1.0)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            step()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        del flush
+        res["ms_cold_median"] = sorted(times)[len(times) // 2]
+    del d, o, ST, ws
+    tokens = w.B * w.T
+    flops = prefill_flops_per_token_head(w.chunk, w.dk, w.dv) * tokens * w.H
+    nbytes = prefill_bytes(w)
+    gbs = nbytes / (ms_event * 1e-3) / 1e9
+    res.update({
+        "ms_per_call": ms_event, "ms_wall": wall * 1e3 / steps, "tokens_per_s": tokens / (ms_event * 1e-3),
+        "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
+        "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": gbs / HBM_PEAK_GBS,
+                     "traffic": load_traffic(w.name, digest)},
+        "mfma_frac": flops / (ms_event * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
+                   "io": w.io,
+                   "gates": (w.gate + " " + ("channel" if w.alpha_mode else "scalar") + " alpha, "
+                             + ["scalar", "shared-vector", "key/value-vector"][w.beta_mode] + " beta"
+                             + (", write key" if w.write_key else "")),
+                   "S0": "nonzero" if w.s0_std > 0 else "zero",
+                   "kernel_path": {1: "bf16-mfma", 2: "fp32-valu"}[path]},
+    })
+    return res
+
+
+def dmem_bytes(w):
+    """Algorithmic HBM bytes of one delta-mem context pass: q, k, v and the two gates
+    read per (token, head), the segment marks per token, the memories read and
+    written, the group reads written."""
+    es = 2 if w.io == "bf16" else 4
+    gs = 2 if w.gate == "bf16" else 4
+    ntok = w.B * w.T * w.H
+    n = ntok * (3 * w.r * es + 2 * gs) + (w.B * w.T if w.seg_mean > 0 else 0)
+    n += 2 * w.B * w.H * w.r * w.r * 4 + ntok // w.J * w.r * es
+    return n
+
+
+def bench_dmem(g, gi, stream, reps, digest=None):
+    """The delta-mem context passes (8192 memories of 8 x 8, 256 tokens): segment writes
+    (SSW) and four sub-states per group (MSW), inputs resident; events on the launch
+    stream around each call (the memories evolve from call to call, the work does not)."""
+    import numpy as np
+    import torch
+
+    res = {}
+    for w in (gi.DMEM_SSW, gi.DMEM_MSW):
+        x = gi.make_dmem_seq(w)
+        q, k, v = (gi.to_torch(x[n], w.io) for n in ("q", "k", "v"))
+        lam, beta = gi.to_torch(x["lam"], w.gate), gi.to_torch(x["beta"], w.gate)
+        se = torch.from_numpy(np.ascontiguousarray(x["seg_end"])).cuda() if x["seg_end"] is not None else None
+        M = gi.to_torch(x["M0"], gi.F32)
+        o = torch.empty((w.B, w.T, w.H // w.J, w.r), dtype=q.dtype, device=q.device)
+        desc = g.Desc(B=w.B, T=w.T, H=w.H, dk=w.r, dv=w.r, chunk=64, io_dtype=g._dtype_code(q),
+                      gate_dtype=g._dtype_code(lam), alpha_mode=0, beta_mode=0, flags=0)
+
+        def call():
+            rc = g.gdr_dmem_fwd(desc, w.J, q, k, v, lam, beta, se, M, o, stream)
+            if rc != g.GDR_OK:
+                raise g.GdrError(rc, "gdr_dmem_fwd")
+
+        call()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            call()
+            b.record(stream)
+            torch.cuda.synchronize()
+            times.append(a.elapsed_time(b))
+        ms = sorted(times)[len(times) // 2]
+        nbytes = dmem_bytes(w)
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        res[w.name] = {"ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "algorithmic_bytes": nbytes,
+                       "writes": "segment (SSW)" if w.seg_mean > 0 else f"token, {w.J} sub-states (MSW)",
+                       "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                    "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(w.name, digest)}}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -363,63 +498,16 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes_read": 4 * n, "copy_bytes_written": 4 * n, "launches": 3}))
         return
-    w = {"gdn": gi.GDN_PREFILL, "kda_fg2plus": gi.KDA_FG2PLUS_PREFILL, "osdn_long": gi.OSDN_LONG_PREFILL}[args.workload]
-    x = gi.make_prefill(w)
-    d = {k: gi.to_torch(x[k], w.io if k in ("q", "k", "k_w", "v") else (w.gate if k != "S0" else gi.F32))
-         for k in x}
-    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], d["beta_v"], chunk=w.chunk)
-    path = g.gdr_chunk_fwd_path(desc)
-    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=d["q"].dtype, device=dev)
-    ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
-    wsz = g.gdr_chunk_fwd_workspace_size(desc)
-    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        rc = g.gdr_chunk_fwd(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"], d["beta_v"],
-                             d["S0"], o, ST, ws, wsz, stream)
-        if rc != g.GDR_OK:
-            raise g.GdrError(rc, "gdr_chunk_fwd")
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    # the K calls run back to back between one pair of HIP events on the launch stream
-    # (an event pair around every call would add its own few microseconds per call)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        step()
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_event = e0.elapsed_time(e1) / args.steps
-    ms_step = wall * 1e3 / args.steps
-
-    # cold-cache time: flush L2 and the Infinity Cache between launches
-    flush = torch.empty(512 * 1024 * 1024 // 4, dtype=torch.float32, device=dev)
-    cold = []
-    for _ in range(5):
-        flush.fill_(1.0)
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record(stream)
-        step()
-        b.record(stream)
-        torch.cuda.synchronize()
-        cold.append(a.elapsed_time(b))
-    del flush
-    ms_cold = sorted(cold)[len(cold) // 2]
-
-    tokens = w.B * w.T
-    flops = prefill_flops_per_token_head(w.chunk, w.dk, w.dv) * tokens * w.H
-    nbytes = prefill_bytes(w)
+    wl = {"gdn": gi.GDN_PREFILL, "kda_fg2plus": gi.KDA_FG2PLUS_PREFILL, "osdn_long": gi.OSDN_LONG_PREFILL}
+    w = wl[args.workload]
     digest = kernel_source_digest()
-    traffic = load_traffic(w.name, digest)
-    roof = {"bound": "hbm", "achieved": nbytes / (ms_event * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "traffic": traffic}
-    roof["frac"] = roof["achieved"] / roof["peak"]
+    stream = torch.cuda.current_stream()
+    inputs = {w.name: gi.make_prefill(w)}
+    x = inputs[w.name]
+    head = time_prefill(g, gi, w, x, args.steps, args.warmup, stream, digest, cold=True)
+    progress(f"prefill {w.name}: {head['ms_per_call']:.4f} ms per call")
+    ms_step = head["ms_wall"]
+    tokens = w.B * w.T
     out = {
         "metric": "tokens/s gated-delta chunk fwd (H=16,d=128,T=4096); % MFMA peak; decode GB/s",
         "value": tokens / (ms_step * 1e-3),
@@ -428,18 +516,29 @@ def main():
         "ms_per_step": ms_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "T": w.T, "dk": w.dk, "dv": w.dv, "chunk": w.chunk,
-                   "gates": ("fp32 " + ("channel" if w.alpha_mode else "scalar") + " alpha, "
-                             + ["scalar", "shared-vector", "key/value-vector"][w.beta_mode] + " beta"
-                             + (", write key" if w.write_key else "")),
-                   "S0": "nonzero" if w.s0_std > 0 else "zero", "global_batch": w.B, "seq_len": w.T,
-                   "parallelism": "single GPU", "kernel_path": {1: "bf16-mfma", 2: "fp32-valu"}[path]},
-        "roofline": roof,
-        "mfma_frac": flops / (ms_event * 1e-3) / (BF16_MFMA_PEAK_TFLOPS * 1e12),
-        "prefill_detail": {"ms_event_mean": ms_event, "ms_cold_median": ms_cold,
-                           "algorithmic_bytes": nbytes, "algorithmic_flops": flops,
-                           "gbs_cold": nbytes / (ms_cold * 1e-3) / 1e9, "kernel_source_digest": digest},
+        "config": dict(head["config"], global_batch=w.B, seq_len=w.T, parallelism="single GPU"),
+        "roofline": head["roofline"],
+        "mfma_frac": head["mfma_frac"],
+        "prefill_detail": {"ms_event_mean": head["ms_per_call"], "ms_cold_median": head["ms_cold_median"],
+                           "algorithmic_bytes": head["algorithmic_bytes"], "algorithmic_flops": head["algorithmic_flops"],
+                           "gbs_cold": head["algorithmic_bytes"] / (head["ms_cold_median"] * 1e-3) / 1e9,
+                           "kernel_source_digest": digest},
     }
+    if not args.only_prefill:
+        # every other prefill configuration, timed the same way (fewer calls)
+        cfgs = {}
+        for wc, steps in ((gi.TINY_GDN_F32, 200), (gi.GDN_PREFILL, 20), (gi.KDA_FG2PLUS_PREFILL, 20),
+                          (gi.OSDN_LONG_PREFILL, 5)):
+            if wc.name == w.name:
+                cfgs[wc.name] = {k: head[k] for k in ("ms_per_call", "tokens_per_s", "roofline", "mfma_frac",
+                                                      "config")}
+                continue
+            if wc.name not in inputs:
+                inputs[wc.name] = gi.make_prefill(wc)
+            r = time_prefill(g, gi, wc, inputs[wc.name], steps, max(steps // 2, 3), stream, digest)
+            progress(f"prefill {wc.name}: {r['ms_per_call']:.4f} ms per call")
+            cfgs[wc.name] = {k: r[k] for k in ("ms_per_call", "tokens_per_s", "roofline", "mfma_frac", "config")}
+        out["configs"] = cfgs
 
     if not args.only_prefill:
         dec = {}
@@ -474,12 +573,22 @@ def main():
                                          "frac": gbs / HBM_PEAK_GBS, "traffic": load_traffic(wd.name, digest)}}
             del graph, dd, S
         out["decode"] = dec
+        out["configs"].update(dec)  # the decode configuration (and its delta-mem case) in the same table
+        progress("decode done")
         out["mc_readout"] = bench_mc_readout(g, gi, stream, args.mc_reps, digest)
-        out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps, digest)
+        progress("mc_readout done")
+        out["dmem_pass"] = bench_dmem(g, gi, stream, args.mc_reps, digest)
+        progress("delta-mem passes done")
+        out["osdn_precond"] = bench_osdn_precond(g, gi, stream, args.mc_reps, digest,
+                                                 inputs.get(gi.OSDN_LONG_PREFILL.name))
+        progress("osdn_precond done")
         out["sdm"] = bench_sdm(g, gi, stream, args.mc_reps, digest)
+        progress("sdm done")
         out["copy_bandwidth"] = copy_bandwidth()
+        progress("copy_bandwidth done")
 
     if not args.no_cpu:
+        progress("CPU oracle baseline")
         out["cpu_baseline"] = cpu_baseline(w, x, args.cpu_heads)
         if not args.only_prefill:
             out["cpu_baseline_detail"] = cpu_baseline_detail(gi)
