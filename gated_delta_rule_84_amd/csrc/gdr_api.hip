@@ -426,7 +426,10 @@ int gdr_dmem_fwd(const gdr_desc *d, int32_t J, const void *q, const void *k, con
     if ((r != 8 && r != 16) || (J != 1 && J != 2 && J != 4 && J != 8) || J > 64 / r) return GDR_EUNSUPPORTED;
     if (d->H % J) return GDR_EINVAL;
     const long long nbh = (long long)d->B * d->H, ntok = nbh * d->T;
-    if (nbh > 0x7fffffffLL || ntok * r > 0x7fffffffffffLL) return GDR_EUNSUPPORTED;
+    // every tensor is addressed with 32-bit byte offsets
+    if (nbh > 0x7fffffffLL || ntok * r * (d->io_dtype == GDR_BF16 ? 2 : 4) > 0x7fffffffLL ||
+        (long long)d->B * d->T > 0x7fffffffLL)
+        return GDR_EUNSUPPORTED;
     if (ntok == 0) return GDR_OK;
     if (!q || !k || !v || !lam || !beta || !M || !out) return GDR_EINVAL;
     const size_t es = d->io_dtype == GDR_BF16 ? 2 : 4, gs = d->gate_dtype == GDR_BF16 ? 2 : 4;

@@ -335,7 +335,8 @@ int gdr_sdm_fwd(const gdr_desc *desc, int32_t n, int32_t W, int32_t R, const flo
  *   out       [B, T, H / J, r] io_dtype (bf16 rounded to nearest even)
  * desc: B, T, H >= 0; dk == dv == r; alpha_mode, beta_mode scalar; flags 0; chunk
  * not used.  Supported: r = 8 (J = 1, 2, 4, 8) or r = 16 (J = 1, 2, 4), H a multiple
- * of J (else GDR_EUNSUPPORTED / GDR_EINVAL).  Outputs must not overlap the inputs.
+ * of J, each of q, k, v at most 2^31 - 1 bytes (else GDR_EUNSUPPORTED / GDR_EINVAL).
+ * Outputs must not overlap the inputs.
  * Runs on `stream`; returns once the work is enqueued.
  */
 int gdr_dmem_fwd(const gdr_desc *desc, int32_t J, const void *q, const void *k, const void *v, const void *lam,

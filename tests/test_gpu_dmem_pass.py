@@ -59,6 +59,11 @@ CASES = [
     ("r16_f32_J2", BASE.scaled(r=16, H=2, J=2, io=gi.F32, gate=gi.F32, seed=611)),
     ("one_token", BASE.scaled(T=1, seed=612)),
     ("ragged_block_T6", BASE.scaled(B=3, T=6, H=2, seed=613)),
+    # tensors under 4 bytes (one bf16 gate, three segment marks) and a gate tensor
+    # whose size is not a multiple of 4 bytes (its last element in a half word)
+    ("one_memory_one_token", BASE.scaled(B=1, T=1, H=1, seed=614)),
+    ("one_memory_three_tokens", BASE.scaled(B=1, T=3, H=1, seed=615)),
+    ("odd_gate_count_r16", BASE.scaled(B=7, T=33, H=1, r=16, seed=616)),
 ]
 
 
