@@ -61,7 +61,12 @@ def _bind(lib):
     ip = ctypes.POINTER(ctypes.c_int)
     lib.gdr_ref_forward.argtypes = [ctypes.c_int] * 7 + [dp] * 10 + [ip, ctypes.c_int, ctypes.c_int]
     lib.gdr_ref_forward.restype = ctypes.c_int
-    lib.gdr_ref_decode_step.argtypes = [ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_int]
+    lib.gdr_ref_decode_step_f64.argtypes = [ctypes.c_int] * 6 + [dp] * 9 + [ctypes.c_int]
+    lib.gdr_ref_decode_step_f64.restype = ctypes.c_int
+    vp = ctypes.c_void_p
+    lib.gdr_ref_chunk_fwd.argtypes = [vp] * 12 + [ctypes.c_size_t, vp]
+    lib.gdr_ref_chunk_fwd.restype = ctypes.c_int
+    lib.gdr_ref_decode_step.argtypes = [vp] * 11
     lib.gdr_ref_decode_step.restype = ctypes.c_int
     lib.gdr_ref_dmem_step.argtypes = [ctypes.c_int] * 4 + [dp] * 7 + [ctypes.c_int]
     lib.gdr_ref_dmem_step.restype = ctypes.c_int
@@ -165,11 +170,11 @@ def decode_step(S, q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, alpha_mode=
     if beta_mode is None:
         beta_mode = 0 if beta_k.ndim == 2 else (2 if beta_v is not None else 1)
     o = np.empty((B, H, dv))
-    rc = _load().gdr_ref_decode_step(B, H, dk, dv, alpha_mode, beta_mode, _dp(q), _dp(k), _dp(k_w),
+    rc = _load().gdr_ref_decode_step_f64(B, H, dk, dv, alpha_mode, beta_mode, _dp(q), _dp(k), _dp(k_w),
                                      _dp(v), _dp(alpha), _dp(beta_k), _dp(beta_v), _dp(S), _dp(o),
                                      nthreads)
     if rc != 0:
-        raise ValueError(f"gdr_ref_decode_step rejected its arguments (status {rc})")
+        raise ValueError(f"gdr_ref_decode_step_f64 rejected its arguments (status {rc})")
     return o, S
 
 

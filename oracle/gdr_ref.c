@@ -181,10 +181,10 @@ int gdr_ref_forward(int B, int T, int H, int dk, int dv, int alpha_mode, int bet
  * read-out o [B, H, dv].  Per-token inputs have the prefill layouts with T
  * removed: q, k, kw [B, H, dk], v [B, H, dv], alpha [B, H] or [B, H, dk], ...
  */
-int gdr_ref_decode_step(int B, int H, int dk, int dv, int alpha_mode, int beta_mode,
-                        const double *q, const double *k, const double *kw, const double *v,
-                        const double *alpha, const double *beta_k, const double *beta_v,
-                        double *S, double *o, int nthreads)
+int gdr_ref_decode_step_f64(int B, int H, int dk, int dv, int alpha_mode, int beta_mode,
+                            const double *q, const double *k, const double *kw, const double *v,
+                            const double *alpha, const double *beta_k, const double *beta_v,
+                            double *S, double *o, int nthreads)
 {
     int rc = ref_check(B, 1, H, dk, dv, alpha_mode, beta_mode);
     if (rc) return rc;
@@ -309,6 +309,132 @@ int gdr_ref_osdn_precond(int B, int T, int H, int dk, const double *k, const dou
         if (qgeo) qgeo[bh] = T > 0 ? exp(logsum / T) : 1.0;
     }
     return REF_OK;
+}
+
+/*
+ * Mirrors of the GPU library's two entry points, with its argument list: a
+ * descriptor laid out field for field like the library's (declared here, not
+ * shared), HOST pointers to inputs in their stored dtypes (dtype 0: bf16 bit
+ * patterns, 1: fp32), the fp64 recurrence above inside, o written in the io
+ * dtype and the states in fp32 -- each output rounded the way the input generator
+ * stores values (fp64 -> fp32 round-to-nearest-even -> bf16 round-to-nearest-even).
+ * The chunk size, workspace and stream are accepted and not used (the recurrence is
+ * sequential); flags must be 0.  S0 == NULL starts from 0, ST == NULL skips it;
+ * S0 == ST is allowed.
+ */
+typedef struct {
+    int B, T, H, dk, dv, chunk, io_dtype, gate_dtype, alpha_mode, beta_mode, flags;
+} gdr_ref_desc;
+
+static double ref_ld(const void *p, size_t i, int dtype)
+{
+    if (dtype == 0) {
+        const unsigned int u = (unsigned int)((const unsigned short *)p)[i] << 16;
+        float f;
+        memcpy(&f, &u, 4);
+        return f;
+    }
+    return ((const float *)p)[i];
+}
+
+static void ref_st(void *p, size_t i, double x, int dtype)
+{
+    const float f = (float)x;
+    if (dtype != 0) {
+        ((float *)p)[i] = f;
+        return;
+    }
+    unsigned int u;
+    memcpy(&u, &f, 4);
+    if ((u & 0x7fffffffu) > 0x7f800000u) u = 0x7fc00000u;   /* NaN */
+    else u += 0x7fffu + ((u >> 16) & 1u);                   /* nearest, ties to even */
+    ((unsigned short *)p)[i] = (unsigned short)(u >> 16);
+}
+
+/* fp64 copy of n stored values (NULL in, NULL out); *bad set on allocation failure */
+static double *ref_up(const void *p, size_t n, int dtype, int *bad)
+{
+    if (!p) return NULL;
+    double *x = (double *)malloc(sizeof(double) * (n ? n : 1));
+    if (!x) { *bad = 1; return NULL; }
+    for (size_t i = 0; i < n; ++i) x[i] = ref_ld(p, i, dtype);
+    return x;
+}
+
+static int ref_desc_ok(const gdr_ref_desc *d)
+{
+    if (!d || d->flags != 0) return 0;
+    if ((d->io_dtype != 0 && d->io_dtype != 1) || (d->gate_dtype != 0 && d->gate_dtype != 1)) return 0;
+    return ref_check(d->B, d->T < 0 ? -1 : (d->T ? d->T : 1), d->H, d->dk, d->dv, d->alpha_mode, d->beta_mode) == REF_OK;
+}
+
+int gdr_ref_chunk_fwd(const gdr_ref_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                      const void *alpha, const void *beta_k, const void *beta_v, const float *S0, void *o,
+                      float *ST, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace; (void)workspace_bytes; (void)stream;
+    if (!ref_desc_ok(d)) return REF_EINVAL;
+    const size_t ntok = (size_t)d->B * d->T * d->H, nbh = (size_t)d->B * d->H, sd = (size_t)d->dk * d->dv;
+    if (ntok && (!q || !k || !v || !alpha || !beta_k || !o)) return REF_EINVAL;
+    if (d->beta_mode == 2 && ntok && !beta_v) return REF_EINVAL;
+    int bad = 0;
+    const int io = d->io_dtype, gt = d->gate_dtype;
+    double *q8 = ref_up(q, ntok * d->dk, io, &bad), *k8 = ref_up(k, ntok * d->dk, io, &bad);
+    double *w8 = ref_up(k_w, ntok * d->dk, io, &bad), *v8 = ref_up(v, ntok * d->dv, io, &bad);
+    double *a8 = ref_up(alpha, ntok * (d->alpha_mode ? d->dk : 1), gt, &bad);
+    double *bk8 = ref_up(beta_k, ntok * (d->beta_mode ? d->dk : 1), gt, &bad);
+    double *bv8 = ref_up(d->beta_mode == 2 ? beta_v : NULL, ntok * d->dv, gt, &bad);
+    double *s08 = ref_up(S0, nbh * sd, 1, &bad);
+    double *o8 = (double *)malloc(sizeof(double) * (ntok * d->dv ? ntok * d->dv : 1));
+    double *st8 = (double *)malloc(sizeof(double) * (nbh * sd ? nbh * sd : 1));
+    int rc = REF_EINVAL;
+    if (!bad && o8 && st8) {
+        if (ntok == 0) {  /* no token: S_T = S0 */
+            for (size_t i = 0; i < nbh * sd; ++i) st8[i] = s08 ? s08[i] : 0.0;
+            rc = REF_OK;
+        } else {
+            rc = gdr_ref_forward(d->B, d->T, d->H, d->dk, d->dv, d->alpha_mode, d->beta_mode, q8, k8, w8, v8, a8,
+                                 bk8, bv8, s08, o8, st8, NULL, 0, 0);
+        }
+        if (rc == REF_OK) {
+            for (size_t i = 0; i < ntok * d->dv; ++i) ref_st(o, i, o8[i], io);
+            if (ST)
+                for (size_t i = 0; i < nbh * sd; ++i) ST[i] = (float)st8[i];
+        }
+    }
+    free(q8); free(k8); free(w8); free(v8); free(a8); free(bk8); free(bv8); free(s08); free(o8); free(st8);
+    return rc;
+}
+
+int gdr_ref_decode_step(const gdr_ref_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                        const void *alpha, const void *beta_k, const void *beta_v, float *S, void *o, void *stream)
+{
+    (void)stream;
+    if (!ref_desc_ok(d)) return REF_EINVAL;
+    const size_t nbh = (size_t)d->B * d->H, sd = (size_t)d->dk * d->dv;
+    if (nbh == 0) return REF_OK;
+    if (!q || !k || !v || !alpha || !beta_k || !S || !o) return REF_EINVAL;
+    if (d->beta_mode == 2 && !beta_v) return REF_EINVAL;
+    int bad = 0;
+    const int io = d->io_dtype, gt = d->gate_dtype;
+    double *q8 = ref_up(q, nbh * d->dk, io, &bad), *k8 = ref_up(k, nbh * d->dk, io, &bad);
+    double *w8 = ref_up(k_w, nbh * d->dk, io, &bad), *v8 = ref_up(v, nbh * d->dv, io, &bad);
+    double *a8 = ref_up(alpha, nbh * (d->alpha_mode ? d->dk : 1), gt, &bad);
+    double *bk8 = ref_up(beta_k, nbh * (d->beta_mode ? d->dk : 1), gt, &bad);
+    double *bv8 = ref_up(d->beta_mode == 2 ? beta_v : NULL, nbh * d->dv, gt, &bad);
+    double *s8 = ref_up(S, nbh * sd, 1, &bad);
+    double *o8 = (double *)malloc(sizeof(double) * nbh * d->dv);
+    int rc = REF_EINVAL;
+    if (!bad && o8) {
+        rc = gdr_ref_decode_step_f64(d->B, d->H, d->dk, d->dv, d->alpha_mode, d->beta_mode, q8, k8, w8, v8, a8, bk8,
+                                     bv8, s8, o8, 0);
+        if (rc == REF_OK) {
+            for (size_t i = 0; i < nbh * d->dv; ++i) ref_st(o, i, o8[i], io);
+            for (size_t i = 0; i < nbh * sd; ++i) S[i] = (float)s8[i];
+        }
+    }
+    free(q8); free(k8); free(w8); free(v8); free(a8); free(bk8); free(bv8); free(s8); free(o8);
+    return rc;
 }
 
 int gdr_ref_max_threads(void)
