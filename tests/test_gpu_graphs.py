@@ -1,5 +1,5 @@
-"""Prefill (every kernel family), segment checkpoints, OSDN phase 1 and the
-Memory-Caching read-out inside captured HIP graphs.  The library allocates
+"""Prefill (every kernel family), segment checkpoints, OSDN phase 1, the
+Memory-Caching read-out and the delta-mem pass inside captured HIP graphs.  The library allocates
 nothing, clears nothing with memsets and launches only its own kernels, so a call
 made on a capturing stream is recorded whole.  Each case captures one call, then
 replays the graph three times with eager work between the replays, and every
@@ -104,3 +104,33 @@ def test_mc_readout_graph_replays_equal_eager():
     graph, _ = _capture(torch, lambda: g.mc_readout(q, ckpt, w.seg, gates=gates, o_in=o_in, out=o_g))
     _replay_and_compare(torch, graph, (o_g,), lambda: (g.mc_readout(q, ckpt, w.seg, gates=gates, o_in=o_in),),
                         "mc_readout")
+
+
+@pytest.mark.parametrize("seg", [False, True], ids=["token_writes", "segment_writes"])
+def test_dmem_pass_graph_replays_equal_eager(seg):
+    """The delta-mem pass (memories updated in place) captured in a graph: before each
+    replay the memories are reset from M0 outside the graph; every replay's reads and
+    memories equal an eager call on a copy of M0, bit for bit."""
+    import numpy as np
+
+    torch, g = gpu()
+    w = gi.DMEM_MSW.scaled(B=40, T=70, H=8, J=4, seg_mean=5.0 if seg else 0.0, seed=128)
+    x = gi.make_dmem_seq(w)
+    q, k, v = (gi.to_torch(x[n], w.io) for n in ("q", "k", "v"))
+    lam, beta = gi.to_torch(x["lam"], w.gate), gi.to_torch(x["beta"], w.gate)
+    se = torch.from_numpy(np.ascontiguousarray(x["seg_end"])).cuda() if seg else None
+    M0 = gi.to_torch(x["M0"], gi.F32)
+    M_g = M0.clone()
+    out_g = torch.empty((w.B, w.T, w.H // w.J, w.r), dtype=q.dtype, device="cuda")
+    graph, _ = _capture(torch, lambda: g.dmem_fwd(M_g, q, k, v, lam, beta, seg_end=se, J=w.J, out=out_g))
+    for rep in range(3):
+        M_g.copy_(M0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        M_e = M0.clone()
+        out_e = g.dmem_fwd(M_e, q, k, v, lam, beta, seg_end=se, J=w.J)
+        torch.cuda.synchronize()
+        same = (torch.equal(out_g, out_e), torch.equal(M_g, M_e))
+        log(f"[graph dmem seg={seg}] replay {rep}: reads, memories equal {same}")
+        assert all(same)

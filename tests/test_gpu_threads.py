@@ -67,15 +67,28 @@ def test_concurrent_side_stream_calls_equal_solo_calls():
         o = g.sdm_fwd(M, ks, qs, v, a, b, ws.W, ws.R, ctx=ctx, stream=stream)
         return (o, M)
 
-    solo = [osdn(None), prefill(None), sdm(None)]
+    wd = gi.DMEM_SSW.scaled(B=512, T=200, H=1, seed=134)
+    xd = gi.make_dmem_seq(wd)
+    dq, dkk, dv = (gi.to_torch(xd[n], wd.io) for n in ("q", "k", "v"))
+    dl, db = gi.to_torch(xd["lam"], wd.gate), gi.to_torch(xd["beta"], wd.gate)
+    dse = torch.from_numpy(xd["seg_end"]).cuda()
+    dM0 = gi.to_torch(xd["M0"], gi.F32)
+
+    def dmem(stream, ctx=None):
+        M = dM0.clone()
+        o = g.dmem_fwd(M, dq, dkk, dv, dl, db, seg_end=dse, stream=stream)
+        return (o, M)
+
+    solo = [osdn(None), prefill(None), sdm(None), dmem(None)]
     torch.cuda.synchronize()
     for name, pair in (("osdn + prefill", [osdn, prefill]), ("osdn + osdn", [osdn, osdn]),
-                       ("sdm + prefill", [sdm, prefill]), ("all three", [osdn, prefill, sdm])):
+                       ("sdm + prefill", [sdm, prefill]), ("all three", [osdn, prefill, sdm]),
+                       ("dmem + prefill + sdm", [dmem, prefill, sdm])):
         ctxs = [g.Context() for _ in pair]
         outs = _run_threads(torch, [lambda st, f=f, c=c: f(st, c) for f, c in zip(pair, ctxs)])
         for c in ctxs:
             c.close()
-        ref = {osdn: solo[0], prefill: solo[1], sdm: solo[2]}
+        ref = {osdn: solo[0], prefill: solo[1], sdm: solo[2], dmem: solo[3]}
         same = [all(torch.equal(x, y) for x, y in zip(out, ref[f])) for f, out in zip(pair, outs)]
         log(f"[threads] {name}: equal to the solo calls {same}")
         assert all(same)
