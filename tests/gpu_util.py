@@ -72,4 +72,7 @@ def run_prefill(w, x, *, heads=None, nthreads=0):
                finite=bool(np.isfinite(o_gpu).all() and np.isfinite(S_gpu).all()), oracle_s=t_or)
     log(f"          rel-L2 o={res['o']:.3e} S={res['S']:.3e} o_vs_rounded_oracle={res['o_vs_rounded']:.3e} "
         f"oracle {t_or:.1f}s")
+    # the stored output is as close to the oracle's own stored output as to the exact one
+    # (rounding both to the storage type removes no more than the tolerance)
+    assert res["o_vs_rounded"] <= TOL[w.io], res
     return res
