@@ -24,6 +24,11 @@ FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
     # packed-fp32 instructions disabled on purpose for the device pass
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # matrix-core results in ordinary VGPRs: the recurrence kernels read and rescale
+    # their accumulators on the vector ALU every chunk, and accumulators held in AGPRs
+    # cost a v_accvgpr move for each such access (the prefill state kernel's loop had
+    # about 190 of them per chunk)
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I", os.path.join(ROOT, "include"), "-I", CSRC,
     "-Wall", "-Wno-unused-function",
 ]
