@@ -100,6 +100,19 @@ __device__ __forceinline__ u32x4 ld16(const void *p) { return *reinterpret_cast<
 
 __device__ __forceinline__ float ld_gate(const void *p, long i, int bf16) { return ld_elem(p, i, bf16); }
 
+// Orders that let every matrix-core fragment come out of LDS as one 16-byte read.
+// A B fragment built from two vertically adjacent C tiles holds, in lane (r, q), rows
+// 4q .. 4q+3 of each tile, i.e. contraction slots 8q .. 8q+7 of a 32-block.
+//  * Key order inside the state kernels: row 4q + i of state tile kt holds key
+//    skey(kt, q, i), so the state fragment of k step kk covers the consecutive keys
+//    32 kk + 8 q .. + 7 and the key / query fragments are plain 16-byte row pieces.
+//  * Token columns of Tm and P in the record: column s = 32 kk + 16 h + 4 q + i sits at
+//    pcol(s) = 32 kk + 8 q + 4 h + i, the order of the residual fragments built from
+//    C tiles of token rows.
+__device__ __forceinline__ int skey(int kt, int q, int i) { return 32 * (kt >> 1) + 8 * q + 4 * (kt & 1) + i; }
+__device__ __forceinline__ int pcol(int s) { return (s & 32) | ((s & 12) << 1) | ((s & 16) >> 2) | (s & 3); }
+__device__ __forceinline__ int pcol_inv(int c) { return (c & 32) | ((c & 4) << 2) | ((c & 24) >> 1) | (c & 3); }
+
 
 // Workgroup barrier ordered for LDS only: the fences are restricted to the local
 // address space, so the barrier waits for this wave's LDS traffic but not for its
@@ -116,7 +129,7 @@ __device__ __forceinline__ void lds_barrier() {
 // pieces shared by the two prep kernels (256 threads, four waves)
 // ---------------------------------------------------------------------------
 // The lower-triangular Tm (fp32 rows in Ts, unit diagonal implied) to the record as
-// bf16 rows of 64, 16 bytes per store.
+// bf16 rows of 64 in pcol order, 16 bytes per store.
 __device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[kC + 8], const int tid) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {  // 512 pieces of 8 bf16
@@ -124,7 +137,7 @@ __device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[kC + 8], c
         u32x4 o;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const int ca = c0 + 2 * j, cb = ca + 1;
+            const int ca = pcol_inv(c0 + 2 * j), cb = pcol_inv(c0 + 2 * j + 1);
             const float va = ca < row ? Ts[row][ca] : (ca == row ? 1.f : 0.f);
             const float vb = cb < row ? Ts[row][cb] : (cb == row ? 1.f : 0.f);
             o[j] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)va) |
@@ -276,8 +289,8 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
             }
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
-            Ph[tp][s] = __builtin_bit_cast(uint16_t, hi);
-            Pl[tp][s] = __builtin_bit_cast(uint16_t, lo);
+            Ph[tp][pcol(s)] = __builtin_bit_cast(uint16_t, hi);
+            Pl[tp][pcol(s)] = __builtin_bit_cast(uint16_t, lo);
         }
     }
     __syncthreads();
@@ -506,8 +519,8 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
                 const float pv = (J <= IP && s <= tq && tq < n) ? accP[J][i] : 0.f;
                 const __bf16 hi = (__bf16)pv;
                 const __bf16 lo = (__bf16)(pv - (float)hi);
-                Ph[tq][s] = __builtin_bit_cast(uint16_t, hi);
-                Pl[tq][s] = __builtin_bit_cast(uint16_t, lo);
+                Ph[tq][pcol(s)] = __builtin_bit_cast(uint16_t, hi);
+                Pl[tq][pcol(s)] = __builtin_bit_cast(uint16_t, lo);
             }
         }
     } else {
@@ -549,8 +562,8 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
             const float pv = (s <= te && te < n) ? aP[j] : 0.f;
             const __bf16 hi = (__bf16)pv;
             const __bf16 lo = (__bf16)(pv - (float)hi);
-            Ph[te][s] = __builtin_bit_cast(uint16_t, hi);
-            Pl[te][s] = __builtin_bit_cast(uint16_t, lo);
+            Ph[te][pcol(s)] = __builtin_bit_cast(uint16_t, hi);
+            Pl[te][pcol(s)] = __builtin_bit_cast(uint16_t, lo);
         }
     }
     __syncthreads();
@@ -580,12 +593,13 @@ __device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
 // is a 16-column MFMA whose B operand is built in registers from the C tiles of
 // the product before it.  A C tile holds rows 4q .. 4q+3 of its 16 rows in lane
 // (r, q), so two vertically adjacent C tiles give lane (r, q) the eight rows
-// {4q .. 4q+3, 16+4q .. 16+4q+3} of a 32-row block: the contraction index of
-// every product runs in that order within each 32-block, and the A operands are
-// read from LDS in the same order (two 8-byte reads per fragment).  The
-// transposed write key comes from the row-major key tile with the gfx950
-// transposing LDS read (ds_read_b64_tr_b16: lane j of each 16-lane group receives
-// element j of the 4 rows addressed by its group).
+// {4q .. 4q+3, 16+4q .. 16+4q+3} of a 32-row block.  The state's key rows are
+// therefore kept in the skey order and Tm's and P's token columns in the pcol order,
+// which map those eight rows to eight consecutive keys or stored columns: every A
+// operand is one 16-byte LDS read.  The transposed write key comes from the
+// row-major key tile with the gfx950 transposing LDS read (ds_read_b64_tr_b16:
+// lane j of each 16-lane group receives element j of the 4 rows addressed by its
+// group; each lane addresses the 4 consecutive keys of its skey group).
 // Waves 2 and 3 ("side" waves) take the rest for the same columns: they copy the
 // next chunk's operands global -> LDS (global_load_lds; keys, queries, write keys,
 // Tm and the decay factors into the other half of a double buffer at the chunk
@@ -636,14 +650,8 @@ __device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &l
     lo = cat(la, lb);
 }
 
-// A fragment of rows t (lane row r) of a key-width tile, k step kk, in the
-// contraction order {4q .. 4q+3, 16+4q .. 16+4q+3} of the 32-block
-__device__ __forceinline__ u32x4 frag_wide(const uint16_t (*M)[kD], int t, int kk, int q) {
-    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1), sw = t & 15;
-    return cat(ld8(&M[t][8 * (p1 ^ sw) + hf]), ld8(&M[t][8 * (p2 ^ sw) + hf]));
-}
-
-// B fragment (natural order: 8 consecutive keys) of a key-width tile row t
+// Fragment of row t (lane row r) of a key-width tile, k step kk: keys 32 kk + 8 q .. + 7
+// (the state's key order, skey)
 __device__ __forceinline__ u32x4 frag_row(const uint16_t (*M)[kD], int t, int kk, int q) {
     return *reinterpret_cast<const u32x4 *>(&M[t][8 * ((4 * kk + q) ^ (t & 15))]);
 }
@@ -748,7 +756,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + skey(kt, q, i)) * kD + cw + r];
         } else {
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -775,7 +783,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) ka[kk][tt] = frag_wide(B.K, 16 * tt + r, kk, q);
+                    for (int tt = 0; tt < 4; ++tt) ka[kk][tt] = frag_row(B.K, 16 * tt + r, kk, q);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     sh[kk] = sm.Sx[w][2 * kk][l];
@@ -822,8 +830,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
                     for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                        const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
-                        ta[f] = cat(ld8(&B.T[t][8 * (p1 ^ sw) + hf]), ld8(&B.T[t][8 * (p2 ^ sw) + hf]));
+                        ta[f] = *reinterpret_cast<const u32x4 *>(&B.T[t][8 * ((4 * kk + q) ^ sw)]);
                     }
                 }
 #pragma unroll
@@ -861,7 +868,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
-                        const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
+                        const int pc = 4 * (kt >> 1) + a, hf = 4 * (kt & 1);
                         kw[kt][kk] = cat(ld_tr(&KWs[t1][8 * (pc ^ (t1 & 15)) + hf]),
                                          ld_tr(&KWs[t2][8 * (pc ^ (t2 & 15)) + hf]));
                     }
@@ -881,7 +888,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Ck[(long)(16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+                    for (int i = 0; i < 4; ++i) Ck[(long)(skey(kt, q, i)) * kD + cw + r] = S[kt][i];
             }
         } else {
             if (c + 1 < p.c1) issue(c + 1, bb ^ 1);
@@ -892,7 +899,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) qa[kk][tt] = frag_wide(B.Q, 16 * tt + r, kk, q);
+                    for (int tt = 0; tt < 4; ++tt) qa[kk][tt] = frag_row(B.Q, 16 * tt + r, kk, q);
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk) {
                     sh[kk] = sm.Sx[w][2 * kk][l];
@@ -918,9 +925,8 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                 const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
                 for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
-                    ph[f] = cat(ld8(&sm.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Ph[t][8 * (p2 ^ sw) + hf]));
-                    pl[f] = cat(ld8(&sm.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Pl[t][8 * (p2 ^ sw) + hf]));
+                    ph[f] = *reinterpret_cast<const u32x4 *>(&sm.Ph[t][8 * ((4 * kk + q) ^ sw)]);
+                    pl[f] = *reinterpret_cast<const u32x4 *>(&sm.Pl[t][8 * ((4 * kk + q) ^ sw)]);
                 }
             }
             // B1: D published; V and the P terms of this chunk consumed.  The side wave's
@@ -977,7 +983,7 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + skey(kt, q, i)) * kD + cw + r] = S[kt][i];
     }
 }
 
@@ -1115,7 +1121,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r];
+                for (int i = 0; i < 4; ++i) S[kt][i] = p.S0[((long)bh * kD + skey(kt, q, i)) * kD + cw + r];
         } else {
 #pragma unroll
             for (int kt = 0; kt < 8; ++kt) S[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1147,8 +1153,8 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                     u32x4 ah[4], al[4];
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
-                        ah[tt] = frag_wide(sm.Uh, 16 * tt + r, kk, q);
-                        al[tt] = frag_wide(sm.Ul, 16 * tt + r, kk, q);
+                        ah[tt] = frag_row(sm.Uh, 16 * tt + r, kk, q);
+                        al[tt] = frag_row(sm.Ul, 16 * tt + r, kk, q);
                     }
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
@@ -1192,8 +1198,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                     const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
                     for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                        const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
-                        ta[f] = cat(ld8(&sm.T[t][8 * (p1 ^ sw) + hf]), ld8(&sm.T[t][8 * (p2 ^ sw) + hf]));
+                        ta[f] = *reinterpret_cast<const u32x4 *>(&sm.T[t][8 * ((4 * kk + q) ^ sw)]);
                     }
                 }
 #pragma unroll
@@ -1220,13 +1225,13 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
             {
                 const int a = r & 3, m = r >> 2;
 #pragma unroll
-                for (int kt = 0; kt < 8; ++kt) S[kt] *= *reinterpret_cast<const f32x4 *>(&sm.GC[16 * kt + 4 * q]);
+                for (int kt = 0; kt < 8; ++kt) S[kt] *= *reinterpret_cast<const f32x4 *>(&sm.GC[skey(kt, q, 0)]);
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
                     for (int kk = 0; kk < 2; ++kk) {
                         const int t1 = 32 * kk + 4 * q + m, t2 = t1 + 16;
-                        const int pc = 2 * kt + (a >> 1), hf = 4 * (a & 1);
+                        const int pc = 4 * (kt >> 1) + a, hf = 4 * (kt & 1);
                         const u32x4 wh = cat(ld_tr(&sm.Wh[t1][8 * (pc ^ (t1 & 15)) + hf]),
                                              ld_tr(&sm.Wh[t2][8 * (pc ^ (t2 & 15)) + hf]));
                         const u32x4 wl = cat(ld_tr(&sm.Wl[t1][8 * (pc ^ (t1 & 15)) + hf]),
@@ -1242,7 +1247,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) Ck[(long)(16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+                    for (int i = 0; i < 4; ++i) Ck[(long)(skey(kt, q, i)) * kD + cw + r] = S[kt][i];
             }
         } else {
             if (c > 0) issue_w(c);
@@ -1262,8 +1267,8 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                     u32x4 ah[4], al[4];
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
-                        ah[tt] = frag_wide(sm.Qh, 16 * tt + r, kk, q);
-                        al[tt] = frag_wide(sm.Ql, 16 * tt + r, kk, q);
+                        ah[tt] = frag_row(sm.Qh, 16 * tt + r, kk, q);
+                        al[tt] = frag_row(sm.Ql, 16 * tt + r, kk, q);
                     }
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) {
@@ -1279,9 +1284,8 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
                 const int t = 16 * tt + r, sw = (t >> 1) & 7;
 #pragma unroll
                 for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                    const int p1 = 4 * kk + (q >> 1), p2 = p1 + 2, hf = 4 * (q & 1);
-                    ph[f] = cat(ld8(&sm.Ph[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Ph[t][8 * (p2 ^ sw) + hf]));
-                    pl[f] = cat(ld8(&sm.Pl[t][8 * (p1 ^ sw) + hf]), ld8(&sm.Pl[t][8 * (p2 ^ sw) + hf]));
+                    ph[f] = *reinterpret_cast<const u32x4 *>(&sm.Ph[t][8 * ((4 * kk + q) ^ sw)]);
+                    pl[f] = *reinterpret_cast<const u32x4 *>(&sm.Pl[t][8 * ((4 * kk + q) ^ sw)]);
                 }
             }
             lds_barrier();  // B1 (also: this wave's copies of W have landed)
@@ -1328,7 +1332,7 @@ __global__ void __launch_bounds__(256) gdr_state_chan_kernel(ChunkParams p, int 
 #pragma unroll
         for (int kt = 0; kt < 8; ++kt)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + 16 * kt + 4 * q + i) * kD + cw + r] = S[kt][i];
+            for (int i = 0; i < 4; ++i) p.ST[((long)bh * kD + skey(kt, q, i)) * kD + cw + r] = S[kt][i];
     }
 }
 

@@ -11,12 +11,19 @@ from tests.gpu_util import TOL, gpu, log, run_prefill, upload
 
 pytestmark = pytest.mark.gpu
 
-REC_BYTES = 25728  # per-chunk record: T bf16[64][64] | P hi bf16[64][64] | P lo | gam f32[64] | fac f32[64]
+REC_BYTES = 25728  # per-chunk record: T bf16[64][64] | P hi bf16[64][64] | P lo (columns permuted, below)
+#                    | gam f32[64] | fac f32[64]
 #                    | gC (128-byte slot) | g f32[64] | beta f32[64]
 
 
 def _bf16(u16):
     return gi.bf16_bits_to_f32(u16).astype(np.float64)
+
+
+# Tm and P keep their token columns in the order the state kernels' fragments read them:
+# column s = 32 kk + 16 h + 4 q + i is stored at 32 kk + 8 q + 4 h + i.
+_STORED_COL = np.array([(s & 32) | ((s & 12) << 1) | ((s & 16) >> 2) | (s & 3) for s in range(64)])
+assert sorted(_STORED_COL.tolist()) == list(range(64))
 
 
 @pytest.mark.parametrize("T,write_key", [(200, False), (128, True)])
@@ -41,9 +48,9 @@ def test_prep_record_matches_numpy(T, write_key):
         b, h = divmod(bh, w.H)
         for c in range(NT):
             rec = raw[(bh * NT + c) * REC_BYTES:(bh * NT + c + 1) * REC_BYTES]
-            Tg = _bf16(rec[0:8192].view(np.uint16).reshape(64, 64))
-            Pg = _bf16(rec[8192:16384].view(np.uint16).reshape(64, 64)) + \
-                _bf16(rec[16384:24576].view(np.uint16).reshape(64, 64))
+            Tg = _bf16(rec[0:8192].view(np.uint16).reshape(64, 64))[:, _STORED_COL]
+            Pg = (_bf16(rec[8192:16384].view(np.uint16).reshape(64, 64)) +
+                  _bf16(rec[16384:24576].view(np.uint16).reshape(64, 64)))[:, _STORED_COL]
             gam = rec[24576:24832].view(np.float32).astype(np.float64)
             fac = rec[24832:25088].view(np.float32).astype(np.float64)
             gC = float(rec[25088:25092].view(np.float32)[0])
