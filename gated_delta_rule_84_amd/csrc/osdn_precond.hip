@@ -21,7 +21,8 @@
 //   osdn_chain_kernel   one workgroup per (batch, head), chunks in order, only what
 //                       the next chunk needs: x_t = <a_t, d_0>, e = Tm z and
 //                       d_n = P_n d_0 + sum_j (P_n / P_{j+1}) e_j a_j; d_0 and e of
-//                       every chunk go to its record.
+//                       every chunk go to its record.  Four waves carry the chain, four
+//                       more stage the next chunk's keys (as k^2) and record head.
 //   osdn_emit_kernel    every chunk in parallel again: from d_0 and e, d one token at
 //                       a time (a key channel per thread), the write keys, and the
 //                       chunk's sum of log loss ratios.
@@ -240,7 +241,7 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
 }
 
 template <bool BF>
-__global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
+__global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
     // chunk operands, double buffered: a = k^2 (rows of 132 floats: 16-byte aligned,
     // zero past dk; row kPL is a sink), Tm and the vector rows of the record
     constexpr int kKP = kPD + 4;
@@ -249,13 +250,17 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
     __shared__ __attribute__((aligned(16))) float vc[2][7][kPL];  // c, cb, beta, r, P, rho, (Pn in [6][0])
     __shared__ __attribute__((aligned(16))) float d[kPD];
     __shared__ float zs[kPL], we[kPL];
-    const int tid = threadIdx.x;
+    // waves 0-3 carry the chain; waves 4-7 ("stagers") copy the chunk after the current
+    // one into the other half of the LDS double buffer, so that the chain's waves do
+    // nothing between their three barriers per chunk but the chain
+    const int tid = threadIdx.x & (kPThreads - 1);
+    const bool stager = threadIdx.x >= kPThreads;
     const int bh = blockIdx.x;
     const int b = bh / p.H, h = bh % p.H, dk = p.dk;
-    for (int i = tid; i < 2 * (kPL + 1) * kKP; i += kPThreads) (&kf[0][0][0])[i] = 0.f;
+    for (int i = threadIdx.x; i < 2 * (kPL + 1) * kKP; i += 2 * kPThreads) (&kf[0][0][0])[i] = 0.f;
     // d at the start of chunk c0: the initial preconditioner, or (a later block of
     // chunks) what the launch for the block before left in chunk c0's record
-    if (tid < kPD) {
+    if (!stager && tid < kPD) {
         float v = 0.f;
         if (tid < dk)
             v = p.c0 > 0 ? p.rec[((long)bh * p.NT + p.c0) * kPrWords + kPrD0 + tid]
@@ -263,8 +268,8 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
         d[tid] = v;
     }
 
-    // register copies of two chunks ahead (two sets, used alternately): keys (16-byte
-    // pieces) and the record head (Tm and the vectors: 1,136 pieces)
+    // stagers: register copies of two chunks ahead (two sets, used alternately): keys
+    // (16-byte pieces) and the record head (Tm and the vectors: 1,136 pieces)
     constexpr int ksz = BF ? 2 : 4;  // bytes per key element
     const int kpieces = dk * ksz / 16;
     u32x4 kA[8], rA[5], kB[8], rB[5];
@@ -333,10 +338,9 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
         }
     };
 
-    // One chunk of the chain from buffer bf (filled during the previous chunk); at its
-    // end the next chunk is staged into the other buffer from (kn, rn), which are then
-    // refilled with the chunk after that.  Three barriers.
-    auto step = [&](int c, int bf, u32x4 (&kn)[8], u32x4 (&rn)[5]) __attribute__((always_inline)) {
+    // One chunk of the chain from buffer bf (staged during the previous chunk).  Three
+    // barriers.
+    auto step = [&](int c, int bf) __attribute__((always_inline)) {
         float *rec = p.rec + ((long)bh * p.NT + c) * kPrWords;
         lds_sync();  // this chunk's operands staged; d of its start complete
         if (tid < dk) rec[kPrD0 + tid] = d[tid];
@@ -387,25 +391,40 @@ __global__ void __launch_bounds__(kPThreads) osdn_chain_kernel(PcParams p) {
             sum += __shfl_xor(sum, 1);
             if (hf == 0 && i < dk) d[i] = vc[bf][6][0] * d[i] + sum;
         }
-        // stage the next chunk into the other buffer (read last in the previous chunk)
-        if (c + 1 < p.c1) {
-            store_chunk(c + 1, bf ^ 1, kn, rn);
-            if (c + 3 < p.c1) load_chunk(c + 3, kn, rn);
-        }
     };
 
     const int c0 = p.c0, c1 = p.c1;
-    if (c1 > c0) {
-        load_chunk(c0, kA, rA);
-        if (c0 + 1 < c1) load_chunk(c0 + 1, kB, rB);
+    if (stager) {
+        if (c1 > c0) {
+            load_chunk(c0, kA, rA);
+            if (c0 + 1 < c1) load_chunk(c0 + 1, kB, rB);
+        }
         __syncthreads();  // the buffers are zeroed
-        store_chunk(c0, 0, kA, rA);
-        if (c0 + 2 < c1) load_chunk(c0 + 2, kA, rA);
+        if (c1 > c0) {
+            store_chunk(c0, 0, kA, rA);
+            if (c0 + 2 < c1) load_chunk(c0 + 2, kA, rA);
+        }
+        // beside chunk c of the chain: stage chunk c + 1 into the buffer chunk c - 1 used
+        // (free once the chain's waves reach the chunk's first barrier), from (kn, rn),
+        // which are then refilled with chunk c + 3; the chain's three barriers are matched
+        auto stage = [&](int c, u32x4 (&kn)[8], u32x4 (&rn)[5]) __attribute__((always_inline)) {
+            lds_sync();
+            if (c + 1 < c1) {
+                store_chunk(c + 1, (c + 1 - c0) & 1, kn, rn);
+                if (c + 3 < c1) load_chunk(c + 3, kn, rn);
+            }
+            lds_sync();
+            lds_sync();
+        };
+        for (int c = c0; c < c1; c += 2) {
+            stage(c, kB, rB);
+            if (c + 1 < c1) stage(c + 1, kA, rA);
+        }
+        __syncthreads();
+        return;
     }
-    for (int c = c0; c < c1; c += 2) {
-        step(c, 0, kB, rB);
-        if (c + 1 < c1) step(c + 1, 1, kA, rA);
-    }
+    __syncthreads();  // the buffers are zeroed
+    for (int c = c0; c < c1; ++c) step(c, (c - c0) & 1);
     __syncthreads();
     if (tid < dk) {
         if (c1 < p.NT) p.rec[((long)bh * p.NT + c1) * kPrWords + kPrD0 + tid] = d[tid];  // the next block's start
@@ -560,7 +579,7 @@ hipError_t launch_osdn_precond(int B, int T, int H, int dk, int io_bf16, int gat
         a.c1 = c1;
         void *args[] = {&a};
         const long grid = fn == chain_fn ? nbh : nbh * (c1 - c0);
-        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kPThreads), args, 0, s);
+        return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(fn == chain_fn ? 2 * kPThreads : kPThreads), args, 0, s);
     };
     auto finish = [&]() -> hipError_t {
         if (!qgeo) return hipSuccess;
