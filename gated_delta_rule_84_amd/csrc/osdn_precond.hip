@@ -249,7 +249,7 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
     __shared__ __attribute__((aligned(16))) float Tm[2][kPL][kPL + 4];
     __shared__ __attribute__((aligned(16))) float vc[2][7][kPL];  // c, cb, beta, r, P, rho, (Pn in [6][0])
     __shared__ __attribute__((aligned(16))) float d[kPD];
-    __shared__ float zs[kPL], we[kPL];
+    __shared__ __attribute__((aligned(16))) float zs[kPL], we[kPL];
     // waves 0-3 carry the chain; waves 4-7 ("stagers") copy the chunk after the current
     // one into the other half of the LDS double buffer, so that the chain's waves do
     // nothing between their three barriers per chunk but the chain
@@ -272,20 +272,21 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
     // (16-byte pieces) and the record head (Tm and the vectors: 1,136 pieces)
     constexpr int ksz = BF ? 2 : 4;  // bytes per key element
     const int kpieces = dk * ksz / 16;
-    u32x4 kA[8], rA[5], kB[8], rB[5];
+    constexpr int NKP = BF ? 4 : 8;  // key pieces per stager thread (64 rows of at most 128 keys)
+    u32x4 kA[NKP], rA[5], kB[NKP], rB[5];
     // this thread's key pieces (row, 16-byte piece) are the same in every chunk
-    int prow[8], ppc[8];
+    int prow[NKP], ppc[NKP];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < NKP; ++u) {
         const int e = tid + kPThreads * u;
         prow[u] = e / kpieces;
         ppc[u] = e - prow[u] * kpieces;
     }
-    auto load_chunk = [&](int c, u32x4 (&kreg)[8], u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+    auto load_chunk = [&](int c, u32x4 (&kreg)[NKP], u32x4 (&rreg)[5]) __attribute__((always_inline)) {
         const int t0 = c * kPL, n = min(kPL, p.T - t0);
         const char *kb = static_cast<const char *>(p.k);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {  // unconditional (rows clamped): the compiler counts them
+        for (int u = 0; u < NKP; ++u) {  // unconditional (rows clamped): the compiler counts them
             const int t = min(prow[u], n - 1);
             kreg[u] = *reinterpret_cast<const u32x4 *>(kb + ((((long)b * p.T + t0 + t) * p.H + h) * dk) * ksz + 16 * ppc[u]);
         }
@@ -296,10 +297,11 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
             rreg[u] = *reinterpret_cast<const u32x4 *>(rec + 4 * w4);
         }
     };
-    auto store_chunk = [&](int c, int bf, const u32x4 (&kreg)[8], const u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+    // the keys of chunk c into buffer bf as k^2, and the record head
+    auto store_keys = [&](int c, int bf, const u32x4 (&kreg)[NKP]) __attribute__((always_inline)) {
         const int t0 = c * kPL, n = min(kPL, p.T - t0);
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < NKP; ++u) {
             const int t = prow[u], pc = ppc[u];
             const int row = min(t, kPL);
             const bool live = t < n;
@@ -328,8 +330,10 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
                 *reinterpret_cast<f32x4 *>(&kf[bf][row][4 * pc]) = v;
             }
         }
-        // the record head: Tm rows then the vector rows; the clamped duplicate pieces
-        // rewrite the last piece with its own value
+    };
+    auto store_rec = [&](int bf, const u32x4 (&rreg)[5]) __attribute__((always_inline)) {
+        // Tm rows then the vector rows; the clamped duplicate pieces rewrite the last
+        // piece with its own value
 #pragma unroll
         for (int u = 0; u < 5; ++u) {
             const int w = 4 * min(tid + kPThreads * u, kPrD0 / 4 - 1);
@@ -361,15 +365,20 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
             if (part == 0) zs[t] = vc[bf][0][t] - vc[bf][1][t] * vc[bf][4][t] * sum;
         }
         lds_sync();
-        // e = Tm z
+        // e = Tm z  (4 lanes per token, 16 columns each, 16-byte reads)
         {
             const int t = tid >> 2, part = tid & 3;
-            float sum = 0.f;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int jj = 0; jj < 16; ++jj) {
-                const int j = 16 * part + jj;  // strictly lower part of Tm (its diagonal is 1)
-                sum = fmaf(j < t ? Tm[bf][t][j] : 0.f, zs[j], sum);
+            for (int m = 0; m < 4; ++m) {
+                const int j0 = 16 * part + 4 * m;
+                const f32x4 tv = *reinterpret_cast<const f32x4 *>(&Tm[bf][t][j0]);
+                const f32x4 zv = *reinterpret_cast<const f32x4 *>(&zs[j0]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x)  // strictly lower part of Tm (its diagonal is 1)
+                    s4[x] = fmaf(j0 + x < t ? tv[x] : 0.f, zv[x], s4[x]);
             }
+            float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
             sum += __shfl_xor(sum, 1);
             sum += __shfl_xor(sum, 2);
             if (part == 0) {
@@ -378,18 +387,34 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
             }
         }
         lds_sync();
-        // d_n = P_n d_0 + sum_j rho_j e_j a_j: two lanes per key channel, even and odd j
+        // d_n = P_n d_0 + sum_j rho_j e_j a_j: lane (j group g, channel quad m) sums the
+        // tokens j = 8 g .. 8 g + 7 for channels 4 m .. 4 m + 3 (16-byte reads); the eight
+        // j groups of a quad are adjacent lanes
         {
-            const int i = tid >> 1, hf = tid & 1;
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+            const int g = tid & 7, m = tid >> 3;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 w0 = *reinterpret_cast<const f32x4 *>(&we[8 * g]);
+            const f32x4 w1 = *reinterpret_cast<const f32x4 *>(&we[8 * g + 4]);
 #pragma unroll
-            for (int jj = 0; jj < kPL / 2; ++jj) {
-                const int j = 2 * jj + hf;
-                acc[jj & 3] = fmaf(we[j], kf[bf][j][i], acc[jj & 3]);
+            for (int jj = 0; jj < 8; ++jj) {
+                const f32x4 av = *reinterpret_cast<const f32x4 *>(&kf[bf][8 * g + jj][4 * m]);
+                const float wj = jj < 4 ? w0[jj] : w1[jj - 4];
+#pragma unroll
+                for (int x = 0; x < 4; ++x) acc[x] = fmaf(wj, av[x], acc[x]);
             }
-            float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-            sum += __shfl_xor(sum, 1);
-            if (hf == 0 && i < dk) d[i] = vc[bf][6][0] * d[i] + sum;
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                acc[x] += __shfl_xor(acc[x], 1);
+                acc[x] += __shfl_xor(acc[x], 2);
+                acc[x] += __shfl_xor(acc[x], 4);
+            }
+            if (g == 0 && 4 * m < dk) {
+                const float pn = vc[bf][6][0];
+                f32x4 dv = *reinterpret_cast<const f32x4 *>(&d[4 * m]);
+#pragma unroll
+                for (int x = 0; x < 4; ++x) dv[x] = pn * dv[x] + acc[x];
+                *reinterpret_cast<f32x4 *>(&d[4 * m]) = dv;
+            }
         }
     };
 
@@ -401,20 +426,21 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
         }
         __syncthreads();  // the buffers are zeroed
         if (c1 > c0) {
-            store_chunk(c0, 0, kA, rA);
+            store_keys(c0, 0, kA);
+            store_rec(0, rA);
             if (c0 + 2 < c1) load_chunk(c0 + 2, kA, rA);
         }
         // beside chunk c of the chain: stage chunk c + 1 into the buffer chunk c - 1 used
-        // (free once the chain's waves reach the chunk's first barrier), from (kn, rn),
-        // which are then refilled with chunk c + 3; the chain's three barriers are matched
-        auto stage = [&](int c, u32x4 (&kn)[8], u32x4 (&rn)[5]) __attribute__((always_inline)) {
+        // (free once the chain's waves reach the chunk's first barrier) from (kn, rn), the
+        // keys and the record head in the chain's first two barrier intervals, then refill
+        // (kn, rn) with chunk c + 3; the chain's three barriers are matched
+        auto stage = [&](int c, u32x4 (&kn)[NKP], u32x4 (&rn)[5]) __attribute__((always_inline)) {
             lds_sync();
-            if (c + 1 < c1) {
-                store_chunk(c + 1, (c + 1 - c0) & 1, kn, rn);
-                if (c + 3 < c1) load_chunk(c + 3, kn, rn);
-            }
+            if (c + 1 < c1) store_keys(c + 1, (c + 1 - c0) & 1, kn);
             lds_sync();
+            if (c + 1 < c1) store_rec((c + 1 - c0) & 1, rn);
             lds_sync();
+            if (c + 3 < c1) load_chunk(c + 3, kn, rn);
         };
         for (int c = c0; c < c1; c += 2) {
             stage(c, kB, rB);
