@@ -741,14 +741,14 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
         }
     };
 
-    f32x4 S[8];  // chain waves: S[kt][i] = S[16 kt + 4 q + i][cw + r]
+    f32x4 S[8];          // chain waves: S[kt][i] = S[skey(kt, q, i)][cw + r]
+    u32x4 sfh[4], sfl[4];  // chain waves: the state's B fragments (two bf16 terms), kept for Y
     auto publish_state = [&]() __attribute__((always_inline)) {
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) {
-            u32x4 hi, lo;
-            split_frag(S[2 * kk], S[2 * kk + 1], hi, lo);
-            sm.Sx[w][2 * kk][l] = hi;
-            sm.Sx[w][2 * kk + 1][l] = lo;
+            split_frag(S[2 * kk], S[2 * kk + 1], sfh[kk], sfl[kk]);
+            sm.Sx[w][2 * kk][l] = sfh[kk];
+            sm.Sx[w][2 * kk + 1][l] = sfl[kk];
         }
     };
     if (chain) {
@@ -776,28 +776,23 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
         const WsBuf &B = sm.buf[bb];
         const int t0 = c * kC, n = min(kC, p.T - t0);
         if (chain) {
-            // Y = K S (S as two bf16 terms)
+            // Y = K S (S as two bf16 terms, the fragments this wave split last)
             f32x4 Y[4];
             {
-                u32x4 ka[4][4], sh[4], sl[4];
+                u32x4 ka[4][4];
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                     for (int tt = 0; tt < 4; ++tt) ka[kk][tt] = frag_row(B.K, 16 * tt + r, kk, q);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) {
-                    sh[kk] = sm.Sx[w][2 * kk][l];
-                    sl[kk] = sm.Sx[w][2 * kk + 1][l];
-                }
-#pragma unroll
                 for (int tt = 0; tt < 4; ++tt) Y[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sh[kk]), Y[tt]);
-                        Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sl[kk]), Y[tt]);
-                    }
+                    for (int tt = 0; tt < 4; ++tt) Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sfh[kk]), Y[tt]);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) Y[tt] = mfma(as_bf16x8(ka[kk][tt]), as_bf16x8(sfl[kk]), Y[tt]);
+                }
             }
             // R = V - gamma_t Y (rows past the chunk end zeroed)
             u32x4 rh[2], rl[2];
@@ -806,9 +801,10 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) {
                     const f32x4 gam = *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
-                    f32x4 vf;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) vf[i] = bf16_to_f32(sm.V[16 * tt + 4 * q + i][16 * w + r]);
+                    // lane (r, q) receives column r of rows 16 tt + 4 q .. + 3
+                    const u32x2 v4 = ld_tr(&sm.V[16 * tt + 4 * q + (r >> 2)][16 * w + 4 * (r & 3)]);
+                    const f32x4 vf = {__uint_as_float(v4.x << 16), __uint_as_float(v4.x & 0xffff0000u),
+                                      __uint_as_float(v4.y << 16), __uint_as_float(v4.y & 0xffff0000u)};
                     R[tt] = vf - gam * Y[tt];
                 }
                 if (n < kC) {
