@@ -114,6 +114,47 @@ __device__ __forceinline__ int pcol(int s) { return (s & 32) | ((s & 12) << 1) |
 __device__ __forceinline__ int pcol_inv(int c) { return (c & 32) | ((c & 4) << 2) | ((c & 24) >> 1) | (c & 3); }
 
 
+// fp32 x = hi + lo, both bf16 round-to-nearest-even, packed four to a u32x2.
+__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
+    const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
+    hi = u32x2{h0, h1};
+    lo = u32x2{pk_bf16(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u)),
+               pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u))};
+}
+
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
+
+// two C tiles (rows 4q..4q+3 of each) -> one B fragment as two bf16 terms
+__device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
+    u32x2 ha, la, hb, lb;
+    split4(a, ha, la);
+    split4(b, hb, lb);
+    hi = cat(ha, hb);
+    lo = cat(la, lb);
+}
+
+// Inclusive prefix sum (x) and prefix maximum (z) over the 64 lanes of a wave with DPP:
+// shifts by 1, 2, 4 and 8 inside each row of 16 lanes, then the row totals carried by
+// the broadcasts of lanes 15 (to rows 1 and 3) and 31 (to rows 2 and 3).  Lanes with no
+// source take the identity (0 for the sum, -1 for the maximum).  All 64 lanes active.
+__device__ __forceinline__ void wave_scan_sum_max(float &x, int &z) {
+#define GDR_SCAN_STEP(ctrl, rmask)                                                                          \
+    {                                                                                                       \
+        const float y = __builtin_bit_cast(                                                                 \
+            float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, rmask, 0xf, false));   \
+        const int zy = __builtin_amdgcn_update_dpp(-1, z, ctrl, rmask, 0xf, false);                         \
+        x += y;                                                                                             \
+        z = max(z, zy);                                                                                     \
+    }
+    GDR_SCAN_STEP(0x111, 0xf)  // row_shr:1
+    GDR_SCAN_STEP(0x112, 0xf)  // row_shr:2
+    GDR_SCAN_STEP(0x114, 0xf)  // row_shr:4
+    GDR_SCAN_STEP(0x118, 0xf)  // row_shr:8
+    GDR_SCAN_STEP(0x142, 0xa)  // row_bcast:15
+    GDR_SCAN_STEP(0x143, 0xc)  // row_bcast:31
+#undef GDR_SCAN_STEP
+}
+
 // Workgroup barrier ordered for LDS only: the fences are restricted to the local
 // address space, so the barrier waits for this wave's LDS traffic but not for its
 // outstanding global loads into registers, which stay in flight across it.  Copies
@@ -167,10 +208,8 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     __shared__ float gl[kC], bl[kC];
     __shared__ int zl[kC];
     __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part (first: the write keys)
-    __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform; first holds the two P terms
+    __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform (first: the keys, when a separate tensor)
     __shared__ __align__(16) float Xs[4][16][16];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
-    uint16_t(*Ph)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[0][0]);
-    uint16_t(*Pl)[kC + 8] = reinterpret_cast<uint16_t(*)[kC + 8]>(&Ts[kC / 2][0]);
 
     const int blk = blockIdx.x, nc = p.c1 - p.c0;  // chunks c0 .. c1 - 1 of every (batch, head)
     const int c = p.c0 + blk % nc, bh = blk / nc;
@@ -227,7 +266,7 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
         for (int kk = 0; kk < 4; ++kk) {
             const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&KWs[16 * J + r][8 * ((4 * kk + q) ^ r)]));
             if (J <= IG) accG[J] = mfma(as_bf16x8(ka[kk]), kb, accG[J]);
-            if (J <= IP) accP[J] = mfma(as_bf16x8(qa[kk]), kb, accP[J]);
+            if (J <= IP) accP[J] = mfma(kb, as_bf16x8(qa[kk]), accP[J]);  // scores transposed
         }
     }
     // cumulative log decay and beta (wave 0), segmented at zero gates: P_t sums log alpha
@@ -240,15 +279,7 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
         float la = (l < n && !zero) ? logf(a_raw) : 0.f;
         int z = zero ? l : -1;
         const float be = l < n ? b_raw : 0.f;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const float y = __shfl_up(la, off);
-            const int zy = __shfl_up(z, off);
-            if (l >= off) {
-                la += y;
-                z = max(z, zy);
-            }
-        }
+        wave_scan_sum_max(la, z);
         gl[l] = la;
         zl[l] = z;
         bl[l] = be;
@@ -256,46 +287,55 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
 
     __syncthreads();
 
-    // decay / beta weights; Gram to LDS (fp32), scores to LDS as two bf16 terms.
-    // Every LDS read is hoisted ahead of the stores so none waits behind them.
-    float gG[4], gP[4], gS[4], bS[4];
-    int zG[4], zP[4];
+    // decay / beta weights; Gram to LDS (fp32).  Every LDS read is hoisted ahead of the
+    // stores so none waits behind them.  The exponent is clamped at 0, which changes
+    // only entries the masks discard (g decreases in t).
+    char *rec = static_cast<char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
+    float gG[4], gS[4], bS[4], gQ[4][4], bQ[4][4];
+    int zG[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         gG[i] = gl[16 * IG + 4 * q + i];
-        gP[i] = gl[16 * IP + 4 * q + i];
         zG[i] = zl[16 * IG + 4 * q + i];
-        zP[i] = zl[16 * IP + 4 * q + i];
         gS[i] = gl[16 * i + r];
         bS[i] = bl[16 * i + r];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            gQ[J][i] = gl[16 * J + 4 * q + i];
+            bQ[J][i] = bl[16 * J + 4 * q + i];
+        }
     }
+    const int tP = 16 * IP + r;  // the scores' token row of this lane
+    const float gt = gl[tP];
+    const int zt = zl[tP];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
+        if (J <= IG) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * J + r;
-            // computed for every lane and selected (no divergent branch); the exponent is
-            // clamped at 0, which changes only entries the mask discards (g decreases in t)
-            if (J <= IG) {
-                const int t = 16 * IG + 4 * q + i;
+            for (int i = 0; i < 4; ++i) {
+                const int s = 16 * J + r, t = 16 * IG + 4 * q + i;
                 const float v = accG[J][i] * bS[J] * __expf(fminf(gG[i] - gS[J], 0.f));
                 As[t][s] = (s < t && t < n && zG[i] <= s) ? v : 0.f;
             }
-            const int tp = 16 * IP + 4 * q + i;
-            float pv = 0.f;
-            if (J <= IP) {
-                const float v = accP[J][i] * bS[J] * __expf(fminf(gP[i] - gS[J], 0.f));
-                pv = (s <= tp && tp < n && zP[i] <= s) ? v : 0.f;
-            }
-            const __bf16 hi = (__bf16)pv;
-            const __bf16 lo = (__bf16)(pv - (float)hi);
-            Ph[tp][pcol(s)] = __builtin_bit_cast(uint16_t, hi);
-            Pl[tp][pcol(s)] = __builtin_bit_cast(uint16_t, lo);
+        }
+        // scores: lane (r, q) holds P[tP][s] for s = 16 J + 4 q + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * J + 4 * q + i;
+            const float v = accP[J][i] * bQ[J][i] * __expf(fminf(gt - gQ[J][i], 0.f));
+            accP[J][i] = (J <= IP && s <= tP && tP < n && zt <= s) ? v : 0.f;
         }
     }
-    __syncthreads();
-    char *rec = static_cast<char *>(p.ws) + ((long)bh * NT + c) * kRecBytes;
-    store_p(rec + kRecPhi, rec + kRecPlo, Ph, Pl, tid);
+    // P to the record in the pcol column order straight from the C tiles: tiles 2 kk and
+    // 2 kk + 1 give this lane the stored columns 32 kk + 8 q .. + 7 of row tP, as two bf16
+    // terms (16 bytes each)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+        u32x4 hi, lo;
+        split_frag(accP[2 * kk], accP[2 * kk + 1], hi, lo);
+        *reinterpret_cast<u32x4 *>(rec + kRecPhi + 2 * (tP * kC + 32 * kk + 8 * q)) = hi;
+        *reinterpret_cast<u32x4 *>(rec + kRecPlo + 2 * (tP * kC + 32 * kk + 8 * q)) = lo;
+    }
     __syncthreads();
 
     ut_transform(As, Ts, Xs, w, l);
@@ -573,13 +613,6 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
     store_ut(rec + kRcT, Ts, tid);
 }
 
-// fp32 x = hi + lo, both bf16 round-to-nearest-even, packed four to a u32x2.
-__device__ __forceinline__ void split4(f32x4 x, u32x2 &hi, u32x2 &lo) {
-    const uint32_t h0 = pk_bf16(x[0], x[1]), h1 = pk_bf16(x[2], x[3]);
-    hi = u32x2{h0, h1};
-    lo = u32x2{pk_bf16(x[0] - __uint_as_float(h0 << 16), x[1] - __uint_as_float(h0 & 0xffff0000u)),
-               pk_bf16(x[2] - __uint_as_float(h1 << 16), x[3] - __uint_as_float(h1 & 0xffff0000u))};
-}
 
 // ---------------------------------------------------------------------------
 // state kernel, wave-specialised form
@@ -639,16 +672,6 @@ __device__ __forceinline__ u32x2 ld_tr(const uint16_t *p) {
     return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t)(p)));
 }
 
-__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
-
-// two C tiles (rows 4q..4q+3 of each) -> one B fragment as two bf16 terms
-__device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, u32x4 &hi, u32x4 &lo) {
-    u32x2 ha, la, hb, lb;
-    split4(a, ha, la);
-    split4(b, hb, lb);
-    hi = cat(ha, hb);
-    lo = cat(la, lb);
-}
 
 // Fragment of row t (lane row r) of a key-width tile, k step kk: keys 32 kk + 8 q .. + 7
 // (the state's key order, skey)
