@@ -332,8 +332,8 @@ def progress(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
 
-def time_prefill(g, gi, w, x, steps, warmup, stream, digest, cold=False):
-    """`steps` gdr_chunk_fwd calls back to back between one pair of HIP events on the
+def time_prefill(g, gi, w, x, steps, warmup, stream, digest, cold=False, use_ctx=True):
+    """`steps` gdr_chunk_fwd_ctx calls (gdr_chunk_fwd without `use_ctx`) back to back between one pair of HIP events on the
     launch stream after `warmup` untimed calls (an event pair around every call would
     add its own few microseconds per call); with `cold`, also the median of 5 calls
     after flushing L2 and the Infinity Cache.  Returns times and the roofline."""
@@ -348,12 +348,19 @@ def time_prefill(g, gi, w, x, steps, warmup, stream, digest, cold=False):
     ST = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
     wsz = g.gdr_chunk_fwd_workspace_size(desc)
     ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+    # with few (batch, head) pairs and a long sequence the prep of later chunk blocks runs
+    # on the context's stream beside the state recurrence; other shapes ignore it
+    ctx = g.Context() if use_ctx else None
 
     def step():
-        rc = g.gdr_chunk_fwd(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"], d["beta_v"],
-                             d["S0"], o, ST, ws, wsz, stream)
+        if ctx is None:
+            rc = g.gdr_chunk_fwd(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"], d["beta_v"],
+                                 d["S0"], o, ST, ws, wsz, stream)
+        else:
+            rc = g.gdr_chunk_fwd_ctx(desc, d["q"], d["k"], d["k_w"], d["v"], d["alpha"], d["beta_k"],
+                                     d["beta_v"], d["S0"], o, ST, ws, wsz, ctx, stream)
         if rc != g.GDR_OK:
-            raise g.GdrError(rc, "gdr_chunk_fwd")
+            raise g.GdrError(rc, "gdr_chunk_fwd" if ctx is None else "gdr_chunk_fwd_ctx")
 
     for _ in range(warmup):
         step()

@@ -49,6 +49,8 @@ _lib.gdr_chunk_fwd_workspace_size.argtypes = [_dp]
 _lib.gdr_chunk_fwd_workspace_size.restype = ctypes.c_size_t
 _lib.gdr_chunk_fwd.argtypes = [_dp] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp]
 _lib.gdr_chunk_fwd.restype = ctypes.c_int
+_lib.gdr_chunk_fwd_ctx.argtypes = [_dp] + [_vp] * 10 + [_vp, ctypes.c_size_t, _vp, _vp]
+_lib.gdr_chunk_fwd_ctx.restype = ctypes.c_int
 _lib.gdr_chunk_fwd_noalloc.argtypes = [_dp] + [_vp] * 10 + [_vp]
 _lib.gdr_chunk_fwd_noalloc.restype = ctypes.c_int
 _lib.gdr_decode_step.argtypes = [_dp] + [_vp] * 9 + [_vp]
@@ -86,7 +88,7 @@ EXPORTED = ("gdr_chunk_fwd_workspace_size", "gdr_chunk_fwd", "gdr_decode_step", 
             "gdr_status_string", "gdr_version", "gdr_chunk_fwd_ckpt", "gdr_mc_readout_workspace_size",
             "gdr_mc_readout", "gdr_osdn_precond_workspace_size", "gdr_osdn_precond",
             "gdr_sdm_workspace_size", "gdr_sdm_fwd", "gdr_context_create", "gdr_context_destroy",
-            "gdr_chunk_fwd_noalloc", "gdr_dmem_fwd")
+            "gdr_chunk_fwd_noalloc", "gdr_dmem_fwd", "gdr_chunk_fwd_ctx")
 
 
 class GdrError(RuntimeError):
@@ -244,6 +246,15 @@ def gdr_chunk_fwd(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, wo
                                   _ptr(workspace), int(workspace_bytes), _stream(stream)))
 
 
+def gdr_chunk_fwd_ctx(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace,
+                      workspace_bytes: int, ctx, stream=None) -> int:
+    _check_all(_prefill_specs(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST))
+    _check_workspace(workspace, workspace_bytes)
+    return int(_lib.gdr_chunk_fwd_ctx(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
+                                      _ptr(beta_k), _ptr(beta_v), _ptr(S0), _ptr(o), _ptr(ST),
+                                      _ptr(workspace), int(workspace_bytes), _ctx(ctx), _stream(stream)))
+
+
 def gdr_chunk_fwd_noalloc(desc: Desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, stream=None) -> int:
     _check_all(_prefill_specs(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST))
     return int(_lib.gdr_chunk_fwd_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(k_w), _ptr(v), _ptr(alpha),
@@ -374,8 +385,9 @@ def make_desc(q, v, alpha, beta_k, beta_v=None, *, chunk=64, decode=False, flags
 
 
 def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=64, want_state=True,
-              out=None, final_state=None, workspace=None, stream=None):
-    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None)."""
+              out=None, final_state=None, workspace=None, ctx=None, stream=None):
+    """Prefill.  Returns (o [B, T, H, dv] in q's dtype, ST [B, H, dk, dv] fp32 or None).
+    With an execution context `ctx` the call goes through gdr_chunk_fwd_ctx."""
     desc = make_desc(q, v, alpha, beta_k, beta_v, chunk=chunk)
     o = out if out is not None else torch.empty(q.shape[:-1] + (v.shape[-1],), dtype=q.dtype, device=q.device)
     ST = final_state
@@ -385,9 +397,12 @@ def chunk_fwd(q, k, v, alpha, beta_k, *, k_w=None, beta_v=None, S0=None, chunk=6
     if need and (workspace is None or workspace.numel() * workspace.element_size() < need):
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    rc = gdr_chunk_fwd(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace, wbytes, stream)
+    if ctx is None:
+        rc = gdr_chunk_fwd(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace, wbytes, stream)
+    else:
+        rc = gdr_chunk_fwd_ctx(desc, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, workspace, wbytes, ctx, stream)
     if rc != GDR_OK:
-        raise GdrError(rc, "gdr_chunk_fwd")
+        raise GdrError(rc, "gdr_chunk_fwd" if ctx is None else "gdr_chunk_fwd_ctx")
     return o, ST
 
 

@@ -1368,53 +1368,94 @@ size_t chunk_mfma_workspace(const ChunkParams &p) {
     return (size_t)p.B * p.H * NT * (general_gates(p) ? kRcBytes : kRecBytes);
 }
 
-hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t st) {
+// Chunk blocks of the prefill given an execution context (below): at least this many
+// chunks per block, at most kMaxPrepBlocks blocks.
+constexpr int kPrepBlockChunks = 128;
+constexpr int kMaxPrepBlocks = 16;
+static_assert(2 + kMaxPrepBlocks <= kCtxEvents, "one context event per block");
+
+hipError_t launch_chunk_mfma(const ChunkParams &p, const gdr_context *ctx, hipStream_t st) {
     const long nbh = (long)p.B * p.H;
     const int NT = (p.T + kC - 1) / kC;
     if (nbh == 0 || NT == 0) return hipSuccess;
-    ChunkParams arg = p;
-    arg.c0 = 0;
-    arg.c1 = NT;
+    const long groups = (nbh + 7) / 8;
+    const bool gen = general_gates(p);
+    const bool g16 = p.gate_bf16 != 0, ach = p.alpha_ch != 0, bvec = p.beta_mode != 0;
     int nt = NT;
     int nb = (int)nbh;
-    const long groups = (nbh + 7) / 8;
-    if (general_gates(p)) {
-        const bool g16 = p.gate_bf16 != 0, ach = p.alpha_ch != 0, bvec = p.beta_mode != 0;
-        // prep: <GBF16, ACH, BVEC>
-        const void *preps[8] = {
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, false>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, true>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, false>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, true>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, false>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, true>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, false>),
-            reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, true>)};
-        void *pargs[] = {&arg, &nt};
-        const hipError_t e = hipLaunchKernel(preps[(g16 ? 4 : 0) + (ach ? 2 : 0) + (bvec ? 1 : 0)],
-                                             dim3((unsigned)(nbh * NT)), dim3(kThreads), pargs, 0, st);
-        if (e != hipSuccess) return e;
-        // state: <VSCALE, GBF16>
-        const void *states[4] = {reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, false>),
-                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, true>),
-                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, false>),
-                                 reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, true>)};
-        void *sargs[] = {&arg, &nt, &nb};
-        return hipLaunchKernel(states[(bvec ? 2 : 0) + (g16 ? 1 : 0)], dim3((unsigned)(groups * 8 * (kD / kCW))),
-                               dim3(256), sargs, 0, st);
-    }
-    const bool sep = p.kw != p.k;
-    const void *ws_fn = sep ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
-                            : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
-    {
+    // the prep of chunks c0 .. c1 - 1 of every (batch, head)
+    auto prep = [&](int c0, int c1, hipStream_t s) -> hipError_t {
+        ChunkParams arg = p;
+        arg.c0 = c0;
+        arg.c1 = c1;
         void *args[] = {&arg, &nt};
-        const void *prep = p.gate_bf16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
-                                       : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
-        const hipError_t e = hipLaunchKernel(prep, dim3((unsigned)(nbh * NT)), dim3(kThreads), args, 0, st);
-        if (e != hipSuccess) return e;
+        const void *fn;
+        if (gen) {
+            // <GBF16, ACH, BVEC>
+            const void *preps[8] = {
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, false>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, false, true>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, false>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<false, true, true>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, false>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, false, true>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, false>),
+                reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, true>)};
+            fn = preps[(g16 ? 4 : 0) + (ach ? 2 : 0) + (bvec ? 1 : 0)];
+        } else {
+            fn = g16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
+                     : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
+        }
+        return hipLaunchKernel(fn, dim3((unsigned)(nbh * (c1 - c0))), dim3(kThreads), args, 0, s);
+    };
+    // the state recurrence over chunks c0 .. c1 - 1, entering with S0
+    auto state = [&](int c0, int c1, const float *S0) -> hipError_t {
+        ChunkParams arg = p;
+        arg.c0 = c0;
+        arg.c1 = c1;
+        arg.S0 = S0;
+        void *args[] = {&arg, &nt, &nb};
+        const void *fn;
+        if (gen) {
+            // <VSCALE, GBF16>
+            const void *states[4] = {reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, false>),
+                                     reinterpret_cast<const void *>(&gdr_state_chan_kernel<false, true>),
+                                     reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, false>),
+                                     reinterpret_cast<const void *>(&gdr_state_chan_kernel<true, true>)};
+            fn = states[(bvec ? 2 : 0) + (g16 ? 1 : 0)];
+        } else {
+            fn = p.kw != p.k ? reinterpret_cast<const void *>(&gdr_state_ws_kernel<true>)
+                             : reinterpret_cast<const void *>(&gdr_state_ws_kernel<false>);
+        }
+        return hipLaunchKernel(fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(256), args, 0, st);
+    };
+    hipError_t e;
+    // With an execution context, a long sequence with scalar gates whose state kernel
+    // leaves CUs idle (one workgroup per CU and head column block: fewer than 64 (batch,
+    // head) pairs) and whose final state is written is cut into chunk blocks: the prep of
+    // every block runs on the context's second stream while the state recurrence walks
+    // the blocks in order on the caller's stream, one launch per block, each entering with
+    // the state the launch before left in ST and waiting only for its own block's prep.
+    const int nblk = (ctx && p.ST && !gen && nbh < 64) ? min(kMaxPrepBlocks, NT / kPrepBlockChunks) : 1;
+    if (nblk <= 1) {
+        if ((e = prep(0, NT, st)) != hipSuccess) return e;
+        return state(0, NT, p.S0);
     }
-    void *args[] = {&arg, &nt, &nb};
-    return hipLaunchKernel(ws_fn, dim3((unsigned)(groups * 8 * (kD / kCW))), dim3(256), args, 0, st);
+    hipStream_t side = ctx->stream;
+    const hipEvent_t fork = ctx->ev[0], *solved = ctx->ev + 2;
+    auto bound = [&](int j) { return (int)((long)NT * j / nblk); };
+    if ((e = hipEventRecord(fork, st)) != hipSuccess) return e;  // inputs ready on st
+    if ((e = hipStreamWaitEvent(side, fork, 0)) != hipSuccess) return e;
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = prep(bound(j), bound(j + 1), side)) != hipSuccess) return e;
+        if ((e = hipEventRecord(solved[j], side)) != hipSuccess) return e;
+    }
+    // the last wait also joins the second stream back into st
+    for (int j = 0; j < nblk; ++j) {
+        if ((e = hipStreamWaitEvent(st, solved[j], 0)) != hipSuccess) return e;
+        if ((e = state(bound(j), bound(j + 1), j == 0 ? p.S0 : p.ST)) != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gdr

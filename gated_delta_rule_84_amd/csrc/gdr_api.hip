@@ -171,12 +171,14 @@ size_t gdr_chunk_fwd_workspace_size(const gdr_desc *d) {
     return select_path(d, p) == 1 ? chunk_mfma_workspace(p) : 0;
 }
 
-int gdr_chunk_fwd_ckpt(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
-                       const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
-                       void *o, float *ST, int32_t seg_len, float *ckpt, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+// Prefill shared by gdr_chunk_fwd, gdr_chunk_fwd_ckpt and gdr_chunk_fwd_ctx.
+static int chunk_fwd_impl(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                          const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                          void *o, float *ST, int32_t seg_len, float *ckpt, void *workspace,
+                          size_t workspace_bytes, const gdr_context *ctx, void *stream) {
     int rc = check_desc(d, true);
     if (rc) return rc;
+    if (!context_ok(ctx)) return GDR_EINVAL;
     ChunkParams p = chunk_params(d);
     if (seg_len <= 0 || seg_len % d->chunk) return GDR_EINVAL;
     const int nck = d->T / seg_len;
@@ -248,8 +250,25 @@ int gdr_chunk_fwd_ckpt(const gdr_desc *d, const void *q, const void *k, const vo
         p.seg_chunks = seg_len / d->chunk;
         p.nck = nck;
     }
-    const hipError_t e = path == 1 ? launch_chunk_mfma(p, st) : launch_chunk_valu(p, st);
+    const hipError_t e = path == 1 ? launch_chunk_mfma(p, ctx, st) : launch_chunk_valu(p, st);
     return e == hipSuccess ? GDR_OK : GDR_EHIP;
+}
+
+int gdr_chunk_fwd_ckpt(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                       const void *alpha, const void *beta_k, const void *beta_v, const float *S0,
+                       void *o, float *ST, int32_t seg_len, float *ckpt, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    return chunk_fwd_impl(d, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg_len, ckpt, workspace,
+                          workspace_bytes, nullptr, stream);
+}
+
+int gdr_chunk_fwd_ctx(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,
+                      const void *alpha, const void *beta_k, const void *beta_v, const float *S0, void *o,
+                      float *ST, void *workspace, size_t workspace_bytes, const gdr_context *ctx, void *stream) {
+    // no segment ends are kept: a segment longer than any T
+    const int32_t seg = d && d->chunk > 0 ? (0x7fffffff / d->chunk) * d->chunk : 1;
+    return chunk_fwd_impl(d, q, k, k_w, v, alpha, beta_k, beta_v, S0, o, ST, seg, nullptr, workspace,
+                          workspace_bytes, ctx, stream);
 }
 
 int gdr_chunk_fwd(const gdr_desc *d, const void *q, const void *k, const void *k_w, const void *v,

@@ -69,7 +69,7 @@ hipError_t launch_dmem(const DmemParams &p, hipStream_t s);
 hipError_t launch_chunk_valu(const ChunkParams &p, hipStream_t s);
 size_t chunk_mfma_workspace(const ChunkParams &p);
 bool chunk_mfma_supported(const ChunkParams &p);
-hipError_t launch_chunk_mfma(const ChunkParams &p, hipStream_t s);
+hipError_t launch_chunk_mfma(const ChunkParams &p, const gdr_context *ctx, hipStream_t s);
 hipError_t launch_state_copy(const float *S0, float *ST, long n, hipStream_t s);
 size_t mc_readout_workspace(int B, int H, int N);
 size_t osdn_precond_workspace(int B, int T, int H);

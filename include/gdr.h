@@ -33,10 +33,10 @@
  *     allocates no device memory, keeps no pointer after a call returns and has no
  *     global mutable state beyond the per-device address of gdr_chunk_fwd_noalloc's
  *     static scratch array (looked up once, under a lock), so calls from several
- *     host threads are safe (gdr_chunk_fwd_noalloc: see its own rule).  The two
- *     calls that can overlap independent work on a second stream (gdr_osdn_precond,
- *     gdr_sdm_fwd) take it from a caller-owned gdr_context (below); with a NULL
- *     context they run everything on `stream`.
+ *     host threads are safe (gdr_chunk_fwd_noalloc: see its own rule).  The calls
+ *     that can overlap independent work on a second stream (gdr_chunk_fwd_ctx,
+ *     gdr_osdn_precond, gdr_sdm_fwd) take it from a caller-owned gdr_context (below);
+ *     with a NULL context they run everything on `stream`.
  *   - Every tensor is dense and row-major.  q, k, k_w, v, o and the fp32 states
  *     must be 16-byte aligned; alpha, beta_k, beta_v need only their element
  *     alignment (so per-step slices of a gate array are accepted).
@@ -159,6 +159,23 @@ int gdr_chunk_fwd(const gdr_desc *desc, const void *q, const void *k, const void
                   const void *v, const void *alpha, const void *beta_k, const void *beta_v,
                   const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
                   void *stream);
+
+/*
+ * Prefill given an execution context: the arguments, results (bit for bit) and
+ * workspace of gdr_chunk_fwd, plus `ctx` (NULL: exactly gdr_chunk_fwd).  The chunked
+ * pass of the same pages; what the context changes is only where the work runs.
+ * With a context, a call on the scalar-gate matrix-core path (scalar alpha and beta)
+ * with fewer than 64 (b, h) pairs, at least 256 chunks per sequence and ST != NULL is
+ * cut into blocks of chunks: the per-chunk preparation of every block runs on the
+ * context's second stream while the state recurrence, which then occupies fewer than
+ * all compute units, walks the blocks in order on `stream`, each block entering with the
+ * state the block before left in ST.  Any other call runs on `stream` alone.
+ * GDR_EINVAL also for a context created on another device.
+ */
+int gdr_chunk_fwd_ctx(const gdr_desc *desc, const void *q, const void *k, const void *k_w,
+                      const void *v, const void *alpha, const void *beta_k, const void *beta_v,
+                      const float *S0, void *o, float *ST, void *workspace, size_t workspace_bytes,
+                      const gdr_context *ctx, void *stream);
 
 /*
  * Prefill with no workspace argument and no allocation, for callers that cannot

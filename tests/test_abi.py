@@ -84,6 +84,7 @@ def test_descriptor_validation(g, field, value, status):
     d = _desc(g, **{field: value})
     q, k, v, a, b, o, st = _ptrs(n=7)
     assert g.gdr_chunk_fwd(d, q, k, None, v, a, b, None, None, o, st, None, 0, 0) == status
+    assert g.gdr_chunk_fwd_ctx(d, q, k, None, v, a, b, None, None, o, st, None, 0, None, 0) == status
     assert g.gdr_chunk_fwd_path(d) == status
     assert g.gdr_chunk_fwd_workspace_size(d) == 0
 
@@ -106,6 +107,9 @@ def test_null_and_misaligned_pointers(g):
         == g.GDR_EINVAL
     dkv = _desc(g, beta_mode=g.GDR_BETA_KV)
     assert g.gdr_chunk_fwd(dkv, q, k, None, v, a, b, None, None, o, st, None, 0, 0) == g.GDR_EINVAL
+    # the context-taking prefill checks the same arguments before it looks at the context
+    assert g.gdr_chunk_fwd_ctx(d, None, k, None, v, a, b, None, None, o, st, None, 0, None, 0) == g.GDR_EINVAL
+    assert g.gdr_chunk_fwd_ctx(d, q, k, None, v, a, b, None, None, q, st, None, 0, None, 0) == g.GDR_EINVAL
 
 
 def test_output_may_not_alias_inputs(g):

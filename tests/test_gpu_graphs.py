@@ -66,6 +66,25 @@ def test_prefill_graph_replays_equal_eager(case):
     _replay_and_compare(torch, graph, (o_g, S_g), lambda: g.chunk_fwd(*args, **kw), case)
 
 
+def test_prefill_with_context_graph_replays_equal_eager():
+    """A long prefill with an execution context: the prep of each chunk block is forked
+    onto the context's second stream and every state launch waits for its block's event,
+    all recorded in the one graph."""
+    torch, g = gpu()
+    w = gi.OSDN_LONG_PREFILL.scaled(B=1, T=16500, H=2, seed=129)
+    d = upload(gi.make_prefill(w), w)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta_k"])
+    kw = dict(k_w=d["k_w"], S0=d["S0"])
+    ctx = g.Context()
+    o_g = torch.empty(w.B, w.T, w.H, w.dv, dtype=d["q"].dtype, device="cuda")
+    S_g = torch.empty(w.B, w.H, w.dk, w.dv, dtype=torch.float32, device="cuda")
+    desc = g.make_desc(d["q"], d["v"], d["alpha"], d["beta_k"], None)
+    ws_g = torch.empty(g.gdr_chunk_fwd_workspace_size(desc), dtype=torch.uint8, device="cuda")
+    graph, _ = _capture(torch, lambda: g.chunk_fwd(*args, **kw, out=o_g, final_state=S_g, workspace=ws_g,
+                                                   ctx=ctx))
+    _replay_and_compare(torch, graph, (o_g, S_g), lambda: g.chunk_fwd(*args, **kw), "prefill context")
+
+
 def test_checkpointed_prefill_graph_replays_equal_eager():
     torch, g = gpu()
     w = gi.GDN_PREFILL.scaled(B=1, T=520, H=2, seed=124)

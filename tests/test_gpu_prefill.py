@@ -86,6 +86,40 @@ def test_long_sequence(name, w):
     assert torch.equal(o_st, o_one)
 
 
+# With an execution context, a long sequence of few heads runs the prep of chunk blocks on
+# the context's second stream beside the state recurrence (one state launch per block):
+# bit for bit the call without a context, in place too.
+CTX_LONG = [
+    ("gdn_T16500_two_blocks", gi.GDN_PREFILL.scaled(B=1, T=16500, H=2, seed=45)),
+    ("osdn_kw_S0_T65536_eight_blocks", gi.OSDN_LONG_PREFILL.scaled(B=1, T=65536, H=1, seed=46)),
+    ("bf16_gates_T40000_ragged", gi.GDN_PREFILL.scaled(B=2, T=40000, H=1, gate=gi.BF16, seed=47)),
+]
+
+
+@pytest.mark.parametrize("name,w", CTX_LONG, ids=[c[0] for c in CTX_LONG])
+def test_long_sequence_with_context(name, w):
+    torch, g = gpu()
+    x = gi.make_prefill(w)
+    d = upload(x, w)
+    args = (d["q"], d["k"], d["v"], d["alpha"], d["beta_k"])
+    ctx = g.Context()
+    o_ref, S_ref = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"])
+    o_c, S_c = g.chunk_fwd(*args, k_w=d["k_w"], S0=d["S0"], ctx=ctx)
+    S_io = (d["S0"] if d["S0"] is not None else torch.zeros_like(S_ref)).clone()
+    o_io, _ = g.chunk_fwd(*args, k_w=d["k_w"], S0=S_io, final_state=S_io, ctx=ctx)
+    torch.cuda.synchronize()
+    same = torch.equal(o_c, o_ref) and torch.equal(S_c, S_ref)
+    if d["S0"] is not None:
+        same_io = torch.equal(o_io, o_ref) and torch.equal(S_io, S_ref)
+    else:
+        same_io = True  # S0 = zeros differs from S0 = NULL only in how the zero is read
+    log(f"[prefill ctx] {name}: equal to the call without a context {same}; in place {same_io}")
+    assert same and same_io
+    # and against the oracle on one (batch, head)
+    r = run_prefill(w, x, heads=[0])
+    assert r["o"] <= TOL[w.io] and r["S"] <= TOL[w.io], r
+
+
 def test_long_in_place_and_checkpoints():
     """A long sequence with S0 and S_T in one buffer (in-place resume), and with segment
     states kept: both bit for bit against the plain call."""
