@@ -852,15 +852,19 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                         ta[f] = *reinterpret_cast<const u32x4 *>(&B.T[t][8 * ((4 * kk + q) ^ sw)]);
                     }
                 }
+                // consecutive products go to different tiles (a product that accumulates onto
+                // the one just issued waits for it); each tile still sums hi, lo per k step
+                constexpr int f0[4] = {0, 1, 2, 4}, f1[4] = {0, 0, 3, 5};
 #pragma unroll
-                for (int tt = 0, f = 0; tt < 4; ++tt) {
-                    D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+                for (int tt = 0; tt < 4; ++tt) D[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rh[kk]), D[tt]);
-                        D[tt] = mfma(as_bf16x8(ta[f]), as_bf16x8(rl[kk]), D[tt]);
-                    }
-                }
+                for (int tt = 0; tt < 4; ++tt) D[tt] = mfma(as_bf16x8(ta[f0[tt]]), as_bf16x8(rh[0]), D[tt]);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) D[tt] = mfma(as_bf16x8(ta[f0[tt]]), as_bf16x8(rl[0]), D[tt]);
+#pragma unroll
+                for (int tt = 2; tt < 4; ++tt) D[tt] = mfma(as_bf16x8(ta[f1[tt]]), as_bf16x8(rh[1]), D[tt]);
+#pragma unroll
+                for (int tt = 2; tt < 4; ++tt) D[tt] = mfma(as_bf16x8(ta[f1[tt]]), as_bf16x8(rl[1]), D[tt]);
             }
             // publish D for the side wave; E = fac D stays here
             u32x4 eh[2], el[2];
@@ -893,13 +897,15 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     }
 #pragma unroll
                 for (int kt = 0; kt < 8; ++kt) S[kt] *= gC;
+                // the eight state tiles are independent: the hi products of a k step for all of
+                // them, then the lo products (each tile sums hi, lo per k step)
 #pragma unroll
-                for (int kk = 0; kk < 2; ++kk)
+                for (int kk = 0; kk < 2; ++kk) {
 #pragma unroll
-                    for (int kt = 0; kt < 8; ++kt) {
-                        S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(eh[kk]), S[kt]);
-                        S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(el[kk]), S[kt]);
-                    }
+                    for (int kt = 0; kt < 8; ++kt) S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(eh[kk]), S[kt]);
+#pragma unroll
+                    for (int kt = 0; kt < 8; ++kt) S[kt] = mfma(as_bf16x8(kw[kt][kk]), as_bf16x8(el[kk]), S[kt]);
+                }
             }
             publish_state();  // for the next chunk (the side wave read this chunk's before B1)
             if (ckpt_after(p, c)) {
@@ -927,12 +933,12 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) O[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
+                for (int kk = 0; kk < 4; ++kk) {
 #pragma unroll
-                    for (int tt = 0; tt < 4; ++tt) {
-                        O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sh[kk]), O[tt]);
-                        O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sl[kk]), O[tt]);
-                    }
+                    for (int tt = 0; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sh[kk]), O[tt]);
+#pragma unroll
+                    for (int tt = 0; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(qa[kk][tt]), as_bf16x8(sl[kk]), O[tt]);
+                }
 #pragma unroll
                 for (int tt = 0; tt < 4; ++tt) O[tt] *= *reinterpret_cast<const f32x4 *>(&B.G[16 * tt + 4 * q]);
             }
@@ -964,14 +970,21 @@ __global__ void __launch_bounds__(256) gdr_state_ws_kernel(ChunkParams p, int NT
                     dh[kk] = sm.Dx[w][2 * kk][l];
                     dl[kk] = sm.Dx[w][2 * kk + 1][l];
                 }
+                // per tile and k step: ph dh, ph dl, pl dh; consecutive products go to
+                // different tiles
+                constexpr int f0[4] = {0, 1, 2, 4}, f1[4] = {0, 0, 3, 5};
 #pragma unroll
-                for (int tt = 0, f = 0; tt < 4; ++tt)
+                for (int tt = 0; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(ph[f0[tt]]), as_bf16x8(dh[0]), O[tt]);
 #pragma unroll
-                    for (int kk = 0; kk < (tt < 2 ? 1 : 2); ++kk, ++f) {
-                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dh[kk]), O[tt]);
-                        O[tt] = mfma(as_bf16x8(ph[f]), as_bf16x8(dl[kk]), O[tt]);
-                        O[tt] = mfma(as_bf16x8(pl[f]), as_bf16x8(dh[kk]), O[tt]);
-                    }
+                for (int tt = 0; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(ph[f0[tt]]), as_bf16x8(dl[0]), O[tt]);
+#pragma unroll
+                for (int tt = 0; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(pl[f0[tt]]), as_bf16x8(dh[0]), O[tt]);
+#pragma unroll
+                for (int tt = 2; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(ph[f1[tt]]), as_bf16x8(dh[1]), O[tt]);
+#pragma unroll
+                for (int tt = 2; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(ph[f1[tt]]), as_bf16x8(dl[1]), O[tt]);
+#pragma unroll
+                for (int tt = 2; tt < 4; ++tt) O[tt] = mfma(as_bf16x8(pl[f1[tt]]), as_bf16x8(dh[1]), O[tt]);
                 // O goes out as rows: staged (bf16) in this wave's D slot, whose fragments are
                 // already in registers, then 16 bytes per lane and store
                 uint16_t(*Ost)[24] = reinterpret_cast<uint16_t(*)[24]>(&sm.Dx[w][0][0]);
