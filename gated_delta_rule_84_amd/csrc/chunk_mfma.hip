@@ -257,18 +257,23 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) ka[kk] = *reinterpret_cast<const u32x4 *>(&Ks[tg][8 * ((4 * kk + q) ^ (tg & 15))]);
     }
+    // every tile of both row blocks is formed (the masks below zero the ones above the
+    // diagonal): products guarded by the wave's block index would each become a branch
+    // of their own, with the accumulators copied around it
     f32x4 accG[4], accP[4];
 #pragma unroll
     for (int J = 0; J < 4; ++J) {
         accG[J] = f32x4{0.f, 0.f, 0.f, 0.f};
         accP[J] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) {
-            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&KWs[16 * J + r][8 * ((4 * kk + q) ^ r)]));
-            if (J <= IG) accG[J] = mfma(as_bf16x8(ka[kk]), kb, accG[J]);
-            if (J <= IP) accP[J] = mfma(kb, as_bf16x8(qa[kk]), accP[J]);  // scores transposed
-        }
     }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4 *>(&KWs[16 * J + r][8 * ((4 * kk + q) ^ r)]));
+            accG[J] = mfma(as_bf16x8(ka[kk]), kb, accG[J]);
+            accP[J] = mfma(kb, as_bf16x8(qa[kk]), accP[J]);  // scores transposed
+        }
     // cumulative log decay and beta (wave 0), segmented at zero gates: P_t sums log alpha
     // over the chunk's tokens <= t with a zero gate adding 0, and Z_t is the last token
     // <= t whose gate is 0 (-1 if none).  The decay from token s to token t >= s is
@@ -533,16 +538,15 @@ __global__ void __launch_bounds__(kThreads) gdr_prep_chan_kernel(ChunkParams p, 
             for (int J = 0; J < 4; ++J) {
                 const bf16x8 bh8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Whs[16 * J + r][32 * kk + 8 * q]));
                 const bf16x8 bl8 = as_bf16x8(*reinterpret_cast<const u32x4 *>(&Wls[16 * J + r][32 * kk + 8 * q]));
-                if (J <= IG) {
-                    accG[J] = mfma(as_bf16x8(uh[kk]), bh8, accG[J]);
-                    accG[J] = mfma(as_bf16x8(uh[kk]), bl8, accG[J]);
-                    accG[J] = mfma(as_bf16x8(ul[kk]), bh8, accG[J]);
-                }
-                if (J <= IP) {
-                    accP[J] = mfma(as_bf16x8(qh[kk]), bh8, accP[J]);
-                    accP[J] = mfma(as_bf16x8(qh[kk]), bl8, accP[J]);
-                    accP[J] = mfma(as_bf16x8(ql[kk]), bh8, accP[J]);
-                }
+                // every tile is formed; the masks below zero the ones above the diagonal
+                // (guarded products would each become a branch with the accumulators
+                // copied around it)
+                accG[J] = mfma(as_bf16x8(uh[kk]), bh8, accG[J]);
+                accG[J] = mfma(as_bf16x8(uh[kk]), bl8, accG[J]);
+                accG[J] = mfma(as_bf16x8(ul[kk]), bh8, accG[J]);
+                accP[J] = mfma(as_bf16x8(qh[kk]), bh8, accP[J]);
+                accP[J] = mfma(as_bf16x8(qh[kk]), bl8, accP[J]);
+                accP[J] = mfma(as_bf16x8(ql[kk]), bh8, accP[J]);
             }
         __syncthreads();  // P is dead: As and Ts take its place
 
