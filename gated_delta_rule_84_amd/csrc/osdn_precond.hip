@@ -118,6 +118,17 @@ __device__ __forceinline__ void load_keys(const PcParams &p, float (*kf)[PITCH],
     }
 }
 
+// Lane exchanges on the vector ALU (DPP), in place of shuffles through the LDS unit:
+// the value of lane l ^ 1 or l ^ 2 (quad permutes), and of lane l + 4 inside its row of
+// 16 (lanes 12 .. 15 of a row receive 0).  All lanes of the wave must be active.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+constexpr int kDppXor1 = 0xB1;   // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;   // quad_perm [2, 3, 0, 1]
+constexpr int kDppShl4 = 0x104;  // row_shl:4
+
 // workgroup barrier that waits only for this wave's LDS operations: global loads
 // issued for the next chunk stay in flight across it (the memory clobber keeps the
 // compiler from moving memory operations across)
@@ -160,8 +171,8 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
             for (int y = 0; y < 4; ++y) s4[y] += i0 + y < dk ? x[y] : 0.f;
         }
         float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
+        s += dpp_mov<kDppXor1>(s);
+        s += dpp_mov<kDppXor2>(s);
         if (part == 0) nk[t] = s;
     }
     __syncthreads();  // nk is read by wave 0 below
@@ -360,8 +371,8 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
                 for (int x = 0; x < 4; ++x) s4[x] = fmaf(av[x], dv[x], s4[x]);
             }
             float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
+            sum += dpp_mov<kDppXor1>(sum);
+            sum += dpp_mov<kDppXor2>(sum);
             if (part == 0) zs[t] = vc[bf][0][t] - vc[bf][1][t] * vc[bf][4][t] * sum;
         }
         lds_sync();
@@ -379,8 +390,8 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
                     s4[x] = fmaf(j0 + x < t ? tv[x] : 0.f, zv[x], s4[x]);
             }
             float sum = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-            sum += __shfl_xor(sum, 1);
-            sum += __shfl_xor(sum, 2);
+            sum += dpp_mov<kDppXor1>(sum);
+            sum += dpp_mov<kDppXor2>(sum);
             if (part == 0) {
                 we[t] = vc[bf][5][t] * (zs[t] + sum);
                 rec[kPrE + t] = zs[t] + sum;
@@ -402,11 +413,13 @@ __global__ void __launch_bounds__(2 * kPThreads) osdn_chain_kernel(PcParams p) {
 #pragma unroll
                 for (int x = 0; x < 4; ++x) acc[x] = fmaf(wj, av[x], acc[x]);
             }
+            // the eight lanes of a quad's token groups: sums over lane pairs, then quads,
+            // then the quad four lanes up (only lane g = 0 uses the total)
 #pragma unroll
             for (int x = 0; x < 4; ++x) {
-                acc[x] += __shfl_xor(acc[x], 1);
-                acc[x] += __shfl_xor(acc[x], 2);
-                acc[x] += __shfl_xor(acc[x], 4);
+                acc[x] += dpp_mov<kDppXor1>(acc[x]);
+                acc[x] += dpp_mov<kDppXor2>(acc[x]);
+                acc[x] += dpp_mov<kDppShl4>(acc[x]);
             }
             if (g == 0 && 4 * m < dk) {
                 const float pn = vc[bf][6][0];
@@ -510,8 +523,8 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
             for (int z = 0; z < 4; ++z) s4[z] += i0 + z < dk ? x[z] * y[z] : 0.f;
         }
         float s = (s4[0] + s4[1]) + (s4[2] + s4[3]);
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
+        s += dpp_mov<kDppXor1>(s);
+        s += dpp_mov<kDppXor2>(s);
         if (part == 0 && t < n) {
             const double u = 1.0 - (double)vb[t] * (double)s;
             logsum = log(u * u);
