@@ -216,17 +216,31 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
         auto tI = [&](int k) { return w == 0 ? (k == 0 ? 0 : 1) : I0; };
         auto tJ = [&](int k) { return w == 0 ? (k == 2 ? 1 : 0) : J0 + k; };
         f32x4 acc[3] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const int ksteps = (dk + 3) / 4;
-        for (int st = 0; st < ksteps; ++st) {
-            const int ch = 4 * st + q;  // dk is a multiple of 8
+        // a wave with two tiles also forms a copy of its first one in the third slot
+        // (never stored), so the loop carries no branch; two channel steps per
+        // iteration (dk is a multiple of 8), every operand read before the products
+        int ra[3], rb[3];
 #pragma unroll
-            for (int k = 0; k < 3; ++k) {
-                if (k < nt) {
-                    const float av = a[16 * tI(k) + r][ch];
-                    const float bv = a[16 * tJ(k) + r][ch];
-                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, bv, acc[k], 0, 0, 0);
+        for (int k = 0; k < 3; ++k) {
+            const int kk = k < nt ? k : 0;
+            ra[k] = 16 * tI(kk) + r;
+            rb[k] = 16 * tJ(kk) + r;
+        }
+        const int ksteps = dk / 4;
+        for (int st = 0; st < ksteps; st += 2) {
+            float av[2][3], bv[2][3];
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int k = 0; k < 3; ++k) {
+                    av[u][k] = a[ra[k]][4 * (st + u) + q];
+                    bv[u][k] = a[rb[k]][4 * (st + u) + q];
                 }
-            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int k = 0; k < 3; ++k)
+                    acc[k] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[u][k], bv[u][k], acc[k], 0, 0, 0);
         }
 #pragma unroll
         for (int k = 0; k < 3; ++k) {
