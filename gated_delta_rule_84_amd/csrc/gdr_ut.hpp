@@ -21,17 +21,27 @@ __device__ __forceinline__ void ut_transform(float (*As)[kUtN + 4], float (*Ts)[
     if (l < 16) {
         const int base = 16 * w, cc = l;
         float col[16];
+        // row rr + 1 of the block is requested before row rr's dependent chain runs
+        // (only its first rr + 1 entries are used: whole 16-byte pieces up to them)
+        f32x4 nxt[4] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f},
+                        f32x4{0.f, 0.f, 0.f, 0.f}};
+        auto load_row = [&](int rr, f32x4 (&x)[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int m4 = 0; m4 < 4; ++m4)
+                if (4 * m4 < rr) x[m4] = *reinterpret_cast<const f32x4 *>(&As[base + rr][base + 4 * m4]);
+        };
+        load_row(0, nxt);
 #pragma unroll
         for (int rr = 0; rr < 16; ++rr) {
             float a[16];
 #pragma unroll
             for (int m4 = 0; m4 < 4; ++m4) {
-                const f32x4 x = *reinterpret_cast<const f32x4 *>(&As[base + rr][base + 4 * m4]);
-                a[4 * m4] = x[0];
-                a[4 * m4 + 1] = x[1];
-                a[4 * m4 + 2] = x[2];
-                a[4 * m4 + 3] = x[3];
+                a[4 * m4] = nxt[m4][0];
+                a[4 * m4 + 1] = nxt[m4][1];
+                a[4 * m4 + 2] = nxt[m4][2];
+                a[4 * m4 + 3] = nxt[m4][3];
             }
+            if (rr + 1 < 16) load_row(rr + 1, nxt);
             float v = rr == cc ? 1.f : 0.f;
 #pragma unroll
             for (int m = 0; m < rr; ++m) v -= a[m] * col[m];

@@ -259,9 +259,15 @@ __global__ void __launch_bounds__(kPThreads) osdn_chunk_kernel(PcParams p) {
     // Tm = (I + A)^{-1}: diagonal 16 x 16 blocks by forward substitution, the others by
     // the 2 x 2 block-inverse rule on fp32 matrix cores
     ut_transform(A, Ti, Xs, tid >> 6, tid & 63);
-    for (int e = tid; e < kPL * kPL; e += kPThreads) {
-        const int t = e / kPL, j = e % kPL;
-        rec[kPrT + e] = j < t ? Ti[t][j] : (j == t ? 1.f : 0.f);
+    for (int e4 = tid; e4 < kPL * kPL / 4; e4 += kPThreads) {  // 16-byte stores
+        const int t = e4 / (kPL / 4), j0 = 4 * (e4 % (kPL / 4));
+        f32x4 v;
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            const int j = j0 + x;
+            v[x] = j < t ? Ti[t][j] : (j == t ? 1.f : 0.f);
+        }
+        *reinterpret_cast<f32x4 *>(rec + kPrT + 4 * e4) = v;
     }
 }
 
@@ -514,11 +520,19 @@ __global__ void __launch_bounds__(kPThreads) osdn_emit_kernel(PcParams p) {
         float kc[kPL];
 #pragma unroll
         for (int t = 0; t < kPL; ++t) kc[t] = kf[t][tid];
+        if (n == kPL) {  // a full chunk: no per-token test
 #pragma unroll
-        for (int t = 0; t < kPL; ++t) {
-            if (t < n) {
+            for (int t = 0; t < kPL; ++t) {
                 kw[t][tid] = di * kc[t];
                 di = fmaf(vr[t], di, ve[t] * kc[t] * kc[t]);
+            }
+        } else {
+#pragma unroll
+            for (int t = 0; t < kPL; ++t) {
+                if (t < n) {
+                    kw[t][tid] = di * kc[t];
+                    di = fmaf(vr[t], di, ve[t] * kc[t] * kc[t]);
+                }
             }
         }
     }
