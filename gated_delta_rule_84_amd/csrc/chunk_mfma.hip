@@ -169,9 +169,10 @@ __device__ __forceinline__ void lds_barrier() {
 // ---------------------------------------------------------------------------
 // pieces shared by the two prep kernels (256 threads, four waves)
 // ---------------------------------------------------------------------------
-// The lower-triangular Tm (fp32 rows in Ts, unit diagonal implied) to the record as
-// bf16 rows of 64 in pcol order, 16 bytes per store.
-__device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[kC + 8], const int tid) {
+// The lower-triangular Tm (fp32 rows in Ts, row pitch LT, unit diagonal implied) to the
+// record as bf16 rows of 64 in pcol order, 16 bytes per store.
+template <int LT>
+__device__ __forceinline__ void store_ut(char *dst, const float (*Ts)[LT], const int tid) {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {  // 512 pieces of 8 bf16
         const int pc = tid + 256 * m, row = pc >> 3, c0 = (pc & 7) * 8;
@@ -202,14 +203,23 @@ __device__ __forceinline__ void store_p(char *dh, char *dl, const uint16_t (*Ph)
 // ---------------------------------------------------------------------------
 // prep kernel
 // ---------------------------------------------------------------------------
-// GBF16: the gates are bf16 (compile time, so the gate loads carry no branch)
-template <bool GBF16>
-__global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, int NT) {
+// GBF16: the gates are bf16 (compile time, so the gate loads carry no branch).
+// SEP: the write keys are a tensor of their own (k_w != k).  Without one the UT transform
+// runs in place (Tm over the Gram matrix): 22 KB of LDS, five blocks per CU (the
+// registers allow five); with one, Tm has its own array, which first holds the key tile.
+template <bool GBF16, bool SEP>
+__global__ void __launch_bounds__(kThreads, SEP ? 4 : 5) gdr_prep_kernel(ChunkParams p, int NT) {
+    constexpr int PT = SEP ? kC + 8 : kC + 4;  // row pitch of Tm
     __shared__ float gl[kC], bl[kC];
     __shared__ int zl[kC];
     __shared__ __align__(16) float As[kC][kC + 4];  // Gram matrix, strictly lower part (first: the write keys)
-    __shared__ __align__(16) float Ts[kC][kC + 8];  // UT transform (first: the keys, when a separate tensor)
+    __shared__ __align__(16) float Tbuf[SEP ? kC * PT : 4];  // UT transform (first: the keys)
     __shared__ __align__(16) float Xs[4][16][16];  // the four 16 x 16 blocks of A_2:4,0:2 T_0:2,0:2
+    float(*Ts)[PT];
+    if constexpr (SEP)
+        Ts = reinterpret_cast<float(*)[PT]>(&Tbuf[0]);
+    else
+        Ts = As;
 
     const int blk = blockIdx.x, nc = p.c1 - p.c0;  // chunks c0 .. c1 - 1 of every (batch, head)
     const int c = p.c0 + blk % nc, bh = blk / nc;
@@ -241,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 4) gdr_prep_kernel(ChunkParams p, in
     // rows 16 w .. 16 w + 15, 16-byte pieces of row t stored at piece ^ (t & 15)) and
     // every wave reads its B fragments from there; the key tile, when it is a different
     // tensor, likewise into the space Ts takes later -- each tile is read from HBM once
-    const bool sep = p.kw != p.k;
+    constexpr bool sep = SEP;
     uint16_t(*KWs)[kD] = reinterpret_cast<uint16_t(*)[kD]>(&As[0][0]);
     uint16_t(*Ks)[kD] = sep ? reinterpret_cast<uint16_t(*)[kD]>(&Ts[0][0]) : KWs;
 #pragma unroll
@@ -1420,8 +1430,11 @@ hipError_t launch_chunk_mfma(const ChunkParams &p, const gdr_context *ctx, hipSt
                 reinterpret_cast<const void *>(&gdr_prep_chan_kernel<true, true, true>)};
             fn = preps[(g16 ? 4 : 0) + (ach ? 2 : 0) + (bvec ? 1 : 0)];
         } else {
-            fn = g16 ? reinterpret_cast<const void *>(&gdr_prep_kernel<true>)
-                     : reinterpret_cast<const void *>(&gdr_prep_kernel<false>);
+            const void *preps[4] = {reinterpret_cast<const void *>(&gdr_prep_kernel<false, false>),
+                                    reinterpret_cast<const void *>(&gdr_prep_kernel<false, true>),
+                                    reinterpret_cast<const void *>(&gdr_prep_kernel<true, false>),
+                                    reinterpret_cast<const void *>(&gdr_prep_kernel<true, true>)};
+            fn = preps[(g16 ? 2 : 0) + (p.kw != p.k ? 1 : 0)];
         }
         return hipLaunchKernel(fn, dim3((unsigned)(nbh * (c1 - c0))), dim3(kThreads), args, 0, s);
     };

@@ -11,9 +11,14 @@ namespace {
 constexpr int kUtN = 64;
 
 // Tm = (I + A)^{-1} for the strictly lower 64 x 64 A in As, into the lower part of
-// Ts (fp32; the unit diagonal and the upper part are not written).  Ends with a
-// barrier; starts reading As, so the caller has published it with a barrier.
-__device__ __forceinline__ void ut_transform(float (*As)[kUtN + 4], float (*Ts)[kUtN + 8], float (*Xs)[16][16],
+// Ts (fp32, row pitch LT; the unit diagonal and the upper part are not written).
+// Ts may be As itself (LT = kUtN + 4): every 16 x 16 block of A is read before the
+// block of Tm at the same place is written (the diagonal blocks by the wave that
+// inverts them, after its loop; the off-diagonal ones after a barrier that follows
+// their last read).  Ends with a barrier; starts reading As, so the caller has
+// published it with a barrier.
+template <int LT>
+__device__ __forceinline__ void ut_transform(float (*As)[kUtN + 4], float (*Ts)[LT], float (*Xs)[16][16],
                                              const int w, const int l) {
     const int r = l & 15, q = l >> 4;
     // diagonal 16 x 16 blocks of (I + A)^{-1}: wave w, lane c < 16 owns column c;
@@ -72,7 +77,7 @@ __device__ __forceinline__ void ut_transform(float (*As)[kUtN + 4], float (*Ts)[
         };
         auto Ab = [&](int I, int J) { return &As[16 * I][16 * J]; };
         auto Tb = [&](int I, int J) { return &Ts[16 * I][16 * J]; };
-        constexpr int LA = kUtN + 4, LT = kUtN + 8;
+        constexpr int LA = kUtN + 4;
         const f32x4 z = {0.f, 0.f, 0.f, 0.f};
         auto storeT = [&](int I, int J, f32x4 v) __attribute__((always_inline)) {
 #pragma unroll
